@@ -1,0 +1,164 @@
+/*
+ * spec_verify.h -- C ABI of the batched speculative-sampling verify step (MI355X / gfx950).
+ *
+ * The operation.  For each of B sequences a draft model has proposed K tokens
+ * x_0..x_{K-1}; the target model has produced logits at K+1 positions and the draft
+ * at K positions.  With p_t = softmax(zt_t / T) and q_t = softmax(zd_t / T):
+ *   - left to right, draft token x_t is accepted while r_t < p_t(x_t) / q_t(x_t);
+ *   - at the first rejection one token is drawn from (p_t - q_t)+ / ||(p_t - q_t)+||_1,
+ *     the positive part of the pointwise difference over the vocabulary, and the
+ *     step stops;
+ *   - if all K are accepted, a bonus token is drawn from p_K;
+ *   - at temperature 0 the rule is argmax(p_t) == x_t, emitting argmax(p_t) on the
+ *     first mismatch (argmax(p_K) after K matches).
+ * Source: the lesson "Decodificação Especulativa e EAGLE" (ai-engineering.academy,
+ * Phase 10 Lesson 25), sections "O Conceito" (steps 1-4), "A Regra de Exatidão"
+ * and its "Caso ganancioso" paragraph; the same text as "Quy tắc chính xác" in
+ * "Việc giải mã giả định và Eagle" (aiengineeringfromscratch.com).  The temperature
+ * softmax on both sides follows those pages' "Desenvolva" / "Hãy xây dựng nó" listing.
+ *
+ * Readings fixed by this contract where the pages are silent:
+ *   - argmax ties go to the LOWEST index;
+ *   - a categorical draw with weights w and uniform u returns the smallest i with
+ *     w_0 + ... + w_i > u * sum(w); if rounding leaves no such i, the last index
+ *     with w_i > 0.  The draw that follows a rejection or the bonus uses u[b][K];
+ *     test t uses u[b][t];
+ *   - the draw after a rejection uses fp64 weights; should they sum to zero in fp64
+ *     (impossible in exact arithmetic) it draws from p_t and flags NOTE_FALLBACK.
+ *
+ * Memory.  Every pointer named "device" is device memory owned by the caller.  The
+ * library never allocates, frees or retains memory.  All calls are asynchronous on
+ * `stream` (a hipStream_t passed as void*; NULL = the null stream) and never
+ * synchronise the host.  Outputs stay on the device.
+ *
+ * Errors.  Argument errors are detected on the host BEFORE any HIP call and
+ * returned synchronously (SV_ERR_ARG, SV_ERR_DTYPE, SV_ERR_WORKSPACE); a failed
+ * launch returns SV_ERR_HIP.  Data errors are detected on the device and reported
+ * per sequence in out_status[b] (flags below); such a sequence emits tokens -1,
+ * accept length -1 and p = q = NaN.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_ABI_VERSION 1
+
+/* Host-side return codes. */
+typedef enum sv_status {
+    SV_OK = 0,
+    SV_ERR_ARG = 1,        /* bad size, NULL required pointer, misaligned pointer        */
+    SV_ERR_DTYPE = 2,      /* dtype is not one of sv_dtype                                */
+    SV_ERR_WORKSPACE = 3,  /* workspace NULL, misaligned or smaller than required        */
+    SV_ERR_HIP = 4         /* a kernel launch failed                                      */
+} sv_status;
+
+/* Logit storage.  bf16 = the upper 16 bits of an IEEE fp32 (round-trip exact widening). */
+typedef enum sv_dtype {
+    SV_DTYPE_F32 = 0,
+    SV_DTYPE_BF16 = 1
+} sv_dtype;
+
+/* Per-sequence device status flags (out_status[b], OR-ed). */
+#define SV_SEQ_OK               0
+#define SV_SEQ_ERR_TOKEN        1   /* a draft token outside [0, V)                                 */
+#define SV_SEQ_ERR_LOGIT        2   /* NaN in a row the sequence reads, a row whose max is -inf, or
+                                       (sampled sequences) a +inf logit                             */
+#define SV_SEQ_ERR_TEMPERATURE  4   /* T NaN, negative, infinite, or in (0, FLT_MIN)                */
+#define SV_SEQ_ERR_UNIFORM      8   /* (sampled sequences) u NaN or outside [0, 1)                  */
+#define SV_SEQ_NOTE_FALLBACK   16   /* not an error: a categorical draw fell back (see above)       */
+
+/* Returns SV_ABI_VERSION of the loaded library. */
+int sv_abi_version(void);
+
+/* Static text for an sv_status value; "unknown status" otherwise.  Never NULL. */
+const char* sv_status_string(int status);
+
+/*
+ * Bytes of device workspace spec_verify / spec_verify_greedy need for (B, K, V).
+ * Pure host function.  Returns SV_ERR_ARG (and *bytes = 0) when B < 0, K < 0, V < 1,
+ * or the sizes overflow; SV_OK otherwise.  The same size serves both entry points.
+ *
+ * Workspace contract: 256-byte aligned device memory of at least *bytes.  Its content
+ * on entry does not matter (each call initialises what it uses); it can be reused for
+ * any later (B, K, V) that fits.  Calls that share one workspace must be ordered (same
+ * stream, or synchronised): overlapping calls on one workspace race.
+ */
+sv_status sv_workspace_bytes(int B, int K, int V, size_t* bytes);
+
+/*
+ * Sampled verify (temperature > 0), with the greedy rule for sequences whose T == 0.
+ *
+ *   target_logits  device, [B][K+1][V] of `dtype`, row-major and contiguous.
+ *   draft_logits   device, [B][K][V]   of `dtype`; rows of T == 0 sequences are not
+ *                  read.  May be NULL only when K == 0.
+ *   dtype          sv_dtype.  Pointers must be aligned to the element size.
+ *   draft_tokens   device, [B][K] int32.  May be NULL only when K == 0.
+ *   uniforms       device, [B][K+1] fp32, each in [0, 1): slot t < K drives the ratio
+ *                  test of x_t, slot K the final categorical draw.  Not read for T == 0.
+ *   temperature    device, [B] fp32.  T > 0: sampled; T == 0: greedy rule.
+ *   B, K, V        B >= 0 (B == 0 is a no-op), K >= 0 (K == 0 = plain sampling from
+ *                  p_0), V >= 1; B*(K+1)*V must fit in int64.
+ *   out_tokens     device, [B][K+1] int32: x_0..x_{n-1}, the drawn token, then -1.
+ *   out_accept_len device, [B] int32: n in [0, K], the number of accepted drafts.
+ *   out_p, out_q   device, [B][K] fp32, or NULL: p_t(x_t) and q_t(x_t) for every t < K
+ *                  (also past the rejection); NaN for T == 0 sequences.
+ *   out_status     device, [B] int32: SV_SEQ_* flags.
+ *   workspace      device, see sv_workspace_bytes.
+ *   stream         hipStream_t as void*.
+ * Outputs are complete when the stream reaches the end of the call.  Bit-reproducible:
+ * the same inputs give the same outputs on every call.
+ */
+sv_status spec_verify(const void* target_logits, const void* draft_logits, int dtype,
+                      const int32_t* draft_tokens, const float* uniforms,
+                      const float* temperature, int B, int K, int V,
+                      int32_t* out_tokens, int32_t* out_accept_len,
+                      float* out_p, float* out_q, int32_t* out_status,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Greedy verify (temperature 0 for every sequence): accept x_t while the lowest-index
+ * argmax of target row t equals x_t; emit that argmax at the first mismatch, or the
+ * argmax of row K after K matches.  Reads target logits only.  Arguments as for
+ * spec_verify.  Bit-exact by construction (comparisons only).
+ */
+sv_status spec_verify_greedy(const void* target_logits, int dtype,
+                             const int32_t* draft_tokens, int B, int K, int V,
+                             int32_t* out_tokens, int32_t* out_accept_len,
+                             int32_t* out_status,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fill uniforms[B][K+1] (device, fp32) with the counter-based draws of the exact
+ * rule's r ~ Uniform(0, 1) ("A Regra de Exatidão") and of the final categorical draw:
+ *   u[b][t] = (w0 >> 40) * 2^-24,   (w0, w1, w2, w3) = Philox4x64-10(counter, key),
+ *   key = (seed, domain), counter = (t, b, step, 0),
+ * Philox4x64-10 as published by Salmon, Moraes, Dror and Shaw ("Parallel random
+ * numbers: as easy as 1, 2, 3", SC'11).  Every u is a multiple of 2^-24 in [0, 1).
+ * B >= 0, K >= 0; uniforms may be NULL only when B == 0.
+ */
+sv_status sv_fill_uniforms(uint64_t seed, uint64_t domain, uint64_t step, int B, int K,
+                           float* uniforms, void* stream);
+
+/*
+ * Kernel timing for benchmarks (host state, not thread-safe).
+ * sv_profile_begin: until sv_profile_end, every spec_verify / spec_verify_greedy call
+ * records HIP events on its stream around its pass-1 kernel (streaming of the logit
+ * rows, the resolve) and around its pass-2 kernels (the categorical draws).
+ * sv_profile_end: waits for those events, writes the number of calls and the summed
+ * milliseconds of each phase (any pointer may be NULL), and stops recording.  Returns
+ * SV_ERR_HIP if an event could not be created, recorded or read.
+ */
+sv_status sv_profile_begin(void);
+sv_status sv_profile_end(int* calls, double* ms_pass1, double* ms_pass2);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,250 @@
+"""Python binding of libspecverify (the batched speculative-sampling verify step on MI355X).
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI of
+include/spec_verify.h.  PyTorch provides device memory and the stream; nothing here
+computes.  The functions carry the C names.  If the library is not built, importing
+works but every call raises ``LibraryMissing``: there is no fallback path.
+"""
+import ctypes
+import os
+
+__all__ = [
+    "LibraryMissing", "SpecVerifyError", "lib", "lib_path",
+    "sv_abi_version", "sv_status_string", "sv_workspace_bytes",
+    "spec_verify", "spec_verify_greedy", "sv_fill_uniforms", "Workspace",
+    "sv_profile_begin", "sv_profile_end",
+    "SV_OK", "SV_ERR_ARG", "SV_ERR_DTYPE", "SV_ERR_WORKSPACE", "SV_ERR_HIP",
+    "SV_DTYPE_F32", "SV_DTYPE_BF16",
+    "SV_SEQ_ERR_TOKEN", "SV_SEQ_ERR_LOGIT", "SV_SEQ_ERR_TEMPERATURE", "SV_SEQ_ERR_UNIFORM",
+    "SV_SEQ_NOTE_FALLBACK",
+]
+
+SV_OK, SV_ERR_ARG, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_HIP = 0, 1, 2, 3, 4
+SV_DTYPE_F32, SV_DTYPE_BF16 = 0, 1
+SV_SEQ_ERR_TOKEN, SV_SEQ_ERR_LOGIT, SV_SEQ_ERR_TEMPERATURE, SV_SEQ_ERR_UNIFORM = 1, 2, 4, 8
+SV_SEQ_NOTE_FALLBACK = 16
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libspecverify.so")
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {sv_status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded ctypes library (loaded on first use)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise LibraryMissing(
+            f"{lib_path} is not built; run `python -m speculative_decoding_verification_03_amd.build`")
+    L = ctypes.CDLL(lib_path)
+    vp, i32, u64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_size_t
+    L.sv_abi_version.restype = i32
+    L.sv_abi_version.argtypes = []
+    L.sv_status_string.restype = ctypes.c_char_p
+    L.sv_status_string.argtypes = [i32]
+    L.sv_workspace_bytes.restype = i32
+    L.sv_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+    L.spec_verify.restype = i32
+    L.spec_verify.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32,
+                              vp, vp, vp, vp, vp, vp, sz, vp]
+    L.spec_verify_greedy.restype = i32
+    L.spec_verify_greedy.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.sv_fill_uniforms.restype = i32
+    L.sv_fill_uniforms.argtypes = [u64, u64, u64, i32, i32, vp, vp]
+    L.sv_profile_begin.restype = i32
+    L.sv_profile_begin.argtypes = []
+    L.sv_profile_end.restype = i32
+    L.sv_profile_end.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double),
+                                 ctypes.POINTER(ctypes.c_double)]
+    _lib = L
+    return L
+
+
+# --------------------------------------------------------------------------------------
+# thin wrappers over the C names
+# --------------------------------------------------------------------------------------
+
+def sv_abi_version():
+    return lib().sv_abi_version()
+
+
+def sv_status_string(status):
+    return lib().sv_status_string(int(status)).decode()
+
+
+def sv_workspace_bytes(B, K, V):
+    n = ctypes.c_size_t(0)
+    st = lib().sv_workspace_bytes(int(B), int(K), int(V), ctypes.byref(n))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_workspace_bytes")
+    return n.value
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SV_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return SV_DTYPE_F32
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _check(t, name, dtype=None, shape=None):
+    torch = _torch()
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    del torch
+
+
+class Workspace:
+    """Device workspace for spec_verify / spec_verify_greedy, grown on demand."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, B, K, V):
+        need = sv_workspace_bytes(B, K, V)
+        if self.buf is None or self.buf.numel() < need:
+            torch = _torch()
+            self.buf = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _workspace(ws, device, B, K, V):
+    if ws is None:
+        key = str(device)
+        ws = _default_ws.setdefault(key, Workspace(device))
+    return ws.get(B, K, V)
+
+
+def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature,
+                out=None, with_probs=True, workspace=None, stream=None):
+    """Sampled verify (greedy rule where temperature == 0).
+
+    target_logits [B][K+1][V], draft_logits [B][K][V] (bf16 or fp32, same dtype),
+    draft_tokens [B][K] int32, uniforms [B][K+1] fp32, temperature [B] fp32.
+    Returns dict(tokens [B][K+1] int32, accept_len [B] int32, p, q [B][K] fp32 or None,
+    status [B] int32).  Asynchronous on the stream; outputs stay on the device.
+    """
+    torch = _torch()
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    code = _dtype_code(target_logits)
+    _check(target_logits, "target_logits")
+    _check(draft_logits, "draft_logits", target_logits.dtype, (B, K, V))
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K))
+    _check(uniforms, "uniforms", torch.float32, (B, K + 1))
+    _check(temperature, "temperature", torch.float32, (B,))
+    dev = target_logits.device
+    if out is None:
+        out = dict(
+            tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+            accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
+            p=torch.empty((B, K), dtype=torch.float32, device=dev) if with_probs else None,
+            q=torch.empty((B, K), dtype=torch.float32, device=dev) if with_probs else None,
+            status=torch.empty((B,), dtype=torch.int32, device=dev),
+        )
+    ws = _workspace(workspace, dev, B, K, V)
+    st = lib().spec_verify(
+        _ptr(target_logits), _ptr(draft_logits), code, _ptr(draft_tokens), _ptr(uniforms),
+        _ptr(temperature), B, K, V, _ptr(out["tokens"]), _ptr(out["accept_len"]),
+        _ptr(out["p"]), _ptr(out["q"]), _ptr(out["status"]),
+        _ptr(ws), ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify")
+    return out
+
+
+def spec_verify_greedy(target_logits, draft_tokens, out=None, workspace=None, stream=None):
+    """Greedy verify: target_logits [B][K+1][V], draft_tokens [B][K] int32."""
+    torch = _torch()
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    code = _dtype_code(target_logits)
+    _check(target_logits, "target_logits")
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K))
+    dev = target_logits.device
+    if out is None:
+        out = dict(
+            tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+            accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
+            status=torch.empty((B,), dtype=torch.int32, device=dev),
+        )
+    ws = _workspace(workspace, dev, B, K, V)
+    st = lib().spec_verify_greedy(
+        _ptr(target_logits), code, _ptr(draft_tokens), B, K, V, _ptr(out["tokens"]),
+        _ptr(out["accept_len"]), _ptr(out["status"]), _ptr(ws), ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_greedy")
+    return out
+
+
+def sv_fill_uniforms(seed, domain, step, B, K, out=None, device="cuda", stream=None):
+    """uniforms [B][K+1] fp32 from the counter generator (see include/spec_verify.h)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((B, K + 1), dtype=torch.float32, device=device)
+    _check(out, "uniforms", torch.float32, (B, K + 1))
+    st = lib().sv_fill_uniforms(int(seed), int(domain), int(step), int(B), int(K),
+                                _ptr(out), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_fill_uniforms")
+    return out
+
+
+def sv_profile_begin():
+    """Start recording per-kernel HIP events in later calls (benchmark timing)."""
+    st = lib().sv_profile_begin()
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_profile_begin")
+
+
+def sv_profile_end():
+    """Stop recording; returns (calls, ms of pass 1 summed, ms of pass 2 summed)."""
+    calls = ctypes.c_int(0)
+    t1 = ctypes.c_double(0.0)
+    t2 = ctypes.c_double(0.0)
+    st = lib().sv_profile_end(ctypes.byref(calls), ctypes.byref(t1), ctypes.byref(t2))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_profile_end")
+    return calls.value, t1.value, t2.value

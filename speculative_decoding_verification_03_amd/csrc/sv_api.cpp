@@ -1,0 +1,253 @@
+// C ABI of the verify library (include/spec_verify.h): argument validation on the host,
+// workspace layout, kernel launches.  Validation runs before any HIP call, so every
+// SV_ERR_ARG / SV_ERR_DTYPE / SV_ERR_WORKSPACE path works without a GPU.
+#include "spec_verify.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "sv_common.h"
+
+namespace {
+
+// Benchmark timing: per recorded call three events (before pass 1, between the passes,
+// after pass 2).  Events are created on demand and kept for reuse.
+struct Profile {
+    bool on = false;
+    bool failed = false;
+    std::vector<hipEvent_t> pool;
+    size_t used = 0;
+    int calls = 0;
+
+    hipEvent_t next() {
+        if (used == pool.size()) {
+            hipEvent_t e = nullptr;
+            if (hipEventCreate(&e) != hipSuccess) {
+                failed = true;
+                return nullptr;
+            }
+            pool.push_back(e);
+        }
+        return pool[used++];
+    }
+    void record(hipEvent_t e, void* stream) {
+        if (!e || hipEventRecord(e, static_cast<hipStream_t>(stream)) != hipSuccess) failed = true;
+    }
+};
+Profile g_prof;
+
+using sv::Layout;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// B*(K+1)*V and the block counts must fit comfortably.
+bool shape_ok(int B, int K, int V) {
+    if (B < 0 || K < 0 || V < 1) return false;
+    const __int128 cells = (__int128)B * (K + 1) * V;
+    if (cells > (__int128)INT64_MAX / 8) return false;
+    return true;
+}
+
+// Workspace for both entry points: the larger layout, region by region.
+Layout layout_for(int B, int K, int V, int rows_per_seq) { return sv::make_layout(B, K, V, rows_per_seq); }
+
+size_t workspace_need(int B, int K, int V) {
+    const Layout a = layout_for(B, K, V, 2 * K + 1);
+    const Layout b = layout_for(B, K, V, K + 1);
+    return a.total > b.total ? a.total : b.total;
+}
+
+bool grid_ok(int B, int R, const Layout& L) {
+    const __int128 blocks1 = (__int128)B * R * L.nchunk1;
+    const __int128 blocks2 = (__int128)B * L.nchunk2;
+    return blocks1 <= 0x7fffffff && blocks2 <= 0x7fffffff;
+}
+
+sv::VerifyArgs make_args(const void* target, const void* draft, const int32_t* tokens,
+                         const float* uniforms, const float* temperature, int B, int K, int V,
+                         int R, const Layout& L, void* workspace, int32_t* out_tokens,
+                         int32_t* out_n, float* out_p, float* out_q, int32_t* out_status) {
+    sv::VerifyArgs a;
+    memset(&a, 0, sizeof(a));
+    char* ws = static_cast<char*>(workspace);
+    a.target = target;
+    a.draft = draft;
+    a.tokens = tokens;
+    a.uniforms = uniforms;
+    a.temperature = temperature;
+    a.B = B;
+    a.K = K;
+    a.V = V;
+    a.R = R;
+    a.nchunk1 = L.nchunk1;
+    a.ch1 = L.ch1;
+    a.nchunk2 = L.nchunk2;
+    a.ch2 = L.ch2;
+    a.part1 = reinterpret_cast<sv::RowPartial*>(ws + L.off_part1);
+    a.desc = reinterpret_cast<sv::SeqDesc*>(ws + L.off_desc);
+    a.part2a = reinterpret_cast<sv::NormPartial*>(ws + L.off_part2a);
+    a.part2b = reinterpret_cast<double*>(ws + L.off_part2b);
+    // per-sequence completion counters: zeroed by the first kernel of every call
+    a.cnt1 = reinterpret_cast<uint32_t*>(ws + L.off_cnt1);
+    a.cnt2 = reinterpret_cast<uint32_t*>(ws + L.off_cnt2);
+    a.out_tokens = out_tokens;
+    a.out_n = out_n;
+    a.out_p = out_p;
+    a.out_q = out_q;
+    a.out_status = out_status;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sv_abi_version(void) { return SV_ABI_VERSION; }
+
+const char* sv_status_string(int status) {
+    switch (status) {
+        case SV_OK: return "ok";
+        case SV_ERR_ARG: return "invalid argument";
+        case SV_ERR_DTYPE: return "unsupported dtype";
+        case SV_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case SV_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+sv_status sv_workspace_bytes(int B, int K, int V, size_t* bytes) {
+    if (!bytes) return SV_ERR_ARG;
+    *bytes = 0;
+    if (!shape_ok(B, K, V)) return SV_ERR_ARG;
+    *bytes = workspace_need(B, K, V);
+    return SV_OK;
+}
+
+sv_status spec_verify(const void* target_logits, const void* draft_logits, int dtype,
+                      const int32_t* draft_tokens, const float* uniforms,
+                      const float* temperature, int B, int K, int V,
+                      int32_t* out_tokens, int32_t* out_accept_len,
+                      float* out_p, float* out_q, int32_t* out_status,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_DTYPE;
+    if (!shape_ok(B, K, V)) return SV_ERR_ARG;
+    if (B == 0) return SV_OK;
+    const size_t esz = dtype == SV_DTYPE_BF16 ? 2 : 4;
+    if (!target_logits || !uniforms || !temperature || !out_tokens || !out_accept_len ||
+        !out_status)
+        return SV_ERR_ARG;
+    if (K > 0 && (!draft_logits || !draft_tokens)) return SV_ERR_ARG;
+    if (!aligned(target_logits, esz) || (draft_logits && !aligned(draft_logits, esz)))
+        return SV_ERR_ARG;
+    if (!aligned(uniforms, 4) || !aligned(temperature, 4) || !aligned(out_tokens, 4) ||
+        !aligned(out_accept_len, 4) || !aligned(out_status, 4) ||
+        (draft_tokens && !aligned(draft_tokens, 4)) || (out_p && !aligned(out_p, 4)) ||
+        (out_q && !aligned(out_q, 4)))
+        return SV_ERR_ARG;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < workspace_need(B, K, V))
+        return SV_ERR_WORKSPACE;
+    const int R = 2 * K + 1;
+    const Layout L = layout_for(B, K, V, R);
+    if (!grid_ok(B, R, L)) return SV_ERR_ARG;
+
+    const sv::VerifyArgs a = make_args(target_logits, draft_logits, draft_tokens, uniforms,
+                                       temperature, B, K, V, R, L, workspace, out_tokens,
+                                       out_accept_len, out_p, out_q, out_status);
+    const int bf16 = dtype == SV_DTYPE_BF16;
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    if (g_prof.on) {
+        for (auto& e : ev) e = g_prof.next();
+        g_prof.calls++;
+    }
+    if (sv::launch_zero_counters(a, stream) != 0) return SV_ERR_HIP;
+    if (g_prof.on) g_prof.record(ev[0], stream);
+    if (sv::launch_pass1(a, bf16, stream) != 0) return SV_ERR_HIP;
+    if (g_prof.on) g_prof.record(ev[1], stream);
+    if (sv::launch_pass2(a, bf16, stream) != 0) return SV_ERR_HIP;
+    if (g_prof.on) g_prof.record(ev[2], stream);
+    return SV_OK;
+}
+
+sv_status spec_verify_greedy(const void* target_logits, int dtype,
+                             const int32_t* draft_tokens, int B, int K, int V,
+                             int32_t* out_tokens, int32_t* out_accept_len,
+                             int32_t* out_status,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_DTYPE;
+    if (!shape_ok(B, K, V)) return SV_ERR_ARG;
+    if (B == 0) return SV_OK;
+    const size_t esz = dtype == SV_DTYPE_BF16 ? 2 : 4;
+    if (!target_logits || !out_tokens || !out_accept_len || !out_status) return SV_ERR_ARG;
+    if (K > 0 && !draft_tokens) return SV_ERR_ARG;
+    if (!aligned(target_logits, esz) || !aligned(out_tokens, 4) ||
+        !aligned(out_accept_len, 4) || !aligned(out_status, 4) ||
+        (draft_tokens && !aligned(draft_tokens, 4)))
+        return SV_ERR_ARG;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < workspace_need(B, K, V))
+        return SV_ERR_WORKSPACE;
+    const int R = K + 1;
+    const Layout L = layout_for(B, K, V, R);
+    if (!grid_ok(B, R, L)) return SV_ERR_ARG;
+
+    const sv::VerifyArgs a = make_args(target_logits, nullptr, draft_tokens, nullptr, nullptr, B,
+                                       K, V, R, L, workspace, out_tokens, out_accept_len,
+                                       nullptr, nullptr, out_status);
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    if (g_prof.on) {
+        for (auto& e : ev) e = g_prof.next();
+        g_prof.calls++;
+    }
+    if (sv::launch_zero_counters(a, stream) != 0) return SV_ERR_HIP;
+    if (g_prof.on) g_prof.record(ev[0], stream);
+    if (sv::launch_pass1(a, dtype == SV_DTYPE_BF16, stream) != 0) return SV_ERR_HIP;
+    if (g_prof.on) {
+        g_prof.record(ev[1], stream);
+        g_prof.record(ev[2], stream);
+    }
+    return SV_OK;
+}
+
+sv_status sv_fill_uniforms(uint64_t seed, uint64_t domain, uint64_t step, int B, int K,
+                           float* uniforms, void* stream) {
+    if (B < 0 || K < 0) return SV_ERR_ARG;
+    if ((__int128)B * (K + 1) > (__int128)0x7fffffff * sv::kThreads) return SV_ERR_ARG;
+    if (B == 0) return SV_OK;
+    if (!uniforms || !aligned(uniforms, 4)) return SV_ERR_ARG;
+    if (sv::launch_uniforms(seed, domain, step, B, K, uniforms, stream) != 0) return SV_ERR_HIP;
+    return SV_OK;
+}
+
+sv_status sv_profile_begin(void) {
+    g_prof.on = true;
+    g_prof.failed = false;
+    g_prof.used = 0;
+    g_prof.calls = 0;
+    return SV_OK;
+}
+
+sv_status sv_profile_end(int* calls, double* ms_pass1, double* ms_pass2) {
+    double t1 = 0.0, t2 = 0.0;
+    bool ok = !g_prof.failed;
+    for (size_t i = 0; ok && i + 3 <= g_prof.used; i += 3) {
+        float a = 0.f, b = 0.f;
+        if (hipEventSynchronize(g_prof.pool[i + 2]) != hipSuccess ||
+            hipEventElapsedTime(&a, g_prof.pool[i], g_prof.pool[i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&b, g_prof.pool[i + 1], g_prof.pool[i + 2]) != hipSuccess) {
+            ok = false;
+            break;
+        }
+        t1 += a;
+        t2 += b;
+    }
+    if (calls) *calls = g_prof.calls;
+    if (ms_pass1) *ms_pass1 = t1;
+    if (ms_pass2) *ms_pass2 = t2;
+    g_prof.on = false;
+    g_prof.used = 0;
+    return ok ? SV_OK : SV_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,214 @@
+// Device helpers of the verify kernels (gfx950, wave64): logit loads, NaN-propagating
+// maxima, wavefront/workgroup reductions and scans.  All reductions combine in a fixed
+// order, so every result is bit-reproducible from run to run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sv_common.h"
+
+namespace sv {
+
+// IEEE 754-2019 maximum: NaN if either operand is NaN (v_maximum3_f32 on gfx950).
+__device__ __forceinline__ float nmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// One 16-byte streaming load (non-temporal: logits are read once).
+__device__ __forceinline__ u32x4 load16(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Logit element access: fp32 rows or bf16 rows (stored as uint16_t bit patterns).
+template <typename E>
+struct Logit;
+
+template <>
+struct Logit<float> {
+    static constexpr int kVec = 4;  // elements per 16-byte load
+    __device__ static __forceinline__ float at(const float* p, int64_t i) { return p[i]; }
+    __device__ static __forceinline__ void vec(const float* p, float (&z)[4]) {
+        const u32x4 v = load16(p);
+        z[0] = __uint_as_float(v.x); z[1] = __uint_as_float(v.y);
+        z[2] = __uint_as_float(v.z); z[3] = __uint_as_float(v.w);
+    }
+};
+
+template <>
+struct Logit<uint16_t> {
+    static constexpr int kVec = 8;
+    __device__ static __forceinline__ float at(const uint16_t* p, int64_t i) {
+        return __uint_as_float((uint32_t)p[i] << 16);
+    }
+    __device__ static __forceinline__ void vec(const uint16_t* p, float (&z)[8]) {
+        const u32x4 v = load16(p);
+        z[0] = bf16_lo(v.x); z[1] = bf16_hi(v.x);
+        z[2] = bf16_lo(v.y); z[3] = bf16_hi(v.y);
+        z[4] = bf16_lo(v.z); z[5] = bf16_hi(v.z);
+        z[6] = bf16_lo(v.w); z[7] = bf16_hi(v.w);
+    }
+};
+
+// ---------------------------------------------------------------------------------
+// wavefront reductions (butterfly: every lane ends with the same value)
+// ---------------------------------------------------------------------------------
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_nmax(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = nmax(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ int wave_or(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, 64);
+    return v;
+}
+
+// (value, index) maximum with the lowest index on ties; NaN handled by the caller.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
+    if (v2 > v || (v2 == v && i2 < i)) {
+        v = v2;
+        i = i2;
+    }
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float v2 = __shfl_xor(v, o, 64);
+        const int i2 = __shfl_xor(i, o, 64);
+        argmax_merge(v, i, v2, i2);
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// workgroup reductions over kThreads threads; every thread gets the result.
+// `sh` must hold kWaves entries of the value type.  Contains __syncthreads().
+// ---------------------------------------------------------------------------------
+
+__device__ __forceinline__ double block_sum(double v, double* sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    v = wave_sum(v);
+    if (lane == 0) sh[w] = v;
+    __syncthreads();
+    double t = sh[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) t += sh[k];
+    __syncthreads();
+    return t;
+}
+
+__device__ __forceinline__ float block_nmax(float v, float* sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    v = wave_nmax(v);
+    if (lane == 0) sh[w] = v;
+    __syncthreads();
+    float t = sh[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) t = nmax(t, sh[k]);
+    __syncthreads();
+    return t;
+}
+
+__device__ __forceinline__ int block_min(int v, int* sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    v = wave_min(v);
+    if (lane == 0) sh[w] = v;
+    __syncthreads();
+    int t = sh[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) t = min(t, sh[k]);
+    __syncthreads();
+    return t;
+}
+
+__device__ __forceinline__ int block_max(int v, int* sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    v = wave_max(v);
+    if (lane == 0) sh[w] = v;
+    __syncthreads();
+    int t = sh[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) t = max(t, sh[k]);
+    __syncthreads();
+    return t;
+}
+
+__device__ __forceinline__ int block_or(int v, int* sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    v = wave_or(v);
+    if (lane == 0) sh[w] = v;
+    __syncthreads();
+    int t = sh[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) t |= sh[k];
+    __syncthreads();
+    return t;
+}
+
+__device__ __forceinline__ void block_argmax(float& v, int& i, float* shv, int* shi) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    wave_argmax(v, i);
+    if (lane == 0) {
+        shv[w] = v;
+        shi[w] = i;
+    }
+    __syncthreads();
+    v = shv[0];
+    i = shi[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) argmax_merge(v, i, shv[k], shi[k]);
+    __syncthreads();
+}
+
+// Exclusive prefix sum of one fp64 value per thread, in thread order; also returns
+// the workgroup total.  Fixed combination order (Hillis-Steele inside each wave, then
+// wave totals left to right), so results are reproducible.
+__device__ __forceinline__ double block_exclusive_scan(double v, double& total, double* sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    double incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) sh[w] = incl;
+    __syncthreads();
+    double before = 0.0, tot = 0.0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+        if (k < w) before += sh[k];
+        tot += sh[k];
+    }
+    __syncthreads();
+    total = tot;
+    // exclusive = inclusive minus own value would round differently; shift instead
+    double excl = __shfl_up(incl, 1, 64);
+    if (lane == 0) excl = 0.0;
+    return before + excl;
+}
+
+}  // namespace sv

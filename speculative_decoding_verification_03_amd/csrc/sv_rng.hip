@@ -1,0 +1,56 @@
+// Counter-based uniforms for the verify step: u[b][t] for the ratio tests of the exact
+// rule ("A Regra de Exatidão" on the lesson page "Decodificação Especulativa e EAGLE":
+// one r ~ Uniform(0, 1) per drafted token) and, in slot K, the final categorical draw.
+//
+// Generator: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC'11): 10 rounds of two 64x64->128-bit multiplies and a
+// permutation, with a Weyl-sequence key schedule.  Contract:
+//   key = (seed, domain), counter = (t, b, step, 0), u = (word0 >> 40) * 2^-24.
+#include <hip/hip_runtime.h>
+
+#include "sv_common.h"
+
+namespace sv {
+
+namespace {
+
+constexpr uint64_t kM0 = 0xD2E7470EE14C6C93ull;
+constexpr uint64_t kM1 = 0xCA5A826395121157ull;
+constexpr uint64_t kW0 = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kW1 = 0xBB67AE8584CAA73Bull;
+
+__global__ __launch_bounds__(kThreads) void uniforms_kernel(uint64_t seed, uint64_t domain,
+                                                            uint64_t step, int64_t total, int K1,
+                                                            float* __restrict__ u) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= total) return;
+    uint64_t c0 = (uint64_t)(i % K1), c1 = (uint64_t)(i / K1), c2 = step, c3 = 0;
+    uint64_t k0 = seed, k1 = domain;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t lo0 = kM0 * c0, hi0 = __umul64hi(kM0, c0);
+        const uint64_t lo1 = kM1 * c2, hi1 = __umul64hi(kM1, c2);
+        const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+        k0 += kW0;
+        k1 += kW1;
+    }
+    u[i] = (float)(uint32_t)(c0 >> 40) * 0x1p-24f;
+}
+
+}  // namespace
+
+int launch_uniforms(uint64_t seed, uint64_t domain, uint64_t step, int B, int K, float* u,
+                    void* stream) {
+    const int64_t total = (int64_t)B * (K + 1);
+    if (total == 0) return 0;
+    const int64_t blocks = (total + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(uniforms_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), seed, domain, step, total, K + 1, u);
+    return (int)hipGetLastError();
+}
+
+}  // namespace sv

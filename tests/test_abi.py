@@ -1,0 +1,149 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/spec_verify.h
+declares, and rejects bad arguments on the host before any HIP call (no compute call
+is made here: every call below fails validation or is a pure host function)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_decoding_verification_03_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(sv.lib_path),
+                                reason="libspecverify.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "sv_abi_version", "sv_status_string", "sv_workspace_bytes", "spec_verify",
+        "spec_verify_greedy", "sv_fill_uniforms", "sv_profile_begin", "sv_profile_end"])
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(sv.lib_path)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    assert sv.sv_abi_version() == 1
+    assert sv.sv_status_string(sv.SV_OK) == "ok"
+    assert sv.sv_status_string(sv.SV_ERR_ARG) == "invalid argument"
+    assert sv.sv_status_string(sv.SV_ERR_WORKSPACE).startswith("workspace")
+    assert sv.sv_status_string(99) == "unknown status"
+
+
+def test_workspace_bytes():
+    a = sv.sv_workspace_bytes(256, 8, 152064)
+    assert a > 0 and a % 256 == 0
+    assert sv.sv_workspace_bytes(0, 8, 152064) > 0 or sv.sv_workspace_bytes(0, 8, 152064) == 0
+    assert sv.sv_workspace_bytes(1, 0, 1) > 0
+    # grows with the batch
+    assert sv.sv_workspace_bytes(1024, 10, 262144) > a
+    for bad in [(-1, 4, 10), (4, -1, 10), (4, 4, 0)]:
+        with pytest.raises(sv.SpecVerifyError) as e:
+            sv.sv_workspace_bytes(*bad)
+        assert e.value.status == sv.SV_ERR_ARG
+    n = ctypes.c_size_t(7)
+    assert sv.lib().sv_workspace_bytes(4, 4, 10, None) == sv.SV_ERR_ARG
+    assert sv.lib().sv_workspace_bytes(2 ** 30, 2 ** 20, 2 ** 30, ctypes.byref(n)) == sv.SV_ERR_ARG
+    assert n.value == 0
+
+
+def _p(addr):
+    return ctypes.c_void_p(addr)
+
+
+# fake, never-dereferenced addresses: validation must reject before any HIP call
+GOOD = 0x100000
+WS = 0x200000
+
+
+def call_verify(**kw):
+    args = dict(t=GOOD, d=GOOD, dtype=sv.SV_DTYPE_BF16, x=GOOD, u=GOOD, T=GOOD, B=4, K=3, V=64,
+                tok=GOOD, n=GOOD, p=GOOD, q=GOOD, st=GOOD, ws=WS, wsb=1 << 30)
+    args.update(kw)
+    a = args
+    return sv.lib().spec_verify(_p(a["t"]), _p(a["d"]), a["dtype"], _p(a["x"]), _p(a["u"]),
+                                _p(a["T"]), a["B"], a["K"], a["V"], _p(a["tok"]), _p(a["n"]),
+                                _p(a["p"]), _p(a["q"]), _p(a["st"]), _p(a["ws"]), a["wsb"], None)
+
+
+def call_greedy(**kw):
+    args = dict(t=GOOD, dtype=sv.SV_DTYPE_F32, x=GOOD, B=4, K=3, V=64, tok=GOOD, n=GOOD,
+                st=GOOD, ws=WS, wsb=1 << 30)
+    args.update(kw)
+    a = args
+    return sv.lib().spec_verify_greedy(_p(a["t"]), a["dtype"], _p(a["x"]), a["B"], a["K"], a["V"],
+                                       _p(a["tok"]), _p(a["n"]), _p(a["st"]), _p(a["ws"]), a["wsb"],
+                                       None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), sv.SV_ERR_DTYPE),
+    (dict(dtype=-1), sv.SV_ERR_DTYPE),
+    (dict(B=-1), sv.SV_ERR_ARG),
+    (dict(K=-1), sv.SV_ERR_ARG),
+    (dict(V=0), sv.SV_ERR_ARG),
+    (dict(t=0), sv.SV_ERR_ARG),
+    (dict(d=0), sv.SV_ERR_ARG),
+    (dict(x=0), sv.SV_ERR_ARG),
+    (dict(u=0), sv.SV_ERR_ARG),
+    (dict(T=0), sv.SV_ERR_ARG),
+    (dict(tok=0), sv.SV_ERR_ARG),
+    (dict(n=0), sv.SV_ERR_ARG),
+    (dict(st=0), sv.SV_ERR_ARG),
+    (dict(t=GOOD + 1), sv.SV_ERR_ARG),            # bf16 logits need 2-byte alignment
+    (dict(u=GOOD + 2), sv.SV_ERR_ARG),
+    (dict(p=GOOD + 2), sv.SV_ERR_ARG),
+    (dict(ws=0), sv.SV_ERR_WORKSPACE),
+    (dict(ws=WS + 64), sv.SV_ERR_WORKSPACE),      # 256-byte alignment
+    (dict(wsb=16), sv.SV_ERR_WORKSPACE),
+    (dict(B=2 ** 30, K=2 ** 20, V=2 ** 30), sv.SV_ERR_ARG),
+])
+def test_spec_verify_rejects_bad_arguments(kw, status):
+    assert call_verify(**kw) == status
+
+
+def test_spec_verify_edge_shapes_without_launch():
+    assert call_verify(B=0, t=0, d=0, x=0, u=0, T=0, tok=0, n=0, st=0, ws=0, wsb=0) == sv.SV_OK
+    # K == 0 needs no draft logits and no draft tokens, but still the rest
+    assert call_verify(K=0, d=0, x=0, ws=0) == sv.SV_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), sv.SV_ERR_DTYPE),
+    (dict(B=-3), sv.SV_ERR_ARG),
+    (dict(t=0), sv.SV_ERR_ARG),
+    (dict(x=0), sv.SV_ERR_ARG),
+    (dict(t=GOOD + 2), sv.SV_ERR_ARG),            # fp32 logits need 4-byte alignment
+    (dict(wsb=0), sv.SV_ERR_WORKSPACE),
+])
+def test_spec_verify_greedy_rejects_bad_arguments(kw, status):
+    assert call_greedy(**kw) == status
+
+
+def test_fill_uniforms_rejects_bad_arguments():
+    L = sv.lib()
+    assert L.sv_fill_uniforms(1, 0, 0, -1, 4, _p(GOOD), None) == sv.SV_ERR_ARG
+    assert L.sv_fill_uniforms(1, 0, 0, 4, -1, _p(GOOD), None) == sv.SV_ERR_ARG
+    assert L.sv_fill_uniforms(1, 0, 0, 4, 4, None, None) == sv.SV_ERR_ARG
+    assert L.sv_fill_uniforms(1, 0, 0, 4, 4, _p(GOOD + 1), None) == sv.SV_ERR_ARG
+    assert L.sv_fill_uniforms(1, 0, 0, 0, 4, None, None) == sv.SV_OK
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    t = torch.zeros((2, 3, 8))
+    with pytest.raises(ValueError):
+        sv.spec_verify_greedy(t, torch.zeros((2, 2), dtype=torch.int32))

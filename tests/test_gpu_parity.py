@@ -1,0 +1,304 @@
+"""Parity of the HIP verify path (through the C ABI) with the fp64 oracle, on MI355X.
+
+Greedy and data-error results must match bit for bit; sampled results must match
+except on near-ties (see parity_util), with near-ties under 1e-4 of the draws and
+reported probabilities within 1e-5 relative.  Every workload runs at its full size
+(workload 5 compares a sample of its sequences); edge cases cover K = 0, V = 1,
+ragged and misaligned rows, multi-chunk rows, argmax ties, -inf logits, data errors,
+determinism and workspace reuse.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import speculative_decoding_verification_03_amd as sv
+from speculative_decoding_verification_03_amd import workloads as W
+from oracle import philox
+from oracle import spec_verify_oracle as O
+from parity_util import Tally, compare, logits_to_host, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert os.path.exists(sv.lib_path), "libspecverify.so is not built"
+    return torch.device("cuda:0")
+
+
+def gpu_uniforms(seed, step, B, K):
+    return sv.sv_fill_uniforms(seed, 0, step, B, K)
+
+
+def run_sampled(inp, u):
+    out = sv.spec_verify(inp["target"], inp["draft"], inp["tokens"], u, inp["temperature"])
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+def run_greedy(inp):
+    out = sv.spec_verify_greedy(inp["target"], inp["tokens"])
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+def oracle_sampled(inp, u, seqs=None):
+    if seqs is None:
+        return O.verify(logits_to_host(inp["target"]), logits_to_host(inp["draft"]),
+                        inp["tokens"].cpu().numpy(), u.cpu().numpy(),
+                        inp["temperature"].cpu().numpy())
+    idx = torch.tensor(seqs, device=inp["target"].device)
+    r = O.verify(logits_to_host(inp["target"][idx]), logits_to_host(inp["draft"][idx]),
+                 inp["tokens"][idx].cpu().numpy(), u[idx].cpu().numpy(),
+                 inp["temperature"][idx].cpu().numpy())
+    return r
+
+
+def oracle_greedy(inp):
+    return O.verify_greedy(logits_to_host(inp["target"]), inp["tokens"].cpu().numpy())
+
+
+def subset(host_out, seqs):
+    return {k: (None if v is None else v[seqs]) for k, v in host_out.items()}
+
+
+# ------------------------------------------------------------------------------------
+# uniforms
+# ------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed,domain,step,B,K", [
+    (1001, 0, 0, 1, 4), (1004, 0, 7, 256, 8), (2 ** 63 + 5, 3, 2 ** 40, 33, 0),
+    (1005, 0, 1, 1024, 10)])
+def test_uniforms_bit_exact(dev, seed, domain, step, B, K):
+    say(f"uniforms seed={seed} domain={domain} step={step} B={B} K={K}")
+    u = sv.sv_fill_uniforms(seed, domain, step, B, K)
+    torch.cuda.synchronize()
+    ref = np.array(philox.uniforms(seed, domain, step, B, K), dtype=np.float32)
+    assert np.array_equal(u.cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------------------------------
+# the five workloads
+# ------------------------------------------------------------------------------------
+
+def test_workload1_batched_and_single(dev):
+    # 10,000 verify steps of B=1: batched into one call (sequences are independent) ...
+    say("workload 1: 10000 steps as one call")
+    inp = W.make_inputs(1, device=dev, B=10000)
+    u = gpu_uniforms(1001, 0, 10000, inp["K"])
+    tally = compare(run_sampled(inp, u), oracle_sampled(inp, u), range(10000), inp["temperature"].cpu())
+    say("  ", tally)
+    tally.assert_ok("workload 1 batched")
+    # ... and in its own launch configuration, B = 1 per call
+    say("workload 1: 40 single-sequence calls")
+    t1 = Tally()
+    for step in range(40):
+        inp = W.make_inputs(1, step=step, device=dev)
+        u = gpu_uniforms(1001, step, 1, inp["K"])
+        t1.merge(compare(run_sampled(inp, u), oracle_sampled(inp, u), [0], inp["temperature"].cpu()))
+    say("  ", t1)
+    t1.assert_ok("workload 1 single")
+
+
+def test_workload2_sampled_and_greedy(dev):
+    t = Tally()
+    for step in range(12):
+        say(f"workload 2 step {step}")
+        inp = W.make_inputs(2, step=step, device=dev)
+        u = gpu_uniforms(1002, step, inp["B"], inp["K"])
+        t.merge(compare(run_sampled(inp, u), oracle_sampled(inp, u), range(inp["B"]),
+                        inp["temperature"].cpu()))
+        g = compare(run_greedy(inp), oracle_greedy(inp), range(inp["B"]), None, greedy_only=True)
+        g.assert_ok("workload 2 greedy")
+    say("  ", t)
+    t.assert_ok("workload 2 sampled")
+
+
+@pytest.mark.parametrize("cfg,steps", [(3, 2), (4, 2)])
+def test_workload_full_size(dev, cfg, steps):
+    t = Tally()
+    for step in range(steps):
+        say(f"workload {cfg} step {step}: {W.describe(cfg)}")
+        inp = W.make_inputs(cfg, step=step, device=dev)
+        u = gpu_uniforms(1000 + cfg, step, inp["B"], inp["K"])
+        gpu = run_sampled(inp, u)
+        say("   gpu done; oracle ...")
+        t.merge(compare(gpu, oracle_sampled(inp, u), range(inp["B"]), inp["temperature"].cpu()))
+        del inp
+        torch.cuda.empty_cache()
+    say("  ", t)
+    t.assert_ok(f"workload {cfg}")
+
+
+def test_workload5_full_size_sampled_sequences(dev):
+    say(f"workload 5: {W.describe(5)} (11.3 GB of logits)")
+    inp = W.make_inputs(5, device=dev)
+    u = gpu_uniforms(1005, 0, inp["B"], inp["K"])
+    gpu = run_sampled(inp, u)
+    B = inp["B"]
+    seqs = sorted({int(s) for g in range(4) for s in np.linspace(g * B // 4, (g + 1) * B // 4 - 1, 10)})
+    say(f"   gpu done; oracle on {len(seqs)} sequences")
+    orc = oracle_sampled(inp, u, seqs)
+    t = compare(subset(gpu, seqs), orc, range(len(seqs)), inp["temperature"][seqs].cpu())
+    say("  ", t)
+    t.assert_ok("workload 5")
+    # the adversarial group rejects the first draft almost always
+    adv = gpu["accept_len"][3 * B // 4:]
+    assert (adv == 0).mean() > 0.9
+    del inp
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------------------------
+# edge cases
+# ------------------------------------------------------------------------------------
+
+def random_case(dev, B, K, V, dtype, temps, seed, sigma=1.0, scale=2.0):
+    g = torch.Generator(device=dev).manual_seed(seed)
+    zt = scale * torch.randn((B, K + 1, V), generator=g, device=dev)
+    zd = zt[:, :K] + sigma * torch.randn((B, K, V), generator=g, device=dev)
+    T = torch.tensor(temps, dtype=torch.float32)
+    inp = dict(target=zt.to(dtype).contiguous(), draft=zd.to(dtype).contiguous(), temperature=T.to(dev))
+    inp["tokens"] = W._draft_tokens(inp["draft"], T, g)
+    return inp
+
+
+EDGE = [
+    # B, K, V, dtype, temperatures
+    (3, 0, 1000, torch.float32, [1.0, 0.0, 0.5]),        # K = 0: plain sampling / argmax
+    (2, 3, 1, torch.bfloat16, [1.0, 0.0]),               # V = 1
+    (4, 2, 7, torch.bfloat16, [0.3, 1.0, 0.0, 2.0]),     # V smaller than a vector
+    (5, 4, 1001, torch.bfloat16, [1.0, 0.7, 0.0, 1.3, 0.2]),  # ragged, misaligned rows
+    (3, 5, 1003, torch.float32, [1.0, 0.0, 0.9]),        # ragged fp32
+    (2, 6, 40000, torch.bfloat16, [1.0, 0.8]),           # several chunks per row
+    (1, 12, 70001, torch.bfloat16, [0.6]),               # long K, several chunks, ragged
+    (6, 3, 130000, torch.float32, [1.0, 0.0, 0.05, 1.2, 0.0, 0.5]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(EDGE)))
+def test_edge_shapes(dev, case):
+    B, K, V, dt, temps = EDGE[case]
+    say(f"edge case {case}: B={B} K={K} V={V} {dt} T={temps}")
+    t = Tally()
+    for rep in range(3):
+        inp = random_case(dev, B, K, V, dt, temps, seed=100 * case + rep)
+        u = gpu_uniforms(77 + case, rep, B, K)
+        t.merge(compare(run_sampled(inp, u), oracle_sampled(inp, u), range(B), inp["temperature"].cpu()))
+        g = compare(run_greedy(inp), oracle_greedy(inp), range(B), None, greedy_only=True)
+        g.assert_ok(f"edge {case} greedy")
+    say("  ", t)
+    t.assert_ok(f"edge {case}")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_greedy_ties_bit_exact(dev, dt):
+    say(f"greedy ties {dt}")
+    g = torch.Generator(device=dev).manual_seed(5)
+    for V in (3, 64, 4096 + 5, 40000):
+        B, K = 16, 4
+        z = torch.randint(0, 3, (B, K + 1, V), generator=g, device=dev).to(torch.float32)
+        z[:4] = 1.0  # rows that are entirely ties
+        z[4:8, :, V // 2:] = 5.0  # ties spanning many threads and chunks
+        target = z.to(dt).contiguous()
+        amax = torch.argmax(z, dim=-1).to(torch.int32)
+        tokens = amax[:, :K].clone()
+        tokens[::3, 1] = (tokens[::3, 1] + 1) % V
+        inp = dict(target=target, tokens=tokens.contiguous())
+        r = compare(run_greedy(inp), oracle_greedy(inp), range(B), None, greedy_only=True)
+        r.assert_ok(f"ties V={V}")
+        inp["draft"] = target[:, :K].contiguous()
+        inp["temperature"] = torch.zeros(B, device=dev)
+        u = gpu_uniforms(3, V, B, K)
+        r = compare(run_sampled(inp, u), oracle_sampled(inp, u), range(B), inp["temperature"].cpu())
+        r.assert_ok(f"ties via spec_verify V={V}")
+
+
+def test_neg_inf_logits(dev):
+    say("-inf logits")
+    B, K, V = 6, 3, 5000
+    inp = random_case(dev, B, K, V, torch.bfloat16, [1.0, 0.5, 0.0, 1.0, 2.0, 0.8], seed=9)
+    tgt = inp["target"].float()
+    tgt[:, :, ::3] = -float("inf")       # a third of the vocabulary impossible for p
+    drf = inp["draft"].float()
+    drf[:, :, 1::3] = -float("inf")      # another third impossible for q
+    inp["target"] = tgt.to(torch.bfloat16).contiguous()
+    inp["draft"] = drf.to(torch.bfloat16).contiguous()
+    inp["tokens"] = W._draft_tokens(inp["draft"], inp["temperature"].cpu(), torch.Generator(device=dev).manual_seed(1))
+    u = gpu_uniforms(9, 0, B, K)
+    t = compare(run_sampled(inp, u), oracle_sampled(inp, u), range(B), inp["temperature"].cpu())
+    say("  ", t)
+    t.assert_ok("-inf")
+
+
+def test_data_errors_flagged_like_oracle(dev):
+    say("data errors")
+    B, K, V = 12, 3, 3000
+    temps = [1.0, 0.0, 1.0, 0.0, 1.0, 1.0, 0.5, 1.0, 0.0, 1.0, 1.0, 1.0]
+    inp = random_case(dev, B, K, V, torch.float32, temps, seed=4)
+    tgt, drf, tok = inp["target"], inp["draft"], inp["tokens"]
+    tgt[0, 1, 17] = float("nan")         # NaN in a target row, sampled
+    tgt[1, 2, 5] = float("nan")          # NaN, greedy
+    tgt[2, 0, 9] = float("inf")          # +inf is an error when sampled ...
+    tgt[3, 0, 9] = float("inf")          # ... and legal when greedy
+    tgt[4, 3, :] = -float("inf")         # a whole row impossible
+    drf[5, 2, 100] = float("nan")        # NaN in a draft row
+    tok[6, 1] = V                        # token out of range
+    drf[8, 0, 0] = float("nan")          # greedy never reads draft rows
+    T = inp["temperature"]
+    T[7] = -1.0                          # bad temperature
+    T[9] = 1e-40                         # subnormal temperature
+    u = gpu_uniforms(4, 0, B, K)
+    u[10, 1] = 1.0                       # uniform outside [0, 1)
+    u[11, 3] = float("nan")
+    t = compare(run_sampled(inp, u), oracle_sampled(inp, u), range(B), T.cpu())
+    t.assert_ok("data errors")
+    g = compare(run_greedy(inp), oracle_greedy(inp), range(B), None, greedy_only=True)
+    g.assert_ok("data errors greedy")
+
+
+def test_small_temperature_equals_greedy(dev):
+    say("T -> 0 against greedy")
+    B, K, V = 32, 5, 20000
+    inp = random_case(dev, B, K, V, torch.float32, [1e-3] * B, seed=21, sigma=3.0)
+    zt = inp["target"]
+    # unique maxima well above the runner-up in every row
+    for z in (inp["target"], inp["draft"]):
+        top = torch.topk(z, 2, dim=-1)
+        z.scatter_(2, top.indices[..., :1], top.values[..., 1:] + 0.5)
+    inp["tokens"] = torch.argmax(inp["draft"], dim=-1).to(torch.int32).contiguous()
+    u = gpu_uniforms(21, 0, B, K).clamp_min(2.0 ** -24)
+    s = run_sampled(inp, u)
+    gr = run_greedy(inp)
+    assert np.array_equal(s["tokens"], gr["tokens"]) and np.array_equal(s["accept_len"], gr["accept_len"])
+    del zt
+
+
+def test_deterministic_and_workspace_reuse(dev):
+    say("determinism and workspace reuse")
+    inp = W.make_inputs(3, device=dev, B=16)
+    u = gpu_uniforms(1003, 5, 16, inp["K"])
+    ws = sv.Workspace(dev)
+    a = to_host(sv.spec_verify(inp["target"], inp["draft"], inp["tokens"], u, inp["temperature"], workspace=ws))
+    g1 = to_host(sv.spec_verify_greedy(inp["target"], inp["tokens"], workspace=ws))
+    small = random_case(dev, 3, 2, 999, torch.bfloat16, [1.0, 0.0, 0.4], seed=3)
+    us = gpu_uniforms(2, 2, 3, 2)
+    c1 = to_host(sv.spec_verify(small["target"], small["draft"], small["tokens"], us, small["temperature"], workspace=ws))
+    b = to_host(sv.spec_verify(inp["target"], inp["draft"], inp["tokens"], u, inp["temperature"], workspace=ws))
+    g2 = to_host(sv.spec_verify_greedy(inp["target"], inp["tokens"], workspace=ws))
+    c2 = to_host(sv.spec_verify(small["target"], small["draft"], small["tokens"], us, small["temperature"]))
+    torch.cuda.synchronize()
+    for x, y in ((a, b), (g1, g2), (c1, c2)):
+        for k in x:
+            if x[k] is not None:
+                assert np.array_equal(x[k], y[k], equal_nan=True), k
+    t = compare(a, oracle_sampled(inp, u), range(16), inp["temperature"].cpu())
+    t.assert_ok("reuse")
