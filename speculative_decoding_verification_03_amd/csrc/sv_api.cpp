@@ -51,13 +51,15 @@ bool shape_ok(int B, int K, int V) {
     return true;
 }
 
-// Workspace for both entry points: the larger layout, region by region.
-Layout layout_for(int B, int K, int V, int rows_per_seq) { return sv::make_layout(B, K, V, rows_per_seq); }
-
+// Workspace for both entry points: the larger of the two layouts.
 size_t workspace_need(int B, int K, int V) {
-    const Layout a = layout_for(B, K, V, 2 * K + 1);
-    const Layout b = layout_for(B, K, V, K + 1);
-    return a.total > b.total ? a.total : b.total;
+    size_t need = 0;
+    for (int esize : {2, 4})
+        for (int R : {2 * K + 1, K + 1}) {
+            const size_t t = sv::make_layout(B, K, V, esize, R).total;
+            if (t > need) need = t;
+        }
+    return need;
 }
 
 bool grid_ok(int B, int R, const Layout& L) {
@@ -86,13 +88,10 @@ sv::VerifyArgs make_args(const void* target, const void* draft, const int32_t* t
     a.ch1 = L.ch1;
     a.nchunk2 = L.nchunk2;
     a.ch2 = L.ch2;
-    a.part1 = reinterpret_cast<sv::RowPartial*>(ws + L.off_part1);
     a.desc = reinterpret_cast<sv::SeqDesc*>(ws + L.off_desc);
-    a.part2a = reinterpret_cast<sv::NormPartial*>(ws + L.off_part2a);
-    a.part2b = reinterpret_cast<double*>(ws + L.off_part2b);
-    // per-sequence completion counters: zeroed by the first kernel of every call
-    a.cnt1 = reinterpret_cast<uint32_t*>(ws + L.off_cnt1);
-    a.cnt2 = reinterpret_cast<uint32_t*>(ws + L.off_cnt2);
+    a.part1 = reinterpret_cast<sv::RowPartial*>(ws + L.off_part1);
+    a.part2 = reinterpret_cast<sv::DrawPartial*>(ws + L.off_part2);
+    a.unc = reinterpret_cast<sv::UncEntry*>(ws + L.off_unc);
     a.out_tokens = out_tokens;
     a.out_n = out_n;
     a.out_p = out_p;
@@ -150,7 +149,7 @@ sv_status spec_verify(const void* target_logits, const void* draft_logits, int d
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < workspace_need(B, K, V))
         return SV_ERR_WORKSPACE;
     const int R = 2 * K + 1;
-    const Layout L = layout_for(B, K, V, R);
+    const Layout L = sv::make_layout(B, K, V, (int)esz, R);
     if (!grid_ok(B, R, L)) return SV_ERR_ARG;
 
     const sv::VerifyArgs a = make_args(target_logits, draft_logits, draft_tokens, uniforms,
@@ -162,11 +161,11 @@ sv_status spec_verify(const void* target_logits, const void* draft_logits, int d
         for (auto& e : ev) e = g_prof.next();
         g_prof.calls++;
     }
-    if (sv::launch_zero_counters(a, stream) != 0) return SV_ERR_HIP;
     if (g_prof.on) g_prof.record(ev[0], stream);
-    if (sv::launch_pass1(a, bf16, stream) != 0) return SV_ERR_HIP;
+    if (sv::launch_pass1(a, bf16, 0, B, stream) != 0) return SV_ERR_HIP;
     if (g_prof.on) g_prof.record(ev[1], stream);
-    if (sv::launch_pass2(a, bf16, stream) != 0) return SV_ERR_HIP;
+    if (sv::launch_resolve(a, bf16, 0, B, stream) != 0) return SV_ERR_HIP;
+    if (sv::launch_draw(a, bf16, 0, B, stream) != 0) return SV_ERR_HIP;
     if (g_prof.on) g_prof.record(ev[2], stream);
     return SV_OK;
 }
@@ -189,24 +188,23 @@ sv_status spec_verify_greedy(const void* target_logits, int dtype,
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < workspace_need(B, K, V))
         return SV_ERR_WORKSPACE;
     const int R = K + 1;
-    const Layout L = layout_for(B, K, V, R);
+    const Layout L = sv::make_layout(B, K, V, (int)esz, R);
     if (!grid_ok(B, R, L)) return SV_ERR_ARG;
 
     const sv::VerifyArgs a = make_args(target_logits, nullptr, draft_tokens, nullptr, nullptr, B,
-                                       K, V, R, L, workspace, out_tokens, out_accept_len,
-                                       nullptr, nullptr, out_status);
+                                       K, V, R, L, workspace, out_tokens, out_accept_len, nullptr,
+                                       nullptr, out_status);
     hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
     if (g_prof.on) {
         for (auto& e : ev) e = g_prof.next();
         g_prof.calls++;
     }
-    if (sv::launch_zero_counters(a, stream) != 0) return SV_ERR_HIP;
+    const int bf16 = dtype == SV_DTYPE_BF16;
     if (g_prof.on) g_prof.record(ev[0], stream);
-    if (sv::launch_pass1(a, dtype == SV_DTYPE_BF16, stream) != 0) return SV_ERR_HIP;
-    if (g_prof.on) {
-        g_prof.record(ev[1], stream);
-        g_prof.record(ev[2], stream);
-    }
+    if (sv::launch_pass1(a, bf16, 0, B, stream) != 0) return SV_ERR_HIP;
+    if (g_prof.on) g_prof.record(ev[1], stream);
+    if (sv::launch_resolve(a, bf16, 0, B, stream) != 0) return SV_ERR_HIP;
+    if (g_prof.on) g_prof.record(ev[2], stream);
     return SV_OK;
 }
 

@@ -7,13 +7,8 @@
 
 namespace sv {
 
-constexpr int kThreads = 256;  // every kernel: 4 wave64 per workgroup
+constexpr int kThreads = 256;  // workgroup size of the streaming, sweep and final kernels
 constexpr int kWaves = kThreads / 64;
-
-// Pass-2 descriptor modes.
-constexpr int kModeNone = 0;      // greedy, failed, or nothing to draw
-constexpr int kModeResidual = 1;  // draw from (p_n - q_n)+
-constexpr int kModeBonus = 2;     // draw from p_K
 
 // Per-sequence status flags (same values as the public SV_SEQ_* macros).
 constexpr int kSeqErrToken = 1;
@@ -22,62 +17,85 @@ constexpr int kSeqErrTemperature = 4;
 constexpr int kSeqErrUniform = 8;
 constexpr int kSeqNoteFallback = 16;
 
+// Draw modes handed from the resolve to the sweep and final kernels.
+constexpr int kModeNone = 0;      // greedy or failed: outputs complete after the resolve
+constexpr int kModeResidual = 1;  // draw from (p_n - q_n)+
+constexpr int kModeBonus = 2;     // draw from p_K
+
 // One (row, chunk) result of pass 1.  Greedy rows: m = chunk max, idx = lowest index
-// reaching it.  Sampled rows: m = chunk max, s = sum_i exp((z_i - m) / T) over the chunk.
+// reaching it.  Sampled rows: m = chunk max, s = sum_i 2^((z_i - m) * c2) over the chunk,
+// c2 = fp32(log2(e) / T) (fp32 exponentials, fp64 sum).
 struct alignas(16) RowPartial {
     float m;
     int32_t idx;
     double s;
 };
 
-// Work item handed from the resolve to pass 2, one per sequence.
-struct alignas(32) SeqDesc {
-    int32_t mode;   // kMode*
-    int32_t n;      // accepted drafts: the row pair (residual) or K (bonus)
-    float T;        // temperature
-    float mt;       // max of target row n
-    float md;       // max of draft row n (residual only)
-    float u;        // uniform of the final draw
-    int32_t status; // flags so far
-    int32_t pad;
+// The resolve's result for one sequence.
+struct alignas(16) SeqDesc {
+    int32_t mode;  // kMode*
+    int32_t n;     // accepted drafts = row of the draw
+    float T;       // temperature
+    float u;       // uniform of the final draw
+    float mt, md;  // maxima of target row n and draft row n
+    double St, Sd; // pass-1 normalisers of those rows: sum exp((z - m) / T)
+    int32_t pad[2];
 };
 
-// Pass-2 normaliser partials for one chunk of the rejected row pair.
-struct alignas(16) NormPartial {
-    double sp;
-    double sq;
+// Sweep results per (sequence, chunk, wave sub-chunk), fp64, with
+//   a_i = exp((zt_i - mt)/T) and b_i = exp((zd_i - md)/T):
+//   sp, sq = sum a_i, sum b_i;
+//   A, B   = sums of a_i, b_i over the positions whose residual is certainly positive;
+//   Eq     = sum of a_i over the positions with zt_i - mt == zd_i - md exactly (a_i == b_i);
+//   nunc   = the positions left undecided, whose (a, b, i) are kept in up to kUnc slots.
+// Bonus draws use sp only.
+constexpr int kUnc = 8;
+struct alignas(16) DrawPartial {
+    double sp, sq, A, B, Eq;
+    int32_t nunc;  // undecided positions seen (may exceed kUnc: the slots are then incomplete)
+    int32_t pad;
 };
+struct alignas(16) UncEntry {
+    double a, b;
+    int64_t i;
+    int64_t pad;
+};
+
+constexpr int kSubUnit = 512;  // sub-chunks are multiples of 64 lanes x 8 positions
 
 struct Layout {
     int nchunk1, ch1;  // pass-1 chunks per row and elements per chunk (multiple of 64)
-    int nchunk2, ch2;  // pass-2 chunks per row and elements per chunk (multiple of 256)
-    size_t off_part1, off_cnt1, off_desc, off_part2a, off_part2b, off_cnt2, total;
+    int nchunk2, ch2;  // sweep chunks per row and positions per chunk (kWaves sub-chunks)
+    size_t off_desc, off_part1, off_part2, off_unc, total;
 };
 
-// Pass-1 chunking: aim for enough workgroups to fill the chip, never chunks shorter
-// than kMinChunk1 elements.  The same function sizes the workspace and the launches.
+// Pass-1 chunks of about kChunkBytes1 (long streams per workgroup), more when the batch
+// is too small to fill the chip, never shorter than kMinChunk1 elements.
+constexpr int64_t kChunkBytes1 = 76 * 1024;
 constexpr int kTargetBlocks1 = 4096;
 constexpr int kMinChunk1 = 4096;
 constexpr int kTargetBlocks2 = 2048;
-constexpr int kMinChunk2 = 2048;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-inline void chunking(int64_t rows, int64_t seqs, int V, int& nchunk1, int& ch1,
+inline void chunking(int64_t rows, int64_t seqs, int V, int esize, int& nchunk1, int& ch1,
                      int& nchunk2, int& ch2) {
+    int64_t by_bytes = ceil_div((int64_t)V * esize, kChunkBytes1);
     int64_t want = rows > 0 ? ceil_div(kTargetBlocks1, rows) : 1;
     int64_t maxc = V / kMinChunk1;
     if (maxc < 1) maxc = 1;
-    int64_t n = want < 1 ? 1 : (want > maxc ? maxc : want);
+    if (want > maxc) want = maxc;
+    int64_t n = by_bytes > want ? by_bytes : want;
+    if (n < 1) n = 1;
     int64_t ch = ceil_div(ceil_div(V, n), 64) * 64;
     nchunk1 = (int)ceil_div(V, ch);
     ch1 = (int)ch;
 
+    const int64_t unit = (int64_t)kWaves * kSubUnit;
     want = seqs > 0 ? ceil_div(kTargetBlocks2, seqs) : 1;
-    maxc = V / kMinChunk2;
-    if (maxc < 1) maxc = 1;
+    maxc = ceil_div(V, unit);
     n = want < 1 ? 1 : (want > maxc ? maxc : want);
-    ch = ceil_div(ceil_div(V, n), 256) * 256;
+    ch = ceil_div(ceil_div(V, n), unit) * unit;
     nchunk2 = (int)ceil_div(V, ch);
     ch2 = (int)ch;
 }
@@ -85,23 +103,18 @@ inline void chunking(int64_t rows, int64_t seqs, int V, int& nchunk1, int& ch1,
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // rows_per_seq = 2K+1 for spec_verify, K+1 for spec_verify_greedy.
-inline Layout make_layout(int B, int K, int V, int rows_per_seq) {
+inline Layout make_layout(int B, int K, int V, int esize, int rows_per_seq) {
     Layout L;
-    chunking((int64_t)B * rows_per_seq, B, V, L.nchunk1, L.ch1, L.nchunk2, L.ch2);
-    // completion counters first; every call zeroes them before its first kernel
+    chunking((int64_t)B * rows_per_seq, B, V, esize, L.nchunk1, L.ch1, L.nchunk2, L.ch2);
     size_t off = 0;
-    L.off_cnt1 = off;
-    off = align256(off + sizeof(uint32_t) * (size_t)B);
-    L.off_cnt2 = off;
-    off = align256(off + sizeof(uint32_t) * (size_t)B);
     L.off_desc = off;
     off = align256(off + sizeof(SeqDesc) * (size_t)B);
     L.off_part1 = off;
     off = align256(off + sizeof(RowPartial) * (size_t)B * rows_per_seq * L.nchunk1);
-    L.off_part2a = off;
-    off = align256(off + sizeof(NormPartial) * (size_t)B * L.nchunk2);
-    L.off_part2b = off;
-    off = align256(off + sizeof(double) * kWaves * (size_t)B * L.nchunk2);
+    L.off_part2 = off;
+    off = align256(off + sizeof(DrawPartial) * kWaves * (size_t)B * L.nchunk2);
+    L.off_unc = off;
+    off = align256(off + sizeof(UncEntry) * kUnc * kWaves * (size_t)B * L.nchunk2);
     L.total = off;
     return L;
 }
@@ -114,12 +127,10 @@ struct VerifyArgs {
     const float* temperature;  // [B] (null when greedy-only)
     int B, K, V, R;            // R = rows per sequence handled by pass 1
     int nchunk1, ch1, nchunk2, ch2;
-    RowPartial* part1;
-    uint32_t* cnt1;
     SeqDesc* desc;
-    NormPartial* part2a;
-    double* part2b;
-    uint32_t* cnt2;
+    RowPartial* part1;
+    DrawPartial* part2;        // [B][nchunk2][kWaves]
+    UncEntry* unc;             // [B][nchunk2][kWaves][kUnc]
     int32_t* out_tokens;
     int32_t* out_n;
     float* out_p;
@@ -127,10 +138,10 @@ struct VerifyArgs {
     int32_t* out_status;
 };
 
-// Internal launchers (return hipError_t as int; 0 = success).
-int launch_zero_counters(const VerifyArgs& a, void* stream);
-int launch_pass1(const VerifyArgs& a, int bf16, void* stream);
-int launch_pass2(const VerifyArgs& a, int bf16, void* stream);
+// Internal launchers (return hipError_t as int; 0 = success).  Sequences [b0, b1).
+int launch_pass1(const VerifyArgs& a, int bf16, int b0, int b1, void* stream);
+int launch_resolve(const VerifyArgs& a, int bf16, int b0, int b1, void* stream);
+int launch_draw(const VerifyArgs& a, int bf16, int b0, int b1, void* stream);
 int launch_uniforms(uint64_t seed, uint64_t domain, uint64_t step, int B, int K, float* u,
                     void* stream);
 

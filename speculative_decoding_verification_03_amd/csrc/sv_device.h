@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "sv_common.h"
@@ -31,8 +32,11 @@ template <>
 struct Logit<float> {
     static constexpr int kVec = 4;  // elements per 16-byte load
     __device__ static __forceinline__ float at(const float* p, int64_t i) { return p[i]; }
-    __device__ static __forceinline__ void vec(const float* p, float (&z)[4]) {
-        const u32x4 v = load16(p);
+    __device__ static __forceinline__ u32x4 neg_inf16() {
+        const uint32_t n = 0xff800000u;
+        return u32x4{n, n, n, n};
+    }
+    __device__ static __forceinline__ void unpack(u32x4 v, float (&z)[4]) {
         z[0] = __uint_as_float(v.x); z[1] = __uint_as_float(v.y);
         z[2] = __uint_as_float(v.z); z[3] = __uint_as_float(v.w);
     }
@@ -44,14 +48,74 @@ struct Logit<uint16_t> {
     __device__ static __forceinline__ float at(const uint16_t* p, int64_t i) {
         return __uint_as_float((uint32_t)p[i] << 16);
     }
-    __device__ static __forceinline__ void vec(const uint16_t* p, float (&z)[8]) {
-        const u32x4 v = load16(p);
+    __device__ static __forceinline__ u32x4 neg_inf16() {
+        const uint32_t n = 0xff80ff80u;  // two bf16 -inf
+        return u32x4{n, n, n, n};
+    }
+    __device__ static __forceinline__ void unpack(u32x4 v, float (&z)[8]) {
         z[0] = bf16_lo(v.x); z[1] = bf16_hi(v.x);
         z[2] = bf16_lo(v.y); z[3] = bf16_hi(v.y);
         z[4] = bf16_lo(v.z); z[5] = bf16_hi(v.z);
         z[6] = bf16_lo(v.w); z[7] = bf16_hi(v.w);
     }
 };
+
+// ---------------------------------------------------------------------------------
+// fp64 2^y for the categorical draws (about 12 VALU operations and one LDS read):
+// y = k/256 + f with k = rint(256 y) and |f| <= 1/512;  2^y = 2^(k>>8) * 2^((k&255)/256) * 2^f,
+// the middle factor from a 256-entry table, 2^f from its Taylor series in f*ln2 to degree 4
+// (truncation below 4e-17).  rint comes from adding 1.5 * 2^52, which leaves k in the low
+// word of the sum.  y is clamped at -1080, which maps -inf and every argument that
+// underflows to 0.  Relative error a few 1e-16.
+// ---------------------------------------------------------------------------------
+
+constexpr int kExpTable = 256;
+
+// Fill the table (kExpTable doubles of LDS) once per workgroup; contains __syncthreads().
+// 2^x for x = j/256 in [0, 1) from the Taylor series of exp(x ln2) to degree 17 (truncation
+// below 2e-19), evaluated by Horner: a few registers, unlike a library exp2.
+__device__ __forceinline__ void exp2_table_init(double* t) {
+    constexpr double c[18] = {1.0,
+                              0.6931471805599453,
+                              0.2402265069591007,
+                              0.055504108664821576,
+                              0.009618129107628477,
+                              0.0013333558146428441,
+                              0.00015403530393381606,
+                              1.5252733804059838e-05,
+                              1.3215486790144305e-06,
+                              1.0178086009239696e-07,
+                              7.054911620801121e-09,
+                              4.44553827187081e-10,
+                              2.5678435993488196e-11,
+                              1.3691488853904124e-12,
+                              6.778726354822543e-14,
+                              3.132436707088427e-15,
+                              1.357024794875514e-16,
+                              5.533046532458238e-18};
+    for (int j = threadIdx.x; j < kExpTable; j += blockDim.x) {
+        const double x = (double)j / kExpTable;
+        double p = c[17];
+#pragma unroll
+        for (int n = 16; n >= 0; --n) p = __builtin_fma(p, x, c[n]);
+        t[j] = p;
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ double exp2_64(double y, const double* t) {
+    constexpr double kRound = 6755399441055744.0;  // 1.5 * 2^52
+    y = fmax(y, -1080.0);
+    const double tk = __builtin_fma(y, 256.0, kRound);
+    const int k = __double2loint(tk);
+    const double f = __builtin_fma(tk - kRound, -1.0 / 256.0, y);
+    double p = 0.009618129107628477;
+    p = __builtin_fma(p, f, 0.055504108664821576);
+    p = __builtin_fma(p, f, 0.2402265069591007);
+    p = __builtin_fma(p, f, 0.6931471805599453);
+    p = __builtin_fma(p, f, 1.0);
+    return ldexp(t[k & (kExpTable - 1)] * p, k >> 8);
+}
 
 // ---------------------------------------------------------------------------------
 // wavefront reductions (butterfly: every lane ends with the same value)

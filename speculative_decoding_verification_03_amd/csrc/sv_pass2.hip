@@ -1,22 +1,32 @@
-// Pass 2 of the verify step: the one categorical draw of each sampled sequence.
+// Pass 2 of the verify step: the resolve and the one categorical draw of each sequence.
 //
-// After a rejection at position n the draw uses (p_n - q_n)+, the positive part of
-// the pointwise difference over the whole vocabulary ("A Regra de Exatidão" on the
-// lesson page "Decodificação Especulativa e EAGLE"; the livestream "IA local 202"
-// describes the same clamp-and-normalise at [12:30]).  After K acceptances it uses p_K
-// (the bonus token, "O Conceito" step 4).  Only the row pair (or the one row) of that
-// draw is read again.
+// resolve_kernel (one wave per sequence): validation, then the left-to-right test
+// r_t < p_t(x_t)/q_t(x_t) of "A Regra de Exatidão" (lesson page "Decodificação
+// Especulativa e EAGLE"), evaluated in fp64 log space from the pass-1 row statistics, or
+// for T = 0 the greedy comparison argmax(p_t) == x_t ("Caso ganancioso").  n = the first
+// failing position (K if none).  Writes every output except the drawn token of a sampled
+// sequence, and a SeqDesc for the draw.
 //
-// Everything here is fp64: normalisers, weights and prefix sums.  An fp32 weight
-// carries a relative error near 1e-7, which at V ~ 1.5e5 moves CDF edges by far more
-// than the width of most cells, so fp32 would change the drawn token on a visible
-// fraction of draws; fp64 keeps those changes below 1e-9 per draw.
+// The draw.  After a rejection at n the token comes from (p_n - q_n)+, the positive part
+// of the pointwise difference over the whole vocabulary ("A Regra de Exatidão"; the
+// livestream "IA local 202" describes the same clamp-and-normalise at [12:30]); after K
+// acceptances from p_K (the bonus token, "O Conceito" step 4).  Only that row pair (or
+// row) is read again.  It is all fp64: an fp32 weight carries a relative error near 1e-7,
+// which at V ~ 1.5e5 moves CDF edges past many narrow cells and would change the drawn
+// token on a visible fraction of draws.
 //
-//   p2_norm_kernel   (residual only) per chunk: sum exp((zt - mt)/T), sum exp((zd - md)/T)
-//   p2_sample_kernel per chunk and wave: sums of the draw weights over contiguous
-//                    sub-chunks; the workgroup that finishes the last chunk of a
-//                    sequence scans the sub-chunk sums, finds the sub-chunk holding
-//                    u * S and scans inside it: token = min{ i : C_i > u * S }.
+// sweep_kernel (sequence x chunk workgroups, one contiguous sub-chunk per wave): exact
+// a_i = exp((zt_i - mt)/T), b_i = exp((zd_i - md)/T); their sums S_p, S_q; the sums A, B of
+// a_i, b_i over the positions whose residual is positive for every rho = S_p/S_q within
+// 1 +- kDelta of the pass-1 estimate rho' = S_p'/S_q'; the sum Eq of a_i over positions
+// with a_i == b_i exactly (their residual sign is that of 1/S_p - 1/S_q).  The few
+// positions between the two bounds are kept as (a_i, b_i, i).
+//
+// final_kernel (one workgroup per sequence): checks rho against rho' (else one exact
+// sweep by this workgroup), forms each sub-chunk's residual mass
+// A/S_p - B/S_q + Eq (1/S_p - 1/S_q)+ plus its kept terms, scans the masses for u * W,
+// and scans inside the sub-chunk that holds it: token = min{ i : C_i > u * W }, C the
+// prefix sums in index order.
 #include <float.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -28,137 +38,576 @@ namespace sv {
 
 namespace {
 
+constexpr double kLog2eD = 1.4426950408889634;
+// Classification margin around rho' and the acceptance test of rho: pass-1 normalisers
+// are within ~1e-6 of the fp64 ones, so kDelta / 2 leaves a wide guard.
+constexpr double kDelta = 8e-6;
+// Positions whose a_i and b_i are both below 2^-80 of their row maxima are skipped: over
+// any vocabulary they move the sums and CDF edges by less than V * 2^-80.
+constexpr double kSkipLog2 = -80.0;
+// Kept (uncertain) positions per sequence handled in the final kernel; more falls back
+// to the exact sweep.
+constexpr int kUncSeq = 256;
+
+// Sweep shape: 16-byte vectors per row whose loads are in flight together per lane, and
+// positions whose exponentials are computed together (register pressure against overlap).
+#ifndef SV_SWEEP_VECTORS
+#define SV_SWEEP_VECTORS 2
+#endif
+#ifndef SV_SWEEP_POSITIONS
+#define SV_SWEEP_POSITIONS 4
+#endif
+
+// ------------------------------------------------------------------------------------
+// the resolve
+// ------------------------------------------------------------------------------------
+
+__device__ __forceinline__ bool row_bad(float m, bool sampled) {
+    return (m != m) || m == -INFINITY || (sampled && m == INFINITY);
+}
+
+__device__ __forceinline__ bool temperature_bad(float T) {
+    return (T != T) || T < 0.0f || T == INFINITY || (T > 0.0f && T < FLT_MIN);
+}
+
+// Row j (0..K target, K+1..2K draft) of sequence b: max over chunks (NaN if any chunk saw
+// a NaN) and the lowest index reaching it.
+__device__ __forceinline__ void merge_greedy(const VerifyArgs& a, int b, int j, float& m, int& idx) {
+    const RowPartial* p = a.part1 + ((int64_t)b * a.R + j) * a.nchunk1;
+    m = -INFINITY;
+    idx = 0x7fffffff;
+    bool bad = false;
+    for (int c = 0; c < a.nchunk1; ++c) {
+        const RowPartial q = p[c];
+        if (q.m != q.m) bad = true;
+        else if (q.m > m) {  // strict: an earlier chunk keeps ties
+            m = q.m;
+            idx = q.idx;
+        }
+    }
+    if (bad) m = __builtin_nanf("");
+}
+
+// Sampled row j: max m and S = sum exp((z - m)/T), from chunk partials in the
+// 2^((z - m) * c2) form.
+__device__ __forceinline__ void merge_sampled(const VerifyArgs& a, int b, int j, float c2, float& m,
+                                              double& S) {
+    const RowPartial* p = a.part1 + ((int64_t)b * a.R + j) * a.nchunk1;
+    m = -INFINITY;
+    for (int c = 0; c < a.nchunk1; ++c) m = nmax(m, p[c].m);
+    S = 0.0;
+    for (int c = 0; c < a.nchunk1; ++c) {
+        const RowPartial q = p[c];
+        if (q.s != 0.0) S += q.s * exp2(((double)q.m - (double)m) * (double)c2);
+    }
+}
+
+// One wave per sequence.
+template <typename E>
+__global__ __launch_bounds__(64) void resolve_kernel(VerifyArgs a, int b0) {
+    const int b = b0 + blockIdx.x;
+    const int lane = threadIdx.x;
+    const int K = a.K, V = a.V;
+    const float T = a.temperature ? a.temperature[b] : 0.0f;
+    const bool sampled = !(T == 0.0f);
+    const int32_t* x = a.tokens + (int64_t)b * K;
+    const float c2 = sampled ? (float)(kLog2eD / (double)T) : 0.0f;
+    int32_t* tok = a.out_tokens + (int64_t)b * (K + 1);
+    float* op = a.out_p ? a.out_p + (int64_t)b * K : nullptr;
+    float* oq = a.out_q ? a.out_q + (int64_t)b * K : nullptr;
+    SeqDesc d{};
+    d.T = T;
+
+    // ---- validation: every row read, every token, every uniform ----
+    int err = 0;
+    if (lane == 0 && temperature_bad(T)) err |= kSeqErrTemperature;
+    for (int t = lane; t < K; t += 64) {
+        const int xt = x[t];
+        if (xt < 0 || xt >= V) err |= kSeqErrToken;
+    }
+    for (int j = lane; j < a.R; j += 64) {
+        if (j > K && !sampled) continue;
+        const RowPartial* p = a.part1 + ((int64_t)b * a.R + j) * a.nchunk1;
+        float m = -INFINITY;
+        for (int c = 0; c < a.nchunk1; ++c) m = nmax(m, p[c].m);
+        if (row_bad(m, sampled)) err |= kSeqErrLogit;
+    }
+    if (sampled) {
+        const float* u = a.uniforms + (int64_t)b * (K + 1);
+        for (int t = lane; t <= K; t += 64) {
+            const float ut = u[t];
+            if (!(ut >= 0.0f && ut < 1.0f)) err |= kSeqErrUniform;
+        }
+    }
+    err = wave_or(err);
+    if (err) {
+        for (int t = lane; t <= K; t += 64) tok[t] = -1;
+        for (int t = lane; t < K; t += 64) {
+            if (op) op[t] = __builtin_nanf("");
+            if (oq) oq[t] = __builtin_nanf("");
+        }
+        if (lane == 0) {
+            a.out_n[b] = -1;
+            a.out_status[b] = err;
+            d.mode = kModeNone;
+            a.desc[b] = d;
+        }
+        return;
+    }
+
+    // ---- the first position that fails ----
+    int first = K;
+    if (!sampled) {
+        for (int t = lane; t < K; t += 64) {
+            float m;
+            int i;
+            merge_greedy(a, b, t, m, i);
+            if (i != x[t]) first = min(first, t);
+            if (op) op[t] = __builtin_nanf("");
+            if (oq) oq[t] = __builtin_nanf("");
+        }
+    } else {
+        const float* u = a.uniforms + (int64_t)b * (K + 1);
+        for (int t = lane; t < K; t += 64) {
+            const int xt = x[t];
+            float mt, md;
+            double St, Sd;
+            merge_sampled(a, b, t, c2, mt, St);
+            merge_sampled(a, b, K + 1 + t, c2, md, Sd);
+            const E* trow = static_cast<const E*>(a.target) + ((int64_t)b * (K + 1) + t) * V;
+            const E* drow = static_cast<const E*>(a.draft) + ((int64_t)b * K + t) * V;
+            const double zt = (double)Logit<E>::at(trow, xt);
+            const double zd = (double)Logit<E>::at(drow, xt);
+            const double lp = (zt - (double)mt) / (double)T - log(St);
+            const double lq = (zd - (double)md) / (double)T - log(Sd);
+            if (op) op[t] = (float)exp(lp);
+            if (oq) oq[t] = (float)exp(lq);
+            // r < p/q in log space; q = 0 with p > 0 accepts, p = 0 rejects
+            const double ut = (double)u[t];
+            bool accept;
+            if (lp == -INFINITY) accept = false;
+            else if (lq == -INFINITY) accept = true;
+            else if (ut == 0.0) accept = true;
+            else accept = log(ut) < lp - lq;
+            if (!accept) first = min(first, t);
+        }
+    }
+    const int n = wave_min(first);
+    for (int t = lane; t <= K; t += 64)
+        if (t != n) tok[t] = t < n ? x[t] : -1;
+    if (lane == 0) {
+        a.out_n[b] = n;
+        d.n = n;
+        if (!sampled) {
+            float m;
+            int i;
+            merge_greedy(a, b, n, m, i);
+            tok[n] = i;
+            a.out_status[b] = 0;
+            d.mode = kModeNone;
+        } else {
+            merge_sampled(a, b, n, c2, d.mt, d.St);
+            if (n < K) {
+                merge_sampled(a, b, K + 1 + n, c2, d.md, d.Sd);
+                d.mode = kModeResidual;
+            } else {
+                d.mode = kModeBonus;
+            }
+            d.u = a.uniforms[(int64_t)b * (K + 1) + K];
+        }
+        a.desc[b] = d;
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// draw weights
+// ------------------------------------------------------------------------------------
+
 template <typename E>
 struct DrawRows {
-    const E* t;     // target row of the draw
-    const E* d;     // draft row (residual only)
-    double mt, md;  // row maxima
-    double invT;
-    double inv_sp, inv_sq;  // 1 / fp64 normalisers (residual only)
-    int residual;           // 1: (p - q)+, 0: exp((zt - mt)/T) (bonus, or fallback to p)
+    const E* t;          // target row of the draw
+    const E* d;          // draft row (residual; the target row again otherwise)
+    double mt, md, c64;  // row maxima, log2(e)/T
+    double inv_sp, inv_sq;
+    int residual;        // 1: (a/S_p - b/S_q)+ ; 0: a (bonus, or the draw from p_n)
+    int vec_ok;          // both rows 16-byte aligned
+    const double* tab;
 
-    __device__ __forceinline__ double weight(int i) const {
-        const double et = exp(((double)Logit<E>::at(t, i) - mt) * invT);
-        if (!residual) return et;
-        const double ed = exp(((double)Logit<E>::at(d, i) - md) * invT);
-        const double w = et * inv_sp - ed * inv_sq;
+    __device__ __forceinline__ double a_of(float z) const { return exp2_64(((double)z - mt) * c64, tab); }
+    __device__ __forceinline__ double b_of(float z) const { return exp2_64(((double)z - md) * c64, tab); }
+    __device__ __forceinline__ double weight(float zt, float zd) const {
+        const double a = a_of(zt);
+        if (!residual) return a;
+        const double w = a * inv_sp - b_of(zd) * inv_sq;
         return w > 0.0 ? w : 0.0;
     }
 };
 
 template <typename E>
-__device__ __forceinline__ DrawRows<E> draw_rows(const VerifyArgs& a, int b, const SeqDesc& d) {
+__device__ __forceinline__ DrawRows<E> draw_rows(const VerifyArgs& a, int b, const SeqDesc& d,
+                                                 const double* tab) {
     DrawRows<E> r;
-    r.t = static_cast<const E*>(a.target) + ((int64_t)b * (a.K + 1) + d.n) * a.V;
     r.residual = d.mode == kModeResidual;
-    r.d = r.residual ? static_cast<const E*>(a.draft) + ((int64_t)b * a.K + d.n) * a.V : nullptr;
+    r.t = static_cast<const E*>(a.target) + ((int64_t)b * (a.K + 1) + d.n) * a.V;
+    r.d = r.residual ? static_cast<const E*>(a.draft) + ((int64_t)b * a.K + d.n) * a.V : r.t;
     r.mt = d.mt;
     r.md = d.md;
-    r.invT = 1.0 / (double)d.T;
+    r.c64 = kLog2eD / (double)d.T;
     r.inv_sp = 1.0;
     r.inv_sq = 1.0;
+    r.vec_ok = ((reinterpret_cast<uintptr_t>(r.t) | reinterpret_cast<uintptr_t>(r.d)) & 15) == 0;
+    r.tab = tab;
     return r;
 }
 
-// Smallest i in [lo, hi) with base + (w_lo + ... + w_i) > target, each thread scanning a
-// contiguous run.  standalone: base = 0 and target = u * (sum over the range).  If no
-// index qualifies (rounding), the last index with positive weight; -1 if there is none.
+// Logits at positions i .. i+VEC-1: one 16-byte vector when aligned and inside [.., hi),
+// else element by element with positions at or past hi reading -inf (weight 0).
 template <typename E>
-__device__ int block_search(const DrawRows<E>& r, int lo, int hi, double base, double target,
-                            bool standalone, double u) {
-    __shared__ double shd[kWaves];
-    __shared__ int shi[kWaves];
-    const int n = hi - lo;
-    const int run = (n + kThreads - 1) / kThreads;
-    const int a0 = min(hi, lo + (int)threadIdx.x * run);
-    const int a1 = min(hi, a0 + run);
-    double s = 0.0;
-    for (int i = a0; i < a1; ++i) s += r.weight(i);
-    double tot;
-    const double ex = block_exclusive_scan(s, tot, shd);
-    if (standalone) {
-        base = 0.0;
-        target = u * tot;
+__device__ __forceinline__ void load_vec(const E* row, int i, int hi, bool vec_ok,
+                                         float (&z)[Logit<E>::kVec]) {
+    constexpr int VEC = Logit<E>::kVec;
+    if (vec_ok && i + VEC <= hi) {
+        Logit<E>::unpack(load16(row + i), z);
+    } else {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) z[k] = (i + k < hi) ? Logit<E>::at(row, i + k) : -INFINITY;
     }
-    double acc = base + ex;
-    int found = 0x7fffffff, lastpos = -1;
-    for (int i = a0; i < a1; ++i) {
-        const double w = r.weight(i);
-        if (w > 0.0) lastpos = i;
-        acc += w;
-        if (found == 0x7fffffff && acc > target) found = i;
+}
+
+// ------------------------------------------------------------------------------------
+// sweep: grid = sequences x nchunk2, each wave one contiguous sub-chunk
+// ------------------------------------------------------------------------------------
+
+struct SweepAcc {
+    double sp = 0.0, sq = 0.0;  // this lane's sums of a_i, b_i
+    double A = 0.0, B = 0.0;    // over the positions with a certainly positive residual
+    double Eq = 0.0;            // over the positions with a_i == b_i
+    double rho_hi, rho_lo;
+    int nunc = 0;               // undecided positions of the whole wave so far
+    int lane;
+    UncEntry* un;
+};
+
+// P positions i0 .. i0+P-1 of this lane.  Every lane of the wave calls this the same number
+// of times (the votes below are wave-wide).
+template <typename E, int P>
+__device__ __forceinline__ void sweep_vec(const DrawRows<E>& r, const float (&zt)[P], const float (&zd)[P],
+                                          int i0, SweepAcc& s) {
+    double xt[P], xd[P];
+    bool need = false;
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+        xt[k] = (double)zt[k] - r.mt;
+        xd[k] = r.residual ? (double)zd[k] - r.md : -INFINITY;
+        need |= fmax(xt[k], xd[k]) * r.c64 >= kSkipLog2;
     }
-    int f = block_min(found, shi);
-    if (f == 0x7fffffff) f = block_max(lastpos, shi);
-    return f;
+    if (!__any(need)) return;  // the whole wave: weights below 2^-80 of the row maxima
+    if (!r.residual) {
+#pragma unroll
+        for (int k = 0; k < P; ++k) s.sp += exp2_64(xt[k] * r.c64, r.tab);
+        return;
+    }
+    double av[P], bv[P];
+    bool unc[P];
+    bool any_unc = false;
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+        av[k] = exp2_64(xt[k] * r.c64, r.tab);
+        bv[k] = exp2_64(xd[k] * r.c64, r.tab);
+        s.sp += av[k];
+        s.sq += bv[k];
+        const bool pos = av[k] > s.rho_hi * bv[k];
+        unc[k] = !pos && av[k] > 0.0 && av[k] >= s.rho_lo * bv[k];
+        any_unc |= unc[k];
+        s.A += pos ? av[k] : 0.0;
+        s.B += pos ? bv[k] : 0.0;
+    }
+    if (__any(any_unc)) {
+        // rare: positions with the same exponent on both rows (a == b exactly) go to Eq,
+        // whose residual sign is that of 1/S_p - 1/S_q; the others are kept, in (k, lane) order
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            const bool eq = unc[k] && xt[k] == xd[k];
+            s.Eq += eq ? av[k] : 0.0;
+            const bool keep = unc[k] && !eq;
+            const uint64_t mask = __ballot(keep);
+            if (mask) {
+                if (keep) {
+                    const int slot = s.nunc + __popcll(mask & ((1ull << s.lane) - 1ull));
+                    if (slot < kUnc) {
+                        UncEntry ue;
+                        ue.a = av[k];
+                        ue.b = bv[k];
+                        ue.i = i0 + k;
+                        ue.pad = 0;
+                        s.un[slot] = ue;
+                    }
+                }
+                s.nunc += __popcll(mask);
+            }
+        }
+    }
 }
 
 template <typename E>
-__device__ void final_draw(const VerifyArgs& a, int b, const SeqDesc& d, DrawRows<E> r) {
+__global__ __launch_bounds__(kThreads) void sweep_kernel(VerifyArgs a, int b0) {
+    constexpr int VEC = Logit<E>::kVec;
+    constexpr int kG = SV_SWEEP_VECTORS;  // 16-byte vectors per row in flight per lane
+    constexpr int P = SV_SWEEP_POSITIONS < VEC ? SV_SWEEP_POSITIONS : VEC;
+    __shared__ double tab[kExpTable];
+    const int b = b0 + blockIdx.x / a.nchunk2;
+    const int c = blockIdx.x % a.nchunk2;
+    const SeqDesc d = a.desc[b];
+    if (d.mode == kModeNone) return;  // whole workgroup
+    exp2_table_init(tab);
+    const DrawRows<E> r = draw_rows<E>(a, b, d, tab);
+
+    const int V = a.V;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int sub = a.ch2 / kWaves;
+    const int lo = min(V, c * a.ch2 + w * sub);
+    const int hi = min(V, lo + sub);
+    const int64_t e = ((int64_t)b * a.nchunk2 + c) * kWaves + w;
+    SweepAcc acc;
+    acc.rho_hi = acc.rho_lo = 1.0;
+    if (r.residual) {
+        const double rho1 = d.St / d.Sd;
+        acc.rho_hi = rho1 * (1.0 + kDelta);
+        acc.rho_lo = rho1 * (1.0 - kDelta);
+    }
+    acc.lane = lane;
+    acc.un = a.unc + e * kUnc;
+
+    // whole, aligned spans of 64 lanes x kG vectors: all loads in flight together
+    const int span = 64 * kG * VEC;
+    const int hi_whole = r.vec_ok ? lo + ((hi - lo) / span) * span : lo;
+    for (int s0 = lo; s0 < hi_whole; s0 += span) {  // wave-uniform trip count
+        u32x4 rt[kG], rd[kG];
+#pragma unroll
+        for (int g = 0; g < kG; ++g) {
+            const int i = s0 + (g * 64 + lane) * VEC;
+            rt[g] = load16(r.t + i);
+            rd[g] = r.residual ? load16(r.d + i) : rt[g];
+        }
+#pragma unroll 1
+        for (int g = 0; g < kG; ++g) {
+            const int i = s0 + (g * 64 + lane) * VEC;
+            float zt[VEC], zd[VEC];
+            Logit<E>::unpack(rt[g], zt);
+            Logit<E>::unpack(rd[g], zd);
+#pragma unroll
+            for (int h = 0; h < VEC; h += P) {  // P positions at a time (constant indices)
+                float tp[P], dp[P];
+#pragma unroll
+                for (int k = 0; k < P; ++k) {
+                    tp[k] = zt[h + k];
+                    dp[k] = zd[h + k];
+                }
+                sweep_vec(r, tp, dp, i + h, acc);
+            }
+        }
+    }
+    // the rest (a partial span at the end, or rows not 16-byte aligned): one position per lane
+#pragma unroll 1
+    for (int i0 = hi_whole; i0 < hi; i0 += 64) {
+        const int i = i0 + lane;
+        const bool in = i < hi;
+        const float t1[1] = {in ? Logit<E>::at(r.t, i) : -INFINITY};
+        const float d1[1] = {(in && r.residual) ? Logit<E>::at(r.d, i) : -INFINITY};
+        sweep_vec(r, t1, d1, i, acc);
+    }
+    const double sp = wave_sum(acc.sp);
+    const double sq = wave_sum(acc.sq);
+    const double A = wave_sum(acc.A);
+    const double Bm = wave_sum(acc.B);
+    const double Eq = wave_sum(acc.Eq);
+    if (lane == 0) {
+        DrawPartial dp;
+        dp.sp = sp;
+        dp.sq = sq;
+        dp.A = A;
+        dp.B = Bm;
+        dp.Eq = Eq;
+        dp.nunc = acc.nunc;
+        dp.pad = 0;
+        a.part2[e] = dp;
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// final: grid = sequences, one workgroup each
+// ------------------------------------------------------------------------------------
+
+// Smallest i in [lo, hi) with base + (w_lo + ... + w_i) > target, in tiles of VEC positions
+// per thread (thread-local prefix, then a workgroup exclusive scan of the thread totals).
+// standalone: base = 0 and target = u * (sum over the range), taken by a first sweep.
+// If no index qualifies (rounding), the last index with positive weight; -1 if none.
+// lo must be a multiple of VEC.
+template <typename E>
+__device__ int block_search(const DrawRows<E>& r, int lo, int hi, double base, double target,
+                            bool standalone, double u) {
+    constexpr int VEC = Logit<E>::kVec;
+    constexpr int kTile = VEC * kThreads;
+    __shared__ double shd[kWaves];
+    __shared__ int shi[kWaves];
+    const int tid = threadIdx.x;
+    if (standalone) {
+        double tot = 0.0;
+        for (int t0 = lo; t0 < hi; t0 += kTile) {
+            const int i = t0 + VEC * tid;
+            float zt[VEC], zd[VEC];
+            load_vec(r.t, i, hi, r.vec_ok, zt);
+            if (r.residual) load_vec(r.d, i, hi, r.vec_ok, zd);
+            double s = 0.0;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) s += r.weight(zt[k], r.residual ? zd[k] : 0.0f);
+            tot += block_sum(s, shd);
+        }
+        base = 0.0;
+        target = u * tot;
+    }
+    double carry = 0.0;
+    int lastpos = -1;
+    for (int t0 = lo; t0 < hi; t0 += kTile) {
+        const int i = t0 + VEC * tid;
+        float zt[VEC], zd[VEC];
+        load_vec(r.t, i, hi, r.vec_ok, zt);
+        if (r.residual) load_vec(r.d, i, hi, r.vec_ok, zd);
+        double w[VEC];
+        double run = 0.0;
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            w[k] = r.weight(zt[k], r.residual ? zd[k] : 0.0f);
+            run += w[k];
+            if (w[k] > 0.0) lastpos = i + k;
+        }
+        double tile_tot;
+        const double ex = block_exclusive_scan(run, tile_tot, shd);
+        double acc = base + carry + ex;
+        int found = 0x7fffffff;
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            acc += w[k];
+            if (found == 0x7fffffff && w[k] > 0.0 && acc > target) found = i + k;
+        }
+        const int f = block_min(found, shi);
+        if (f != 0x7fffffff) return f;
+        carry += tile_tot;
+    }
+    return block_max(lastpos, shi);
+}
+
+template <typename E>
+__global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a, int b0) {
+    __shared__ double tab[kExpTable];
     __shared__ double shd[kWaves];
     __shared__ int shi[kWaves];
     __shared__ double sh_base;
+    const int b = b0 + blockIdx.x;
+    const SeqDesc d = a.desc[b];
+    if (d.mode == kModeNone) return;
+    exp2_table_init(tab);
+    DrawRows<E> r = draw_rows<E>(a, b, d, tab);
     const int tid = threadIdx.x;
     const int nsub = a.nchunk2 * kWaves;
     const int sub = a.ch2 / kWaves;
-    const double* e = a.part2b + (int64_t)b * nsub;
-    int status = d.status;
+    const int64_t e0 = (int64_t)b * nsub;
     const double u = (double)d.u;
+    int status = 0;
 
-    // total draw mass, by the same tiled scan the search below repeats
-    double carry = 0.0;
-    for (int t0 = 0; t0 < nsub; t0 += kThreads) {
-        const double v = (t0 + tid < nsub) ? e[t0 + tid] : 0.0;
-        double tot;
-        block_exclusive_scan(v, tot, shd);
-        carry += tot;
+    // fp64 normalisers and the check that rho' classified every position
+    bool exact_ok = true;
+    if (r.residual) {
+        double sp = 0.0, sq = 0.0;
+        int over = 0;
+        for (int k = tid; k < nsub; k += kThreads) {
+            const DrawPartial dp = a.part2[e0 + k];
+            sp += dp.sp;
+            sq += dp.sq;
+            over |= dp.nunc > kUnc;
+        }
+        sp = block_sum(sp, shd);
+        sq = block_sum(sq, shd);
+        over = block_or(over, shi);
+        r.inv_sp = 1.0 / sp;
+        r.inv_sq = 1.0 / sq;
+        const double rho = sp / sq;
+        const double rho1 = d.St / d.Sd;
+        exact_ok = !over && rho >= rho1 * (1.0 - 0.5 * kDelta) && rho <= rho1 * (1.0 + 0.5 * kDelta);
     }
-    const double total = carry;
 
     int y;
-    if (!(total > 0.0)) {
-        // Residual with zero fp64 mass (exact arithmetic rules it out): draw from p_n.
-        status |= kSeqNoteFallback;
-        r.residual = 0;
+    if (!exact_ok) {
+        // the pass-1 estimate was off, or too many undecided positions: one exact sweep
         y = block_search(r, 0, a.V, 0.0, 0.0, true, u);
     } else {
-        const double target = u * total;
-        carry = 0.0;
-        int hit = 0x7fffffff;
+        // positions with a == b: residual a (1/S_p - 1/S_q) when positive
+        const double eq_gain = r.residual && r.inv_sp > r.inv_sq ? r.inv_sp - r.inv_sq : 0.0;
+        // mass of sub-chunk k in the units of the draw
+        auto mass = [&](int k) -> double {
+            const DrawPartial dp = a.part2[e0 + k];
+            if (!r.residual) return dp.sp;
+            double w = dp.A * r.inv_sp - dp.B * r.inv_sq + dp.Eq * eq_gain;
+            const UncEntry* un = a.unc + (e0 + k) * kUnc;
+            for (int q = 0; q < dp.nunc; ++q) {
+                const double t = un[q].a * r.inv_sp - un[q].b * r.inv_sq;
+                if (t > 0.0) w += t;
+            }
+            return w > 0.0 ? w : 0.0;
+        };
+        double carry = 0.0;
         for (int t0 = 0; t0 < nsub; t0 += kThreads) {
             const int k = t0 + tid;
-            const double v = (k < nsub) ? e[k] : 0.0;
+            const double v = k < nsub ? mass(k) : 0.0;
             double tot;
-            const double ex = block_exclusive_scan(v, tot, shd);
-            const double incl = carry + ex + v;
-            // a sub-chunk without mass never holds the first crossing (guards rounding)
-            const int f = block_min((k < nsub && v > 0.0 && incl > target) ? k : 0x7fffffff, shi);
-            if (f != 0x7fffffff) {
-                if (k == f) sh_base = carry + ex;
-                __syncthreads();
-                hit = f;
-                break;
-            }
+            block_exclusive_scan(v, tot, shd);
             carry += tot;
         }
-        double base = 0.0, tgt = target;
-        if (hit == 0x7fffffff) {
-            // rounding put u*S past every prefix: the last sub-chunk with mass, last index
-            int last = -1;
+        const double total = carry;
+        if (!(total > 0.0)) {
+            // residual without fp64 mass (exact arithmetic rules it out): draw from p_n
+            status |= kSeqNoteFallback;
+            r.residual = 0;
+            y = block_search(r, 0, a.V, 0.0, 0.0, true, u);
+        } else {
+            const double target = u * total;
+            carry = 0.0;
+            int hit = 0x7fffffff;
             for (int t0 = 0; t0 < nsub; t0 += kThreads) {
                 const int k = t0 + tid;
-                last = max(last, (k < nsub && e[k] > 0.0) ? k : -1);
+                const double v = k < nsub ? mass(k) : 0.0;
+                double tot;
+                const double ex = block_exclusive_scan(v, tot, shd);
+                const double incl = carry + ex + v;
+                // a sub-chunk without mass never holds the first crossing (guards rounding)
+                const int f = block_min((k < nsub && v > 0.0 && incl > target) ? k : 0x7fffffff, shi);
+                if (f != 0x7fffffff) {
+                    if (k == f) sh_base = carry + ex;
+                    __syncthreads();
+                    hit = f;
+                    break;
+                }
+                carry += tot;
             }
-            hit = block_max(last, shi);
-            tgt = INFINITY;
-            status |= kSeqNoteFallback;
-        } else {
-            base = sh_base;
+            double base = 0.0, tgt = target;
+            if (hit == 0x7fffffff) {
+                // rounding put u*W past every prefix: the last sub-chunk with mass, last index
+                int last = -1;
+                for (int t0 = 0; t0 < nsub; t0 += kThreads) {
+                    const int k = t0 + tid;
+                    if (k < nsub && mass(k) > 0.0) last = max(last, k);
+                }
+                hit = block_max(last, shi);
+                tgt = INFINITY;
+                status |= kSeqNoteFallback;
+            } else {
+                base = sh_base;
+            }
+            const int c = hit / kWaves, w = hit % kWaves;
+            const int lo = min(a.V, c * a.ch2 + w * sub);
+            const int hi = min(a.V, lo + sub);
+            y = block_search(r, lo, hi, base, tgt, false, u);
         }
-        const int c = hit / kWaves, w = hit % kWaves;
-        const int lo = min(a.V, c * a.ch2 + w * sub);
-        const int hi = min(a.V, lo + sub);
-        y = block_search(r, lo, hi, base, tgt, false, u);
     }
     if (tid == 0) {
         a.out_tokens[(int64_t)b * (a.K + 1) + d.n] = y;
@@ -166,89 +615,28 @@ __device__ void final_draw(const VerifyArgs& a, int b, const SeqDesc& d, DrawRow
     }
 }
 
-template <typename E>
-__global__ __launch_bounds__(kThreads) void p2_norm_kernel(VerifyArgs a) {
-    __shared__ double shd[kWaves];
-    const int b = blockIdx.x / a.nchunk2;
-    const int c = blockIdx.x - b * a.nchunk2;
-    const SeqDesc d = a.desc[b];
-    if (d.mode != kModeResidual) return;  // whole workgroup
-    const DrawRows<E> r = draw_rows<E>(a, b, d);
-    const int lo = c * a.ch2;
-    const int hi = min(a.V, lo + a.ch2);
-    double sp = 0.0, sq = 0.0;
-    for (int i = lo + threadIdx.x; i < hi; i += kThreads) {
-        sp += exp(((double)Logit<E>::at(r.t, i) - r.mt) * r.invT);
-        sq += exp(((double)Logit<E>::at(r.d, i) - r.md) * r.invT);
-    }
-    sp = block_sum(sp, shd);
-    sq = block_sum(sq, shd);
-    if (threadIdx.x == 0) {
-        NormPartial np;
-        np.sp = sp;
-        np.sq = sq;
-        a.part2a[(int64_t)b * a.nchunk2 + c] = np;
-    }
-}
-
-template <typename E>
-__global__ __launch_bounds__(kThreads) void p2_sample_kernel(VerifyArgs a) {
-    __shared__ int sh_last;
-    __shared__ double sh_inv[2];
-    const int b = blockIdx.x / a.nchunk2;
-    const int c = blockIdx.x - b * a.nchunk2;
-    const SeqDesc d = a.desc[b];
-    if (d.mode == kModeNone) return;  // whole workgroup, and every workgroup of b
-    DrawRows<E> r = draw_rows<E>(a, b, d);
-    if (r.residual) {
-        if (threadIdx.x == 0) {
-            const NormPartial* np = a.part2a + (int64_t)b * a.nchunk2;
-            double sp = 0.0, sq = 0.0;
-            for (int k = 0; k < a.nchunk2; ++k) {
-                sp += np[k].sp;
-                sq += np[k].sq;
-            }
-            sh_inv[0] = 1.0 / sp;
-            sh_inv[1] = 1.0 / sq;
-        }
-        __syncthreads();
-        r.inv_sp = sh_inv[0];
-        r.inv_sq = sh_inv[1];
-    }
-    // each wave: one contiguous sub-chunk of this chunk
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int sub = a.ch2 / kWaves;
-    const int lo = min(a.V, c * a.ch2 + w * sub);
-    const int hi = min(a.V, lo + sub);
-    double acc = 0.0;
-    for (int i = lo + lane; i < hi; i += 64) acc += r.weight(i);
-    acc = wave_sum(acc);
-    if (lane == 0) a.part2b[((int64_t)b * a.nchunk2 + c) * kWaves + w] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        const uint32_t old = atomicInc(&a.cnt2[b], (uint32_t)a.nchunk2 - 1);
-        sh_last = (old == (uint32_t)a.nchunk2 - 1);
-    }
-    __syncthreads();
-    if (sh_last) {
-        __threadfence();
-        final_draw<E>(a, b, d, r);
-    }
-}
-
 }  // namespace
 
-int launch_pass2(const VerifyArgs& a, int bf16, void* stream) {
-    const int64_t blocks = (int64_t)a.B * a.nchunk2;
-    if (blocks == 0) return 0;
+int launch_resolve(const VerifyArgs& a, int bf16, int b0, int b1, void* stream) {
+    if (b1 <= b0) return 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (bf16)
+        hipLaunchKernelGGL(resolve_kernel<uint16_t>, dim3(b1 - b0), dim3(64), 0, s, a, b0);
+    else
+        hipLaunchKernelGGL(resolve_kernel<float>, dim3(b1 - b0), dim3(64), 0, s, a, b0);
+    return (int)hipGetLastError();
+}
+
+int launch_draw(const VerifyArgs& a, int bf16, int b0, int b1, void* stream) {
+    if (b1 <= b0) return 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const unsigned sweep_blocks = (unsigned)((int64_t)(b1 - b0) * a.nchunk2);
     if (bf16) {
-        hipLaunchKernelGGL(p2_norm_kernel<uint16_t>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
-        hipLaunchKernelGGL(p2_sample_kernel<uint16_t>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(sweep_kernel<uint16_t>, dim3(sweep_blocks), dim3(kThreads), 0, s, a, b0);
+        hipLaunchKernelGGL(final_kernel<uint16_t>, dim3(b1 - b0), dim3(kThreads), 0, s, a, b0);
     } else {
-        hipLaunchKernelGGL(p2_norm_kernel<float>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
-        hipLaunchKernelGGL(p2_sample_kernel<float>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(sweep_kernel<float>, dim3(sweep_blocks), dim3(kThreads), 0, s, a, b0);
+        hipLaunchKernelGGL(final_kernel<float>, dim3(b1 - b0), dim3(kThreads), 0, s, a, b0);
     }
     return (int)hipGetLastError();
 }
