@@ -91,7 +91,7 @@ sv::VerifyArgs make_args(const void* target, const void* draft, const int32_t* t
     a.desc = reinterpret_cast<sv::SeqDesc*>(ws + L.off_desc);
     a.part1 = reinterpret_cast<sv::RowPartial*>(ws + L.off_part1);
     a.part2 = reinterpret_cast<sv::DrawPartial*>(ws + L.off_part2);
-    a.unc = reinterpret_cast<sv::UncEntry*>(ws + L.off_unc);
+    a.bkt = reinterpret_cast<sv::Bucket*>(ws + L.off_bkt);
     a.out_tokens = out_tokens;
     a.out_n = out_n;
     a.out_p = out_p;

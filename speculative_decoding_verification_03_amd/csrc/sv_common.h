@@ -46,19 +46,19 @@ struct alignas(16) SeqDesc {
 //   a_i = exp((zt_i - mt)/T) and b_i = exp((zd_i - md)/T):
 //   sp, sq = sum a_i, sum b_i;
 //   A, B   = sums of a_i, b_i over the positions whose residual is certainly positive;
-//   Eq     = sum of a_i over the positions with zt_i - mt == zd_i - md exactly (a_i == b_i);
-//   nunc   = the positions left undecided, whose (a, b, i) are kept in up to kUnc slots.
+//   nbkt   = buckets of undecided positions: positions whose logit difference
+//            D_i = (zt_i - mt) - (zd_i - md) lies too close to the sign threshold, grouped
+//            by equal D_i (equal D means equal a_i / b_i, hence one residual sign); each
+//            bucket keeps its sums of a_i and b_i.  nbkt > kBuckets: the buckets overflowed.
 // Bonus draws use sp only.
-constexpr int kUnc = 8;
+constexpr int kBuckets = 16;
 struct alignas(16) DrawPartial {
-    double sp, sq, A, B, Eq;
-    int32_t nunc;  // undecided positions seen (may exceed kUnc: the slots are then incomplete)
-    int32_t pad;
+    double sp, sq, A, B;
+    int32_t nbkt;
+    int32_t pad[3];
 };
-struct alignas(16) UncEntry {
+struct alignas(16) Bucket {
     double a, b;
-    int64_t i;
-    int64_t pad;
 };
 
 constexpr int kSubUnit = 512;  // sub-chunks are multiples of 64 lanes x 8 positions
@@ -66,7 +66,7 @@ constexpr int kSubUnit = 512;  // sub-chunks are multiples of 64 lanes x 8 posit
 struct Layout {
     int nchunk1, ch1;  // pass-1 chunks per row and elements per chunk (multiple of 64)
     int nchunk2, ch2;  // sweep chunks per row and positions per chunk (kWaves sub-chunks)
-    size_t off_desc, off_part1, off_part2, off_unc, total;
+    size_t off_desc, off_part1, off_part2, off_bkt, total;
 };
 
 // Pass-1 chunks of about kChunkBytes1 (long streams per workgroup), more when the batch
@@ -113,8 +113,8 @@ inline Layout make_layout(int B, int K, int V, int esize, int rows_per_seq) {
     off = align256(off + sizeof(RowPartial) * (size_t)B * rows_per_seq * L.nchunk1);
     L.off_part2 = off;
     off = align256(off + sizeof(DrawPartial) * kWaves * (size_t)B * L.nchunk2);
-    L.off_unc = off;
-    off = align256(off + sizeof(UncEntry) * kUnc * kWaves * (size_t)B * L.nchunk2);
+    L.off_bkt = off;
+    off = align256(off + sizeof(Bucket) * kBuckets * kWaves * (size_t)B * L.nchunk2);
     L.total = off;
     return L;
 }
@@ -130,7 +130,7 @@ struct VerifyArgs {
     SeqDesc* desc;
     RowPartial* part1;
     DrawPartial* part2;        // [B][nchunk2][kWaves]
-    UncEntry* unc;             // [B][nchunk2][kWaves][kUnc]
+    Bucket* bkt;               // [B][nchunk2][kWaves][kBuckets]
     int32_t* out_tokens;
     int32_t* out_n;
     float* out_p;

@@ -15,18 +15,20 @@
 // which at V ~ 1.5e5 moves CDF edges past many narrow cells and would change the drawn
 // token on a visible fraction of draws.
 //
-// sweep_kernel (sequence x chunk workgroups, one contiguous sub-chunk per wave): exact
-// a_i = exp((zt_i - mt)/T), b_i = exp((zd_i - md)/T); their sums S_p, S_q; the sums A, B of
-// a_i, b_i over the positions whose residual is positive for every rho = S_p/S_q within
-// 1 +- kDelta of the pass-1 estimate rho' = S_p'/S_q'; the sum Eq of a_i over positions
-// with a_i == b_i exactly (their residual sign is that of 1/S_p - 1/S_q).  The few
-// positions between the two bounds are kept as (a_i, b_i, i).
+// sweep_kernel (sequence x chunk workgroups, one contiguous sub-chunk per wave):
+// a_i = exp((zt_i - mt)/T) and b_i = exp((zd_i - md)/T) in fp64 (a 256-entry LDS table of
+// 2^(j/256) and a cubic), their sums S_p, S_q, and the sums A, B of a_i, b_i over the
+// positions whose residual is positive for every rho = S_p/S_q within 1 +- kDelta of the
+// pass-1 estimate rho'.  The sign test uses the logit difference
+// D_i = (zt_i - mt) - (zd_i - md): p_i > q_i exactly when D_i > T ln rho.  Positions whose
+// D_i falls inside the bracket go to buckets of equal D_i (equal D, equal a/b ratio, one
+// residual sign), each with its sums of a_i and b_i.
 //
 // final_kernel (one workgroup per sequence): checks rho against rho' (else one exact
 // sweep by this workgroup), forms each sub-chunk's residual mass
-// A/S_p - B/S_q + Eq (1/S_p - 1/S_q)+ plus its kept terms, scans the masses for u * W,
-// and scans inside the sub-chunk that holds it: token = min{ i : C_i > u * W }, C the
-// prefix sums in index order.
+// A/S_p - B/S_q + sum over buckets of (a/S_p - b/S_q)+, scans the masses for u * W, and
+// scans inside the sub-chunk that holds it: token = min{ i : C_i > u * W }, C the prefix
+// sums in index order.
 #include <float.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -45,9 +47,6 @@ constexpr double kDelta = 8e-6;
 // Positions whose a_i and b_i are both below 2^-80 of their row maxima are skipped: over
 // any vocabulary they move the sums and CDF edges by less than V * 2^-80.
 constexpr double kSkipLog2 = -80.0;
-// Kept (uncertain) positions per sequence handled in the final kernel; more falls back
-// to the exact sweep.
-constexpr int kUncSeq = 256;
 
 // Sweep shape: 16-byte vectors per row whose loads are in flight together per lane, and
 // positions whose exponentials are computed together (register pressure against overlap).
@@ -227,14 +226,15 @@ template <typename E>
 struct DrawRows {
     const E* t;          // target row of the draw
     const E* d;          // draft row (residual; the target row again otherwise)
-    double mt, md, c64;  // row maxima, log2(e)/T
+    double mt, md, c256; // row maxima, 256 log2(e)/T
     double inv_sp, inv_sq;
     int residual;        // 1: (a/S_p - b/S_q)+ ; 0: a (bonus, or the draw from p_n)
     int vec_ok;          // both rows 16-byte aligned
     const double* tab;
 
-    __device__ __forceinline__ double a_of(float z) const { return exp2_64(((double)z - mt) * c64, tab); }
-    __device__ __forceinline__ double b_of(float z) const { return exp2_64(((double)z - md) * c64, tab); }
+    // exp((z - m)/T) = 2^((z - m) * 256 log2(e)/T / 256); z - m is exact in fp64
+    __device__ __forceinline__ double a_of(float z) const { return exp2_256(((double)z - mt) * c256, tab); }
+    __device__ __forceinline__ double b_of(float z) const { return exp2_256(((double)z - md) * c256, tab); }
     __device__ __forceinline__ double weight(float zt, float zd) const {
         const double a = a_of(zt);
         if (!residual) return a;
@@ -252,7 +252,7 @@ __device__ __forceinline__ DrawRows<E> draw_rows(const VerifyArgs& a, int b, con
     r.d = r.residual ? static_cast<const E*>(a.draft) + ((int64_t)b * a.K + d.n) * a.V : r.t;
     r.mt = d.mt;
     r.md = d.md;
-    r.c64 = kLog2eD / (double)d.T;
+    r.c256 = 256.0 * kLog2eD / (double)d.T;
     r.inv_sp = 1.0;
     r.inv_sq = 1.0;
     r.vec_ok = ((reinterpret_cast<uintptr_t>(r.t) | reinterpret_cast<uintptr_t>(r.d)) & 15) == 0;
@@ -281,71 +281,86 @@ __device__ __forceinline__ void load_vec(const E* row, int i, int hi, bool vec_o
 struct SweepAcc {
     double sp = 0.0, sq = 0.0;  // this lane's sums of a_i, b_i
     double A = 0.0, B = 0.0;    // over the positions with a certainly positive residual
-    double Eq = 0.0;            // over the positions with a_i == b_i
-    double rho_hi, rho_lo;
-    int nunc = 0;               // undecided positions of the whole wave so far
+    // p_i > q_i  <=>  D_i = (zt_i - mt) - (zd_i - md) > T ln(S_p / S_q).  With the ratio
+    // known to within 1 +- kDelta of rho', D_i above tau_hi is positive for certain and
+    // D_i in [tau_lo, tau_hi] undecided.
+    double tau_hi, tau_lo;
+    // The wave's buckets of undecided positions, one per lane: lane j holds bucket j
+    // (its D value and sums of a and b).  nbkt is wave-uniform.
+    double bD = 0.0, bA = 0.0, bB = 0.0;
+    int nbkt = 0;
     int lane;
-    UncEntry* un;
 };
 
-// P positions i0 .. i0+P-1 of this lane.  Every lane of the wave calls this the same number
-// of times (the votes below are wave-wide).
+// Adds the undecided positions of this call (flag u, values D, a, b per lane) to the
+// wave's buckets, one distinct D value at a time.
+__device__ __forceinline__ void bucket_add(SweepAcc& s, bool u, double D, double av, double bv) {
+    uint64_t m = __ballot(u);
+    while (m) {  // wave-uniform
+        const int leader = __ffsll((unsigned long long)m) - 1;
+        const double Dv = __shfl(D, leader, 64);
+        const bool match = u && D == Dv;
+        const double sa = wave_sum(match ? av : 0.0);
+        const double sb = wave_sum(match ? bv : 0.0);
+        const uint64_t hit = __ballot(s.lane < s.nbkt && s.bD == Dv);
+        int slot;
+        if (hit) {
+            slot = __ffsll((unsigned long long)hit) - 1;
+        } else {
+            slot = s.nbkt;
+            if (s.nbkt < kBuckets && s.lane == slot) s.bD = Dv;
+            ++s.nbkt;  // past kBuckets: overflowed
+        }
+        if (slot < kBuckets && s.lane == slot) {
+            s.bA += sa;
+            s.bB += sb;
+        }
+        u = u && !match;
+        m = __ballot(u);
+    }
+}
+
+// P positions of this lane.  Every lane of the wave calls this the same number of times
+// (the votes below are wave-wide).
 template <typename E, int P>
 __device__ __forceinline__ void sweep_vec(const DrawRows<E>& r, const float (&zt)[P], const float (&zd)[P],
-                                          int i0, SweepAcc& s) {
-    double xt[P], xd[P];
+                                          SweepAcc& s) {
+    double xt[P], xd[P], yt[P], yd[P];
     bool need = false;
 #pragma unroll
     for (int k = 0; k < P; ++k) {
         xt[k] = (double)zt[k] - r.mt;
         xd[k] = r.residual ? (double)zd[k] - r.md : -INFINITY;
-        need |= fmax(xt[k], xd[k]) * r.c64 >= kSkipLog2;
+        yt[k] = xt[k] * r.c256;
+        yd[k] = xd[k] * r.c256;
+        need |= fmax(yt[k], yd[k]) >= kSkipLog2 * 256.0;
     }
     if (!__any(need)) return;  // the whole wave: weights below 2^-80 of the row maxima
     if (!r.residual) {
 #pragma unroll
-        for (int k = 0; k < P; ++k) s.sp += exp2_64(xt[k] * r.c64, r.tab);
+        for (int k = 0; k < P; ++k) s.sp += exp2_256(yt[k], r.tab);
         return;
     }
-    double av[P], bv[P];
+    double av[P], bv[P], D[P];
     bool unc[P];
     bool any_unc = false;
 #pragma unroll
     for (int k = 0; k < P; ++k) {
-        av[k] = exp2_64(xt[k] * r.c64, r.tab);
-        bv[k] = exp2_64(xd[k] * r.c64, r.tab);
+        av[k] = exp2_256(yt[k], r.tab);
+        bv[k] = exp2_256(yd[k], r.tab);
         s.sp += av[k];
         s.sq += bv[k];
-        const bool pos = av[k] > s.rho_hi * bv[k];
-        unc[k] = !pos && av[k] > 0.0 && av[k] >= s.rho_lo * bv[k];
+        D[k] = xt[k] - xd[k];
+        const bool pos = D[k] > s.tau_hi;
+        unc[k] = !pos && D[k] >= s.tau_lo;
         any_unc |= unc[k];
-        s.A += pos ? av[k] : 0.0;
-        s.B += pos ? bv[k] : 0.0;
+        const double sel = pos ? 1.0 : 0.0;
+        s.A = __builtin_fma(av[k], sel, s.A);
+        s.B = __builtin_fma(bv[k], sel, s.B);
     }
-    if (__any(any_unc)) {
-        // rare: positions with the same exponent on both rows (a == b exactly) go to Eq,
-        // whose residual sign is that of 1/S_p - 1/S_q; the others are kept, in (k, lane) order
+    if (__any(any_unc)) {  // rare
 #pragma unroll
-        for (int k = 0; k < P; ++k) {
-            const bool eq = unc[k] && xt[k] == xd[k];
-            s.Eq += eq ? av[k] : 0.0;
-            const bool keep = unc[k] && !eq;
-            const uint64_t mask = __ballot(keep);
-            if (mask) {
-                if (keep) {
-                    const int slot = s.nunc + __popcll(mask & ((1ull << s.lane) - 1ull));
-                    if (slot < kUnc) {
-                        UncEntry ue;
-                        ue.a = av[k];
-                        ue.b = bv[k];
-                        ue.i = i0 + k;
-                        ue.pad = 0;
-                        s.un[slot] = ue;
-                    }
-                }
-                s.nunc += __popcll(mask);
-            }
-        }
+        for (int k = 0; k < P; ++k) bucket_add(s, unc[k], D[k], av[k], bv[k]);
     }
 }
 
@@ -369,14 +384,13 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(VerifyArgs a, int b0) {
     const int hi = min(V, lo + sub);
     const int64_t e = ((int64_t)b * a.nchunk2 + c) * kWaves + w;
     SweepAcc acc;
-    acc.rho_hi = acc.rho_lo = 1.0;
+    acc.tau_hi = acc.tau_lo = 0.0;
     if (r.residual) {
         const double rho1 = d.St / d.Sd;
-        acc.rho_hi = rho1 * (1.0 + kDelta);
-        acc.rho_lo = rho1 * (1.0 - kDelta);
+        acc.tau_hi = (double)d.T * log(rho1 * (1.0 + kDelta));
+        acc.tau_lo = (double)d.T * log(rho1 * (1.0 - kDelta));
     }
     acc.lane = lane;
-    acc.un = a.unc + e * kUnc;
 
     // whole, aligned spans of 64 lanes x kG vectors: all loads in flight together
     const int span = 64 * kG * VEC;
@@ -389,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(VerifyArgs a, int b0) {
             rt[g] = load16(r.t + i);
             rd[g] = r.residual ? load16(r.d + i) : rt[g];
         }
-#pragma unroll 1
+#pragma unroll
         for (int g = 0; g < kG; ++g) {
             const int i = s0 + (g * 64 + lane) * VEC;
             float zt[VEC], zd[VEC];
@@ -403,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(VerifyArgs a, int b0) {
                     tp[k] = zt[h + k];
                     dp[k] = zd[h + k];
                 }
-                sweep_vec(r, tp, dp, i + h, acc);
+                sweep_vec(r, tp, dp, acc);
             }
         }
     }
@@ -414,22 +428,26 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(VerifyArgs a, int b0) {
         const bool in = i < hi;
         const float t1[1] = {in ? Logit<E>::at(r.t, i) : -INFINITY};
         const float d1[1] = {(in && r.residual) ? Logit<E>::at(r.d, i) : -INFINITY};
-        sweep_vec(r, t1, d1, i, acc);
+        sweep_vec(r, t1, d1, acc);
     }
     const double sp = wave_sum(acc.sp);
     const double sq = wave_sum(acc.sq);
     const double A = wave_sum(acc.A);
     const double Bm = wave_sum(acc.B);
-    const double Eq = wave_sum(acc.Eq);
+    if (lane < acc.nbkt && lane < kBuckets) {
+        Bucket bk;
+        bk.a = acc.bA;
+        bk.b = acc.bB;
+        a.bkt[e * kBuckets + lane] = bk;
+    }
     if (lane == 0) {
         DrawPartial dp;
         dp.sp = sp;
         dp.sq = sq;
         dp.A = A;
         dp.B = Bm;
-        dp.Eq = Eq;
-        dp.nunc = acc.nunc;
-        dp.pad = 0;
+        dp.nbkt = acc.nbkt;
+        dp.pad[0] = dp.pad[1] = dp.pad[2] = 0;
         a.part2[e] = dp;
     }
 }
@@ -524,7 +542,7 @@ __global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a, int b0) {
             const DrawPartial dp = a.part2[e0 + k];
             sp += dp.sp;
             sq += dp.sq;
-            over |= dp.nunc > kUnc;
+            over |= dp.nbkt > kBuckets;
         }
         sp = block_sum(sp, shd);
         sq = block_sum(sq, shd);
@@ -534,6 +552,12 @@ __global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a, int b0) {
         const double rho = sp / sq;
         const double rho1 = d.St / d.Sd;
         exact_ok = !over && rho >= rho1 * (1.0 - 0.5 * kDelta) && rho <= rho1 * (1.0 + 0.5 * kDelta);
+#ifdef SV_DEBUG_FINAL
+        if (tid == 0 && a.out_p) {
+            a.out_p[(int64_t)b * a.K] = (float)(rho / rho1 - 1.0);
+            status |= (over ? 128 : 0) | (exact_ok ? 0 : 64);
+        }
+#endif
     }
 
     int y;
@@ -541,16 +565,15 @@ __global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a, int b0) {
         // the pass-1 estimate was off, or too many undecided positions: one exact sweep
         y = block_search(r, 0, a.V, 0.0, 0.0, true, u);
     } else {
-        // positions with a == b: residual a (1/S_p - 1/S_q) when positive
-        const double eq_gain = r.residual && r.inv_sp > r.inv_sq ? r.inv_sp - r.inv_sq : 0.0;
-        // mass of sub-chunk k in the units of the draw
+        // mass of sub-chunk k in the units of the draw: its certain part and, per bucket of
+        // undecided positions (one residual sign each), the bucket's residual if positive
         auto mass = [&](int k) -> double {
             const DrawPartial dp = a.part2[e0 + k];
             if (!r.residual) return dp.sp;
-            double w = dp.A * r.inv_sp - dp.B * r.inv_sq + dp.Eq * eq_gain;
-            const UncEntry* un = a.unc + (e0 + k) * kUnc;
-            for (int q = 0; q < dp.nunc; ++q) {
-                const double t = un[q].a * r.inv_sp - un[q].b * r.inv_sq;
+            double w = dp.A * r.inv_sp - dp.B * r.inv_sq;
+            const Bucket* bk = a.bkt + (e0 + k) * kBuckets;
+            for (int q = 0; q < dp.nbkt; ++q) {
+                const double t = bk[q].a * r.inv_sp - bk[q].b * r.inv_sq;
                 if (t > 0.0) w += t;
             }
             return w > 0.0 ? w : 0.0;

@@ -222,6 +222,41 @@ def test_greedy_ties_bit_exact(dev, dt):
         r.assert_ok(f"ties via spec_verify V={V}")
 
 
+def near_equal_rows(dev, B, K, V, dtype, temps, seed, jitter):
+    """Draft rows equal to the target rows except at one low-probability position per row,
+    raised by 3 (the draft token there, so it is rejected with probability 1 - e^(-3/T)).
+    The normalisers then differ by ~1e-7 and every other position has p_i / q_i ~ 1 - 1e-7:
+    a tiny residual spread over the whole row.  jitter > 0 also moves every draft logit by
+    a distinct amount of order 1e-6 (fp32), so the residual signs vary position by position."""
+    g = torch.Generator(device=dev).manual_seed(seed)
+    zt = (2.0 * torch.randn((B, K + 1, V), generator=g, device=dev)).to(dtype).float()
+    zd = zt[:, :K].clone()
+    if jitter:
+        zd += jitter * (torch.rand((B, K, V), generator=g, device=dev) - 0.5)
+    j = torch.argmin(zt[:, :K], dim=-1)  # [B, K]
+    zd.scatter_(2, j[..., None], zt[:, :K].gather(2, j[..., None]) + 3.0)
+    T = torch.tensor(temps, dtype=torch.float32, device=dev)
+    return dict(target=zt.to(dtype).contiguous(), draft=zd.to(dtype).contiguous(),
+                tokens=j.to(torch.int32).contiguous(), temperature=T)
+
+
+@pytest.mark.parametrize("dt,jitter", [(torch.bfloat16, 0.0), (torch.float32, 0.0), (torch.float32, 4e-6)])
+def test_near_equal_rows(dev, dt, jitter):
+    # jitter 0: the positions whose residual sign the sweep cannot settle all share one
+    # logit difference (one bucket per wave); jitter 4e-6: they carry many distinct ones,
+    # more than a wave keeps, and the draw takes the exact single-workgroup path.
+    say(f"near-equal rows {dt} jitter={jitter}")
+    B, K, V = 6, 3, 50000
+    t = Tally()
+    for rep in range(2):
+        inp = near_equal_rows(dev, B, K, V, dt, [1.0, 0.7, 1.3, 0.5, 2.0, 1.0], seed=31 + rep, jitter=jitter)
+        u = gpu_uniforms(31, rep, B, K)
+        t.merge(compare(run_sampled(inp, u), oracle_sampled(inp, u), range(B), inp["temperature"].cpu()))
+    say("  ", t)
+    t.assert_ok("near-equal rows")
+    assert t.draws > 0
+
+
 def test_neg_inf_logits(dev):
     say("-inf logits")
     B, K, V = 6, 3, 5000
