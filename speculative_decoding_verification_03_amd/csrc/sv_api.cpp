@@ -64,7 +64,7 @@ size_t workspace_need(int B, int K, int V) {
 
 bool grid_ok(int B, int R, const Layout& L) {
     const __int128 blocks1 = (__int128)B * R * L.nchunk1;
-    const __int128 blocks2 = (__int128)B * L.nchunk2;
+    const __int128 blocks2 = (__int128)B * L.ns2;
     return blocks1 <= 0x7fffffff && blocks2 <= 0x7fffffff;
 }
 
@@ -86,9 +86,10 @@ sv::VerifyArgs make_args(const void* target, const void* draft, const int32_t* t
     a.R = R;
     a.nchunk1 = L.nchunk1;
     a.ch1 = L.ch1;
-    a.nchunk2 = L.nchunk2;
-    a.ch2 = L.ch2;
-    a.desc = reinterpret_cast<sv::SeqDesc*>(ws + L.off_desc);
+    a.ns2 = L.ns2;
+    sv::chunking2(B, V, a.nchunk2, a.ch2);
+    a.desc = ws + L.off_desc;
+    a.wtab = reinterpret_cast<double*>(ws + L.off_wtab);
     a.part1 = reinterpret_cast<sv::RowPartial*>(ws + L.off_part1);
     a.part2 = reinterpret_cast<sv::DrawPartial*>(ws + L.off_part2);
     a.bkt = reinterpret_cast<sv::Bucket*>(ws + L.off_bkt);
@@ -164,7 +165,6 @@ sv_status spec_verify(const void* target_logits, const void* draft_logits, int d
     if (g_prof.on) g_prof.record(ev[0], stream);
     if (sv::launch_pass1(a, bf16, 0, B, stream) != 0) return SV_ERR_HIP;
     if (g_prof.on) g_prof.record(ev[1], stream);
-    if (sv::launch_resolve(a, bf16, 0, B, stream) != 0) return SV_ERR_HIP;
     if (sv::launch_draw(a, bf16, 0, B, stream) != 0) return SV_ERR_HIP;
     if (g_prof.on) g_prof.record(ev[2], stream);
     return SV_OK;
@@ -203,7 +203,7 @@ sv_status spec_verify_greedy(const void* target_logits, int dtype,
     if (g_prof.on) g_prof.record(ev[0], stream);
     if (sv::launch_pass1(a, bf16, 0, B, stream) != 0) return SV_ERR_HIP;
     if (g_prof.on) g_prof.record(ev[1], stream);
-    if (sv::launch_resolve(a, bf16, 0, B, stream) != 0) return SV_ERR_HIP;
+    if (sv::launch_draw(a, bf16, 0, B, stream) != 0) return SV_ERR_HIP;
     if (g_prof.on) g_prof.record(ev[2], stream);
     return SV_OK;
 }

@@ -31,17 +31,6 @@ struct alignas(16) RowPartial {
     double s;
 };
 
-// The resolve's result for one sequence.
-struct alignas(16) SeqDesc {
-    int32_t mode;  // kMode*
-    int32_t n;     // accepted drafts = row of the draw
-    float T;       // temperature
-    float u;       // uniform of the final draw
-    float mt, md;  // maxima of target row n and draft row n
-    double St, Sd; // pass-1 normalisers of those rows: sum exp((z - m) / T)
-    int32_t pad[2];
-};
-
 // Sweep results per (sequence, chunk, wave sub-chunk), fp64, with
 //   a_i = exp((zt_i - mt)/T) and b_i = exp((zd_i - md)/T):
 //   sp, sq = sum a_i, sum b_i;
@@ -61,12 +50,21 @@ struct alignas(16) Bucket {
     double a, b;
 };
 
-constexpr int kSubUnit = 512;  // sub-chunks are multiples of 64 lanes x 8 positions
+// bf16 weight tables: for each draw row, exp((z - m)/T) for every bf16 value z whose biased
+// exponent is in [kTabE0, kTabE0 + kTabNE), i.e. |z| in [2^-10, 32): kTabHalf positive
+// values then kTabHalf negative ones, in bit-pattern order.
+constexpr int kTabE0 = 117;
+constexpr int kTabNE = 15;
+constexpr int kTabHalf = kTabNE * 128;
+constexpr int kTabLen = 2 * kTabHalf;
+constexpr int kSeqDescBytes = 48;  // room for the draw kernels' per-sequence descriptor
+constexpr int kSubUnit = 1024;  // sub-chunks are multiples of 64 lanes x 16 positions
 
 struct Layout {
     int nchunk1, ch1;  // pass-1 chunks per row and elements per chunk (multiple of 64)
-    int nchunk2, ch2;  // sweep chunks per row and positions per chunk (kWaves sub-chunks)
-    size_t off_desc, off_part1, off_part2, off_bkt, total;
+    int ns2;           // draw chunks per sequence reserved in the workspace (any group's
+                       // nchunk2 is at most this)
+    size_t off_desc, off_part1, off_part2, off_bkt, off_wtab, total;
 };
 
 // Pass-1 chunks of about kChunkBytes1 (long streams per workgroup), more when the batch
@@ -74,12 +72,14 @@ struct Layout {
 constexpr int64_t kChunkBytes1 = 76 * 1024;
 constexpr int kTargetBlocks1 = 4096;
 constexpr int kMinChunk1 = 4096;
-constexpr int kTargetBlocks2 = 2048;
+#ifndef SV_TARGET_BLOCKS2
+#define SV_TARGET_BLOCKS2 4096
+#endif
+constexpr int kTargetBlocks2 = SV_TARGET_BLOCKS2;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-inline void chunking(int64_t rows, int64_t seqs, int V, int esize, int& nchunk1, int& ch1,
-                     int& nchunk2, int& ch2) {
+inline void chunking1(int64_t rows, int V, int esize, int& nchunk1, int& ch1) {
     int64_t by_bytes = ceil_div((int64_t)V * esize, kChunkBytes1);
     int64_t want = rows > 0 ? ceil_div(kTargetBlocks1, rows) : 1;
     int64_t maxc = V / kMinChunk1;
@@ -87,15 +87,22 @@ inline void chunking(int64_t rows, int64_t seqs, int V, int esize, int& nchunk1,
     if (want > maxc) want = maxc;
     int64_t n = by_bytes > want ? by_bytes : want;
     if (n < 1) n = 1;
-    int64_t ch = ceil_div(ceil_div(V, n), 64) * 64;
+    const int64_t ch = ceil_div(ceil_div(V, n), 64) * 64;
     nchunk1 = (int)ceil_div(V, ch);
     ch1 = (int)ch;
+}
 
+// Most draw chunks a sequence can have: chunks are whole multiples of kWaves sub-chunks of
+// kSubUnit positions.
+inline int max_chunks2(int V) { return (int)ceil_div(V, (int64_t)kWaves * kSubUnit); }
+
+// Draw chunks for a launch over `seqs` sequences: about kTargetBlocks2 workgroups.
+inline void chunking2(int64_t seqs, int V, int& nchunk2, int& ch2) {
     const int64_t unit = (int64_t)kWaves * kSubUnit;
-    want = seqs > 0 ? ceil_div(kTargetBlocks2, seqs) : 1;
-    maxc = ceil_div(V, unit);
-    n = want < 1 ? 1 : (want > maxc ? maxc : want);
-    ch = ceil_div(ceil_div(V, n), unit) * unit;
+    const int64_t maxc = max_chunks2(V);
+    const int64_t want = seqs > 0 ? ceil_div(kTargetBlocks2, seqs) : 1;
+    const int64_t n = want < 1 ? 1 : (want > maxc ? maxc : want);
+    const int64_t ch = ceil_div(ceil_div(V, n), unit) * unit;
     nchunk2 = (int)ceil_div(V, ch);
     ch2 = (int)ch;
 }
@@ -104,17 +111,21 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // rows_per_seq = 2K+1 for spec_verify, K+1 for spec_verify_greedy.
 inline Layout make_layout(int B, int K, int V, int esize, int rows_per_seq) {
+    (void)K;
     Layout L;
-    chunking((int64_t)B * rows_per_seq, B, V, esize, L.nchunk1, L.ch1, L.nchunk2, L.ch2);
+    chunking1((int64_t)B * rows_per_seq, V, esize, L.nchunk1, L.ch1);
+    L.ns2 = max_chunks2(V);
     size_t off = 0;
     L.off_desc = off;
-    off = align256(off + sizeof(SeqDesc) * (size_t)B);
+    off = align256(off + kSeqDescBytes * (size_t)B);
     L.off_part1 = off;
     off = align256(off + sizeof(RowPartial) * (size_t)B * rows_per_seq * L.nchunk1);
     L.off_part2 = off;
-    off = align256(off + sizeof(DrawPartial) * kWaves * (size_t)B * L.nchunk2);
+    off = align256(off + sizeof(DrawPartial) * kWaves * (size_t)B * L.ns2);
     L.off_bkt = off;
-    off = align256(off + sizeof(Bucket) * kBuckets * kWaves * (size_t)B * L.nchunk2);
+    off = align256(off + sizeof(Bucket) * kBuckets * kWaves * (size_t)B * L.ns2);
+    L.off_wtab = off;
+    if (esize == 2) off = align256(off + sizeof(double) * 2 * kTabLen * (size_t)B);
     L.total = off;
     return L;
 }
@@ -126,11 +137,14 @@ struct VerifyArgs {
     const float* uniforms;     // [B][K+1] (null when greedy-only)
     const float* temperature;  // [B] (null when greedy-only)
     int B, K, V, R;            // R = rows per sequence handled by pass 1
-    int nchunk1, ch1, nchunk2, ch2;
-    SeqDesc* desc;
-    RowPartial* part1;
-    DrawPartial* part2;        // [B][nchunk2][kWaves]
-    Bucket* bkt;               // [B][nchunk2][kWaves][kBuckets]
+    int nchunk1, ch1;          // pass-1 chunking
+    int nchunk2, ch2;          // draw chunking of this launch
+    int ns2;                   // draw chunks per sequence in the workspace arrays
+    void* desc;                // [B] resolve results for the draw kernels (kSeqDescBytes each)
+    RowPartial* part1;         // [B][R][nchunk1]
+    DrawPartial* part2;        // [B][ns2][kWaves]
+    Bucket* bkt;               // [B][ns2][kWaves][kBuckets]
+    double* wtab;              // bf16: [B][2][kTabLen] weight tables of the draw rows
     int32_t* out_tokens;
     int32_t* out_n;
     float* out_p;
@@ -139,8 +153,9 @@ struct VerifyArgs {
 };
 
 // Internal launchers (return hipError_t as int; 0 = success).  Sequences [b0, b1).
+// launch_draw runs the resolve and the draws of those sequences (greedy-only calls: the
+// resolve only) after their pass 1, on the same stream.
 int launch_pass1(const VerifyArgs& a, int bf16, int b0, int b1, void* stream);
-int launch_resolve(const VerifyArgs& a, int bf16, int b0, int b1, void* stream);
 int launch_draw(const VerifyArgs& a, int bf16, int b0, int b1, void* stream);
 int launch_uniforms(uint64_t seed, uint64_t domain, uint64_t step, int B, int K, float* u,
                     void* stream);

@@ -1,11 +1,11 @@
-// Pass 2 of the verify step: the resolve and the one categorical draw of each sequence.
+// Pass 2 of the verify step: the resolve and the one categorical draw of each sequence,
+// in three kernels: resolve_kernel (one workgroup per sequence), sweep_kernel ((sequence,
+// chunk) workgroups) and final_kernel (one workgroup per sequence).
 //
-// resolve_kernel (one wave per sequence): validation, then the left-to-right test
-// r_t < p_t(x_t)/q_t(x_t) of "A Regra de Exatidão" (lesson page "Decodificação
-// Especulativa e EAGLE"), evaluated in fp64 log space from the pass-1 row statistics, or
-// for T = 0 the greedy comparison argmax(p_t) == x_t ("Caso ganancioso").  n = the first
-// failing position (K if none).  Writes every output except the drawn token of a sampled
-// sequence, and a SeqDesc for the draw.
+// Resolve: validation, then the left-to-right test r_t < p_t(x_t)/q_t(x_t) of "A Regra
+// de Exatidão" (lesson page "Decodificação Especulativa e EAGLE"), evaluated in fp64 log
+// space from the pass-1 row statistics, or for T = 0 the greedy comparison
+// argmax(p_t) == x_t ("Caso ganancioso").  n = the first failing position (K if none).
 //
 // The draw.  After a rejection at n the token comes from (p_n - q_n)+, the positive part
 // of the pointwise difference over the whole vocabulary ("A Regra de Exatidão"; the
@@ -15,20 +15,19 @@
 // which at V ~ 1.5e5 moves CDF edges past many narrow cells and would change the drawn
 // token on a visible fraction of draws.
 //
-// sweep_kernel (sequence x chunk workgroups, one contiguous sub-chunk per wave):
-// a_i = exp((zt_i - mt)/T) and b_i = exp((zd_i - md)/T) in fp64 (a 256-entry LDS table of
-// 2^(j/256) and a cubic), their sums S_p, S_q, and the sums A, B of a_i, b_i over the
-// positions whose residual is positive for every rho = S_p/S_q within 1 +- kDelta of the
-// pass-1 estimate rho'.  The sign test uses the logit difference
-// D_i = (zt_i - mt) - (zd_i - md): p_i > q_i exactly when D_i > T ln rho.  Positions whose
-// D_i falls inside the bracket go to buckets of equal D_i (equal D, equal a/b ratio, one
-// residual sign), each with its sums of a_i and b_i.
+// Sweep (each workgroup, one contiguous sub-chunk per wave): a_i = exp((zt_i - mt)/T) and
+// b_i = exp((zd_i - md)/T) in fp64 (a 256-entry LDS table of 2^(j/256) and a Taylor
+// polynomial), their sums S_p, S_q, and the sums A, B of a_i, b_i over the positions whose
+// residual is positive for every rho = S_p/S_q within 1 +- kDelta of the pass-1 estimate
+// rho'.  The sign test uses the logit difference D_i = (zt_i - mt) - (zd_i - md):
+// p_i > q_i exactly when D_i > T ln rho.  Positions whose D_i falls inside the bracket go to
+// buckets of equal D_i (equal D, equal a/b ratio, one residual sign), each with its sums of
+// a_i and b_i.
 //
-// final_kernel (one workgroup per sequence): checks rho against rho' (else one exact
-// sweep by this workgroup), forms each sub-chunk's residual mass
-// A/S_p - B/S_q + sum over buckets of (a/S_p - b/S_q)+, scans the masses for u * W, and
-// scans inside the sub-chunk that holds it: token = min{ i : C_i > u * W }, C the prefix
-// sums in index order.
+// Final (final_kernel, one workgroup per sequence, after the sweep): checks rho against rho' (else one exact sweep by this
+// workgroup), forms each sub-chunk's residual mass A/S_p - B/S_q + sum over buckets of
+// (a/S_p - b/S_q)+, scans the masses for u * W, and scans inside the sub-chunk that holds
+// it: token = min{ i : C_i > u * W }, C the prefix sums in index order.
 #include <float.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -47,6 +46,8 @@ constexpr double kDelta = 8e-6;
 // Positions whose a_i and b_i are both below 2^-80 of their row maxima are skipped: over
 // any vocabulary they move the sums and CDF edges by less than V * 2^-80.
 constexpr double kSkipLog2 = -80.0;
+// Row statistics of the resolve kept in LDS; rows past this are merged again on demand.
+constexpr int kRowsLds = 2 * kThreads;
 
 // Sweep shape: 16-byte vectors per row whose loads are in flight together per lane, and
 // positions whose exponentials are computed together (register pressure against overlap).
@@ -56,6 +57,22 @@ constexpr double kSkipLog2 = -80.0;
 #ifndef SV_SWEEP_POSITIONS
 #define SV_SWEEP_POSITIONS 4
 #endif
+// Waves per SIMD the bf16 sweep's register allocation must allow.
+#ifndef SV_TAB_WAVES
+#define SV_TAB_WAVES 4
+#endif
+
+// The resolve's result for one sequence.
+struct SeqDesc {
+    int mode;      // kMode*
+    int n;         // accepted drafts = row of the draw
+    float T;       // temperature
+    float u;       // uniform of the final draw
+    float mt, md;  // maxima of target row n and draft row n
+    double St, Sd; // pass-1 normalisers of those rows: sum exp((z - m) / T)
+};
+static_assert(sizeof(SeqDesc) <= kSeqDescBytes && kSeqDescBytes % alignof(SeqDesc) == 0,
+              "workspace slot of the descriptor");
 
 // ------------------------------------------------------------------------------------
 // the resolve
@@ -69,153 +86,176 @@ __device__ __forceinline__ bool temperature_bad(float T) {
     return (T != T) || T < 0.0f || T == INFINITY || (T > 0.0f && T < FLT_MIN);
 }
 
-// Row j (0..K target, K+1..2K draft) of sequence b: max over chunks (NaN if any chunk saw
-// a NaN) and the lowest index reaching it.
-__device__ __forceinline__ void merge_greedy(const VerifyArgs& a, int b, int j, float& m, int& idx) {
+struct RowStat {
+    float m;   // row maximum (NaN if any chunk saw a NaN)
+    int idx;   // greedy rows: lowest index reaching m
+    double S;  // sampled rows: sum exp((z - m) / T)
+};
+
+// Row j (0..K target, K+1..2K draft) of sequence b from its pass-1 chunk partials.
+// Greedy: max and lowest index (chunks in order, strict comparison keeps the earlier
+// chunk on ties).  Sampled: max m and S from partials in the 2^((z - m_c) * c2) form.
+__device__ __forceinline__ RowStat merge_row(const VerifyArgs& a, int b, int j, bool sampled, float c2) {
     const RowPartial* p = a.part1 + ((int64_t)b * a.R + j) * a.nchunk1;
-    m = -INFINITY;
-    idx = 0x7fffffff;
-    bool bad = false;
-    for (int c = 0; c < a.nchunk1; ++c) {
-        const RowPartial q = p[c];
-        if (q.m != q.m) bad = true;
-        else if (q.m > m) {  // strict: an earlier chunk keeps ties
-            m = q.m;
-            idx = q.idx;
+    RowStat r{-INFINITY, 0x7fffffff, 0.0};
+    if (!sampled) {
+        bool bad = false;
+#pragma unroll 4
+        for (int c = 0; c < a.nchunk1; ++c) {
+            const RowPartial q = p[c];
+            if (q.m != q.m) bad = true;
+            else if (q.m > r.m) {
+                r.m = q.m;
+                r.idx = q.idx;
+            }
         }
+        if (bad) r.m = __builtin_nanf("");
+        return r;
     }
-    if (bad) m = __builtin_nanf("");
-}
-
-// Sampled row j: max m and S = sum exp((z - m)/T), from chunk partials in the
-// 2^((z - m) * c2) form.
-__device__ __forceinline__ void merge_sampled(const VerifyArgs& a, int b, int j, float c2, float& m,
-                                              double& S) {
-    const RowPartial* p = a.part1 + ((int64_t)b * a.R + j) * a.nchunk1;
-    m = -INFINITY;
-    for (int c = 0; c < a.nchunk1; ++c) m = nmax(m, p[c].m);
-    S = 0.0;
+#pragma unroll 4
+    for (int c = 0; c < a.nchunk1; ++c) r.m = nmax(r.m, p[c].m);
+#pragma unroll 4
     for (int c = 0; c < a.nchunk1; ++c) {
         const RowPartial q = p[c];
-        if (q.s != 0.0) S += q.s * exp2(((double)q.m - (double)m) * (double)c2);
+        if (q.s != 0.0) r.S += q.s * exp2(((double)q.m - (double)r.m) * (double)c2);
     }
+    return r;
 }
 
-// One wave per sequence.
+// The resolve of sequence b by the whole workgroup.  write: also write the outputs (all
+// but the drawn token of a sampled sequence, and its status).  Returns the same SeqDesc
+// in every thread.  Contains __syncthreads().
 template <typename E>
-__global__ __launch_bounds__(64) void resolve_kernel(VerifyArgs a, int b0) {
-    const int b = b0 + blockIdx.x;
-    const int lane = threadIdx.x;
-    const int K = a.K, V = a.V;
+__device__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool write) {
+    __shared__ RowStat rows[kRowsLds];
+    __shared__ int shi[kWaves];
+    __shared__ SeqDesc sd;
+    const int tid = threadIdx.x;
+    const int K = a.K, V = a.V, R = a.R;
     const float T = a.temperature ? a.temperature[b] : 0.0f;
     const bool sampled = !(T == 0.0f);
     const int32_t* x = a.tokens + (int64_t)b * K;
+    const float* u = sampled ? a.uniforms + (int64_t)b * (K + 1) : nullptr;
     const float c2 = sampled ? (float)(kLog2eD / (double)T) : 0.0f;
+
+    // loads that do not depend on the row statistics first: tokens, logits at x_t, uniforms
+    int xt = 0;
+    double zx = 0.0, dx = 0.0;
+    float ut = 0.5f;
+    int err = 0;
+    if (tid < K) {
+        xt = x[tid];
+        if (sampled && xt >= 0 && xt < V) {
+            zx = (double)Logit<E>::at(static_cast<const E*>(a.target) + ((int64_t)b * (K + 1) + tid) * V, xt);
+            dx = (double)Logit<E>::at(static_cast<const E*>(a.draft) + ((int64_t)b * K + tid) * V, xt);
+        }
+    }
+    if (sampled && tid <= K) ut = u[tid];
+    for (int t = tid; t < K; t += kThreads) {
+        const int v = x[t];
+        if (v < 0 || v >= V) err |= kSeqErrToken;
+    }
+    if (sampled)
+        for (int t = tid; t <= K; t += kThreads) {
+            const float v = u[t];
+            if (!(v >= 0.0f && v < 1.0f)) err |= kSeqErrUniform;
+        }
+    if (tid == 0 && temperature_bad(T)) err |= kSeqErrTemperature;
+    // row statistics (draft rows only for sampled sequences)
+    const int nrows = sampled ? R : K + 1;
+    for (int j = tid; j < nrows; j += kThreads) {
+        const RowStat r = merge_row(a, b, j, sampled, c2);
+        if (row_bad(r.m, sampled)) err |= kSeqErrLogit;
+        if (j < kRowsLds) rows[j] = r;
+    }
+    err = block_or(err, shi);  // also orders the rows[] writes before the reads below
+    auto row = [&](int j) -> RowStat { return j < kRowsLds ? rows[j] : merge_row(a, b, j, sampled, c2); };
+
     int32_t* tok = a.out_tokens + (int64_t)b * (K + 1);
     float* op = a.out_p ? a.out_p + (int64_t)b * K : nullptr;
     float* oq = a.out_q ? a.out_q + (int64_t)b * K : nullptr;
-    SeqDesc d{};
-    d.T = T;
-
-    // ---- validation: every row read, every token, every uniform ----
-    int err = 0;
-    if (lane == 0 && temperature_bad(T)) err |= kSeqErrTemperature;
-    for (int t = lane; t < K; t += 64) {
-        const int xt = x[t];
-        if (xt < 0 || xt >= V) err |= kSeqErrToken;
-    }
-    for (int j = lane; j < a.R; j += 64) {
-        if (j > K && !sampled) continue;
-        const RowPartial* p = a.part1 + ((int64_t)b * a.R + j) * a.nchunk1;
-        float m = -INFINITY;
-        for (int c = 0; c < a.nchunk1; ++c) m = nmax(m, p[c].m);
-        if (row_bad(m, sampled)) err |= kSeqErrLogit;
-    }
-    if (sampled) {
-        const float* u = a.uniforms + (int64_t)b * (K + 1);
-        for (int t = lane; t <= K; t += 64) {
-            const float ut = u[t];
-            if (!(ut >= 0.0f && ut < 1.0f)) err |= kSeqErrUniform;
-        }
-    }
-    err = wave_or(err);
     if (err) {
-        for (int t = lane; t <= K; t += 64) tok[t] = -1;
-        for (int t = lane; t < K; t += 64) {
-            if (op) op[t] = __builtin_nanf("");
-            if (oq) oq[t] = __builtin_nanf("");
+        if (write) {
+            for (int t = tid; t <= K; t += kThreads) tok[t] = -1;
+            for (int t = tid; t < K; t += kThreads) {
+                if (op) op[t] = __builtin_nanf("");
+                if (oq) oq[t] = __builtin_nanf("");
+            }
+            if (tid == 0) {
+                a.out_n[b] = -1;
+                a.out_status[b] = err;
+            }
         }
-        if (lane == 0) {
-            a.out_n[b] = -1;
-            a.out_status[b] = err;
-            d.mode = kModeNone;
-            a.desc[b] = d;
-        }
-        return;
+        SeqDesc d{};
+        d.mode = kModeNone;
+        return d;
     }
 
-    // ---- the first position that fails ----
+    // the first position that fails
     int first = K;
-    if (!sampled) {
-        for (int t = lane; t < K; t += 64) {
-            float m;
-            int i;
-            merge_greedy(a, b, t, m, i);
-            if (i != x[t]) first = min(first, t);
-            if (op) op[t] = __builtin_nanf("");
-            if (oq) oq[t] = __builtin_nanf("");
+    for (int t = tid; t < K; t += kThreads) {
+        if (t >= kThreads) {  // K > kThreads: the early loads above covered t < kThreads only
+            xt = x[t];
+            if (sampled) {
+                zx = (double)Logit<E>::at(static_cast<const E*>(a.target) + ((int64_t)b * (K + 1) + t) * V, xt);
+                dx = (double)Logit<E>::at(static_cast<const E*>(a.draft) + ((int64_t)b * K + t) * V, xt);
+                ut = u[t];
+            }
         }
-    } else {
-        const float* u = a.uniforms + (int64_t)b * (K + 1);
-        for (int t = lane; t < K; t += 64) {
-            const int xt = x[t];
-            float mt, md;
-            double St, Sd;
-            merge_sampled(a, b, t, c2, mt, St);
-            merge_sampled(a, b, K + 1 + t, c2, md, Sd);
-            const E* trow = static_cast<const E*>(a.target) + ((int64_t)b * (K + 1) + t) * V;
-            const E* drow = static_cast<const E*>(a.draft) + ((int64_t)b * K + t) * V;
-            const double zt = (double)Logit<E>::at(trow, xt);
-            const double zd = (double)Logit<E>::at(drow, xt);
-            const double lp = (zt - (double)mt) / (double)T - log(St);
-            const double lq = (zd - (double)md) / (double)T - log(Sd);
-            if (op) op[t] = (float)exp(lp);
-            if (oq) oq[t] = (float)exp(lq);
+        if (!sampled) {
+            if (row(t).idx != xt) first = min(first, t);
+            if (write && op) op[t] = __builtin_nanf("");
+            if (write && oq) oq[t] = __builtin_nanf("");
+        } else {
+            const RowStat rt = row(t), rd = row(K + 1 + t);
+            const double lp = (zx - (double)rt.m) / (double)T - log(rt.S);
+            const double lq = (dx - (double)rd.m) / (double)T - log(rd.S);
+            if (write && op) op[t] = (float)exp(lp);
+            if (write && oq) oq[t] = (float)exp(lq);
             // r < p/q in log space; q = 0 with p > 0 accepts, p = 0 rejects
-            const double ut = (double)u[t];
             bool accept;
             if (lp == -INFINITY) accept = false;
             else if (lq == -INFINITY) accept = true;
-            else if (ut == 0.0) accept = true;
-            else accept = log(ut) < lp - lq;
+            else if (ut == 0.0f) accept = true;
+            else accept = log((double)ut) < lp - lq;
             if (!accept) first = min(first, t);
         }
     }
-    const int n = wave_min(first);
-    for (int t = lane; t <= K; t += 64)
-        if (t != n) tok[t] = t < n ? x[t] : -1;
-    if (lane == 0) {
-        a.out_n[b] = n;
+    const int n = block_min(first, shi);
+    if (write)
+        for (int t = tid; t <= K; t += kThreads)
+            if (t != n) tok[t] = t < n ? x[t] : -1;
+    if (tid == 0) {
+        SeqDesc d{};
         d.n = n;
+        d.T = T;
+        if (write) a.out_n[b] = n;
         if (!sampled) {
-            float m;
-            int i;
-            merge_greedy(a, b, n, m, i);
-            tok[n] = i;
-            a.out_status[b] = 0;
+            if (write) {
+                tok[n] = row(n).idx;
+                a.out_status[b] = 0;
+            }
             d.mode = kModeNone;
         } else {
-            merge_sampled(a, b, n, c2, d.mt, d.St);
+            const RowStat rt = row(n);
+            d.mt = rt.m;
+            d.St = rt.S;
             if (n < K) {
-                merge_sampled(a, b, K + 1 + n, c2, d.md, d.Sd);
+                const RowStat rd = row(K + 1 + n);
+                d.md = rd.m;
+                d.Sd = rd.S;
                 d.mode = kModeResidual;
             } else {
                 d.mode = kModeBonus;
             }
             d.u = a.uniforms[(int64_t)b * (K + 1) + K];
         }
-        a.desc[b] = d;
+        sd = d;
     }
+    __syncthreads();
+    const SeqDesc d = sd;
+    __syncthreads();
+    return d;
 }
 
 // ------------------------------------------------------------------------------------
@@ -285,6 +325,9 @@ struct SweepAcc {
     // known to within 1 +- kDelta of rho', D_i above tau_hi is positive for certain and
     // D_i in [tau_lo, tau_hi] undecided.
     double tau_hi, tau_lo;
+    // The same bracket on the computed ratio a_i / b_i (tabulated bf16 weights):
+    // a_i > rho_hi b_i is positive for certain, rho_lo b_i <= a_i <= rho_hi b_i undecided.
+    double rho_hi, rho_lo;
     // The wave's buckets of undecided positions, one per lane: lane j holds bucket j
     // (its D value and sums of a and b).  nbkt is wave-uniform.
     double bD = 0.0, bA = 0.0, bB = 0.0;
@@ -364,25 +407,172 @@ __device__ __forceinline__ void sweep_vec(const DrawRows<E>& r, const float (&zt
     }
 }
 
+// ---- the bf16 path: weights looked up in the per-sequence tables (kTabE0 .. kTabNE) ----
+
+// Table index of the bf16 bit pattern h (in the low 16 bits), clamped into the table, and
+// whether h lies inside it.
+__device__ __forceinline__ uint32_t tab_index(uint32_t h, bool& in) {
+    const uint32_t off = (h & 0x7fffu) - (uint32_t)(kTabE0 * 128);
+    in = off < (uint32_t)kTabHalf;
+    return min(off, (uint32_t)(kTabHalf - 1)) + (h >> 15) * (uint32_t)kTabHalf;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
+
+// P positions of this lane given as bf16 bit patterns; ta, tb the LDS tables of the target
+// and draft rows.  Logits outside the tables take the polynomial (rare: tiny, very large
+// or infinite values); both give the same fp64 value for the same logit.
+template <bool Residual, int P>
+__device__ __forceinline__ void sweep_tab(const DrawRows<uint16_t>& r, const double* ta, const double* tb,
+                                          const uint32_t (&ht)[P], const uint32_t (&hd)[P], SweepAcc& s) {
+    double av[P], bv[P];
+    bool in_all = true;
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+        bool it, id = true;
+        av[k] = ta[tab_index(ht[k], it)];
+        if (Residual) bv[k] = tb[tab_index(hd[k], id)];
+        in_all = in_all && it && id;
+    }
+    if (!__all(in_all)) {
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            bool it, id = true;
+            tab_index(ht[k], it);
+            if (!it) av[k] = r.a_of(bf16_bits_to_float(ht[k]));
+            if (Residual) {
+                tab_index(hd[k], id);
+                if (!id) bv[k] = r.b_of(bf16_bits_to_float(hd[k]));
+            }
+        }
+    }
+    if (!Residual) {
+#pragma unroll
+        for (int k = 0; k < P; ++k) s.sp += av[k];
+        return;
+    }
+    bool unc[P];
+    bool any_unc = false;
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+        s.sp += av[k];
+        s.sq += bv[k];
+        const bool pos = av[k] > s.rho_hi * bv[k];
+        unc[k] = !pos && av[k] > 0.0 && av[k] >= s.rho_lo * bv[k];
+        any_unc |= unc[k];
+        const double sel = pos ? 1.0 : 0.0;
+        s.A = __builtin_fma(av[k], sel, s.A);
+        s.B = __builtin_fma(bv[k], sel, s.B);
+    }
+    if (__any(any_unc)) {  // rare: bucket by the exact logit difference
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            const double D = ((double)bf16_bits_to_float(ht[k]) - r.mt) - ((double)bf16_bits_to_float(hd[k]) - r.md);
+            bucket_add(s, unc[k], D, av[k], bv[k]);
+        }
+    }
+}
+
+// One wave per sub-chunk of chunk c of the draw row(s) of sequence b, bf16 logits, tables
+// in LDS.
+template <bool Residual>
+__device__ __forceinline__ void sweep_chunk_tab(const VerifyArgs& a, const DrawRows<uint16_t>& r,
+                                                const SeqDesc& d, const double* ta, const double* tb,
+                                                int b, int c) {
+    constexpr int VEC = 8;
+    constexpr int kG = SV_SWEEP_VECTORS;
+    const int V = a.V;
+    const int lane = threadIdx.x & 63, w = (threadIdx.x >> 6) & (kWaves - 1);
+    const int sub = a.ch2 / kWaves;
+    const int lo = min(V, c * a.ch2 + w * sub);
+    const int hi = min(V, lo + sub);
+    const int64_t e = ((int64_t)b * a.ns2 + c) * kWaves + w;
+    SweepAcc acc;
+    acc.tau_hi = acc.tau_lo = 0.0;
+    acc.rho_hi = acc.rho_lo = 1.0;
+    if (Residual) {
+        const double rho1 = d.St / d.Sd;
+        acc.rho_hi = rho1 * (1.0 + kDelta);
+        acc.rho_lo = rho1 * (1.0 - kDelta);
+    }
+    acc.lane = lane;
+
+    const int span = 64 * kG * VEC;
+    const int hi_whole = r.vec_ok ? lo + ((hi - lo) / span) * span : lo;
+    u32x4 rt[kG], rd[kG];
+    auto fetch = [&](int s0) {
+#pragma unroll
+        for (int g = 0; g < kG; ++g) {
+            const int i = s0 + (g * 64 + lane) * VEC;
+            rt[g] = load16(r.t + i);
+            rd[g] = Residual ? load16(r.d + i) : rt[g];
+        }
+    };
+    if (lo < hi_whole) fetch(lo);
+    for (int s0 = lo; s0 < hi_whole; s0 += span) {  // wave-uniform trip count
+        uint32_t wt[kG][4], wd[kG][4];
+#pragma unroll
+        for (int g = 0; g < kG; ++g) {
+            wt[g][0] = rt[g].x; wt[g][1] = rt[g].y; wt[g][2] = rt[g].z; wt[g][3] = rt[g].w;
+            wd[g][0] = rd[g].x; wd[g][1] = rd[g].y; wd[g][2] = rd[g].z; wd[g][3] = rd[g].w;
+        }
+        if (s0 + span < hi_whole) fetch(s0 + span);
+#pragma unroll
+        for (int g = 0; g < kG; ++g) {
+#pragma unroll
+            for (int q = 0; q < 4; q += 2) {  // 4 positions: two words of two bf16 each
+                const uint32_t ht[4] = {wt[g][q] & 0xffffu, wt[g][q] >> 16, wt[g][q + 1] & 0xffffu, wt[g][q + 1] >> 16};
+                const uint32_t hd[4] = {wd[g][q] & 0xffffu, wd[g][q] >> 16, wd[g][q + 1] & 0xffffu, wd[g][q + 1] >> 16};
+                sweep_tab<Residual>(r, ta, tb, ht, hd, acc);
+            }
+        }
+    }
+    // the rest (a partial span, or rows not 16-byte aligned): one position per lane; lanes
+    // past the end see -inf (0xff80), which lies outside the tables and weighs 0
+#pragma unroll 1
+    for (int i0 = hi_whole; i0 < hi; i0 += 64) {
+        const int i = i0 + lane;
+        const bool in = i < hi;
+        const uint32_t t1[1] = {in ? (uint32_t)r.t[i] : 0xff80u};
+        const uint32_t d1[1] = {(in && Residual) ? (uint32_t)r.d[i] : 0xff80u};
+        sweep_tab<Residual>(r, ta, tb, t1, d1, acc);
+    }
+    const double sp = wave_sum(acc.sp);
+    const double sq = wave_sum(acc.sq);
+    const double A = wave_sum(acc.A);
+    const double Bm = wave_sum(acc.B);
+    if (lane < acc.nbkt && lane < kBuckets) {
+        Bucket bk;
+        bk.a = acc.bA;
+        bk.b = acc.bB;
+        a.bkt[e * kBuckets + lane] = bk;
+    }
+    if (lane == 0) {
+        DrawPartial dp;
+        dp.sp = sp;
+        dp.sq = sq;
+        dp.A = A;
+        dp.B = Bm;
+        dp.nbkt = acc.nbkt;
+        dp.pad[0] = dp.pad[1] = dp.pad[2] = 0;
+        a.part2[e] = dp;
+    }
+}
+
+// One wave per sub-chunk of chunk c of the draw row(s) of sequence b.
 template <typename E>
-__global__ __launch_bounds__(kThreads) void sweep_kernel(VerifyArgs a, int b0) {
+__device__ __forceinline__ void sweep_chunk(const VerifyArgs& a, const DrawRows<E>& r, const SeqDesc& d,
+                                            int b, int c) {
     constexpr int VEC = Logit<E>::kVec;
     constexpr int kG = SV_SWEEP_VECTORS;  // 16-byte vectors per row in flight per lane
     constexpr int P = SV_SWEEP_POSITIONS < VEC ? SV_SWEEP_POSITIONS : VEC;
-    __shared__ double tab[kExpTable];
-    const int b = b0 + blockIdx.x / a.nchunk2;
-    const int c = blockIdx.x % a.nchunk2;
-    const SeqDesc d = a.desc[b];
-    if (d.mode == kModeNone) return;  // whole workgroup
-    exp2_table_init(tab);
-    const DrawRows<E> r = draw_rows<E>(a, b, d, tab);
 
     const int V = a.V;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int sub = a.ch2 / kWaves;
     const int lo = min(V, c * a.ch2 + w * sub);
     const int hi = min(V, lo + sub);
-    const int64_t e = ((int64_t)b * a.nchunk2 + c) * kWaves + w;
+    const int64_t e = ((int64_t)b * a.ns2 + c) * kWaves + w;
     SweepAcc acc;
     acc.tau_hi = acc.tau_lo = 0.0;
     if (r.residual) {
@@ -392,30 +582,37 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(VerifyArgs a, int b0) {
     }
     acc.lane = lane;
 
-    // whole, aligned spans of 64 lanes x kG vectors: all loads in flight together
+    // whole, aligned spans of 64 lanes x kG vectors per row; the next span's loads are
+    // issued before the current span is processed
     const int span = 64 * kG * VEC;
     const int hi_whole = r.vec_ok ? lo + ((hi - lo) / span) * span : lo;
-    for (int s0 = lo; s0 < hi_whole; s0 += span) {  // wave-uniform trip count
-        u32x4 rt[kG], rd[kG];
+    u32x4 rt[kG], rd[kG];
+    auto fetch = [&](int s0) {
 #pragma unroll
         for (int g = 0; g < kG; ++g) {
             const int i = s0 + (g * 64 + lane) * VEC;
             rt[g] = load16(r.t + i);
             rd[g] = r.residual ? load16(r.d + i) : rt[g];
         }
+    };
+    if (lo < hi_whole) fetch(lo);
+    for (int s0 = lo; s0 < hi_whole; s0 += span) {  // wave-uniform trip count
+        float zt[kG][VEC], zd[kG][VEC];
 #pragma unroll
         for (int g = 0; g < kG; ++g) {
-            const int i = s0 + (g * 64 + lane) * VEC;
-            float zt[VEC], zd[VEC];
-            Logit<E>::unpack(rt[g], zt);
-            Logit<E>::unpack(rd[g], zd);
+            Logit<E>::unpack(rt[g], zt[g]);
+            Logit<E>::unpack(rd[g], zd[g]);
+        }
+        if (s0 + span < hi_whole) fetch(s0 + span);
+#pragma unroll
+        for (int g = 0; g < kG; ++g) {
 #pragma unroll
             for (int h = 0; h < VEC; h += P) {  // P positions at a time (constant indices)
                 float tp[P], dp[P];
 #pragma unroll
                 for (int k = 0; k < P; ++k) {
-                    tp[k] = zt[h + k];
-                    dp[k] = zd[h + k];
+                    tp[k] = zt[g][h + k];
+                    dp[k] = zd[g][h + k];
                 }
                 sweep_vec(r, tp, dp, acc);
             }
@@ -515,21 +712,16 @@ __device__ int block_search(const DrawRows<E>& r, int lo, int hi, double base, d
     return block_max(lastpos, shi);
 }
 
+// The draw of sequence b from the partials of all its chunks.
 template <typename E>
-__global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a, int b0) {
-    __shared__ double tab[kExpTable];
+__device__ void final_seq(const VerifyArgs& a, DrawRows<E> r, const SeqDesc& d, int b) {
     __shared__ double shd[kWaves];
     __shared__ int shi[kWaves];
     __shared__ double sh_base;
-    const int b = b0 + blockIdx.x;
-    const SeqDesc d = a.desc[b];
-    if (d.mode == kModeNone) return;
-    exp2_table_init(tab);
-    DrawRows<E> r = draw_rows<E>(a, b, d, tab);
     const int tid = threadIdx.x;
     const int nsub = a.nchunk2 * kWaves;
     const int sub = a.ch2 / kWaves;
-    const int64_t e0 = (int64_t)b * nsub;
+    const int64_t e0 = (int64_t)b * a.ns2 * kWaves;
     const double u = (double)d.u;
     int status = 0;
 
@@ -638,29 +830,105 @@ __global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a, int b0) {
     }
 }
 
+
+// ------------------------------------------------------------------------------------
+// the kernels
+// ------------------------------------------------------------------------------------
+
+// grid = sequences: the resolve; writes its outputs and the sequence's SeqDesc, and for
+// bf16 logits the weight tables of the draw row(s), entry by entry the same fp64 function
+// as DrawRows::a_of / b_of.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void resolve_kernel(VerifyArgs a, int b0) {
+    __shared__ double tab[kExpTable];
+    const int b = b0 + blockIdx.x;
+    const SeqDesc d = resolve_seq<E>(a, b, true);
+    if (threadIdx.x == 0) reinterpret_cast<SeqDesc*>(a.desc)[b] = d;
+    if constexpr (sizeof(E) == 2) {
+        if (d.mode == kModeNone) return;  // whole workgroup
+        exp2_table_init(tab);
+        const DrawRows<E> r = draw_rows<E>(a, b, d, tab);
+        double* dst = a.wtab + (int64_t)b * 2 * kTabLen;
+        for (int k = threadIdx.x; k < kTabLen; k += kThreads) {
+            const uint32_t h = (k < kTabHalf ? 0u : 0x8000u) | (uint32_t)(kTabE0 * 128 + k % kTabHalf);
+            const float z = bf16_bits_to_float(h);
+            dst[k] = r.a_of(z);
+            if (r.residual) dst[kTabLen + k] = r.b_of(z);
+        }
+    }
+}
+
+// Workgroups of the bf16 sweep: kTabChunks chunks of kThreads each, sharing one copy of
+// the weight tables in LDS.
+constexpr int kTabChunks = 2;
+
+// grid = sequences x ceil(nchunk2 / kTabChunks), bf16: the sweep of kTabChunks chunks.
+__global__ __launch_bounds__(kThreads * kTabChunks) __attribute__((amdgpu_waves_per_eu(SV_TAB_WAVES)))
+void sweep_tab_kernel(VerifyArgs a, int b0) {
+    __shared__ double tab[kExpTable];
+    __shared__ double wt[2 * kTabLen];
+    const int ngrp = (a.nchunk2 + kTabChunks - 1) / kTabChunks;
+    const int b = b0 + (int)(blockIdx.x / (unsigned)ngrp);
+    const int c = (int)(blockIdx.x % (unsigned)ngrp) * kTabChunks + (int)(threadIdx.x / kThreads);
+    const SeqDesc d = reinterpret_cast<const SeqDesc*>(a.desc)[b];
+    if (d.mode == kModeNone) return;  // whole workgroup
+    const bool residual = d.mode == kModeResidual;
+    const int n16 = (residual ? 2 * kTabLen : kTabLen) / 2;  // 16-byte pieces
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.wtab + (int64_t)b * 2 * kTabLen);
+    u32x4* dst = reinterpret_cast<u32x4*>(wt);
+    for (int k = threadIdx.x; k < n16; k += blockDim.x) dst[k] = src[k];
+    exp2_table_init(tab);  // its barrier also publishes wt
+    if (c >= a.nchunk2) return;  // no barrier follows
+    const DrawRows<uint16_t> r = draw_rows<uint16_t>(a, b, d, tab);
+    if (residual) sweep_chunk_tab<true>(a, r, d, wt, wt + kTabLen, b, c);
+    else sweep_chunk_tab<false>(a, r, d, wt, wt, b, c);
+}
+
+// grid = sequences x nchunk2, fp32: the sweep of chunk c of the sequence's draw row(s).
+template <typename E>
+__global__ __launch_bounds__(kThreads) void sweep_kernel(VerifyArgs a, int b0) {
+    __shared__ double tab[kExpTable];
+    const int b = b0 + (int)(blockIdx.x / (unsigned)a.nchunk2);
+    const int c = (int)(blockIdx.x % (unsigned)a.nchunk2);
+    const SeqDesc d = reinterpret_cast<const SeqDesc*>(a.desc)[b];
+    if (d.mode == kModeNone) return;  // whole workgroup
+    exp2_table_init(tab);
+    sweep_chunk<E>(a, draw_rows<E>(a, b, d, tab), d, b, c);
+}
+
+// grid = sequences: the draw from the partials of all chunks.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a, int b0) {
+    __shared__ double tab[kExpTable];
+    const int b = b0 + blockIdx.x;
+    const SeqDesc d = reinterpret_cast<const SeqDesc*>(a.desc)[b];
+    if (d.mode == kModeNone) return;
+    exp2_table_init(tab);
+    final_seq<E>(a, draw_rows<E>(a, b, d, tab), d, b);
+}
+
 }  // namespace
 
-int launch_resolve(const VerifyArgs& a, int bf16, int b0, int b1, void* stream) {
-    if (b1 <= b0) return 0;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (bf16)
-        hipLaunchKernelGGL(resolve_kernel<uint16_t>, dim3(b1 - b0), dim3(64), 0, s, a, b0);
-    else
-        hipLaunchKernelGGL(resolve_kernel<float>, dim3(b1 - b0), dim3(64), 0, s, a, b0);
-    return (int)hipGetLastError();
+template <typename E>
+void launch_all(const VerifyArgs& a, int b0, int b1, hipStream_t s) {
+    hipLaunchKernelGGL(resolve_kernel<E>, dim3(b1 - b0), dim3(kThreads), 0, s, a, b0);
+    if (!a.temperature) return;  // greedy only: the resolve is everything
+    if constexpr (sizeof(E) == 2) {
+        const int ngrp = (a.nchunk2 + kTabChunks - 1) / kTabChunks;
+        const unsigned blocks = (unsigned)((int64_t)(b1 - b0) * ngrp);
+        hipLaunchKernelGGL(sweep_tab_kernel, dim3(blocks), dim3(kThreads * kTabChunks), 0, s, a, b0);
+    } else {
+        const unsigned blocks = (unsigned)((int64_t)(b1 - b0) * a.nchunk2);
+        hipLaunchKernelGGL(sweep_kernel<E>, dim3(blocks), dim3(kThreads), 0, s, a, b0);
+    }
+    hipLaunchKernelGGL(final_kernel<E>, dim3(b1 - b0), dim3(kThreads), 0, s, a, b0);
 }
 
 int launch_draw(const VerifyArgs& a, int bf16, int b0, int b1, void* stream) {
     if (b1 <= b0) return 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const unsigned sweep_blocks = (unsigned)((int64_t)(b1 - b0) * a.nchunk2);
-    if (bf16) {
-        hipLaunchKernelGGL(sweep_kernel<uint16_t>, dim3(sweep_blocks), dim3(kThreads), 0, s, a, b0);
-        hipLaunchKernelGGL(final_kernel<uint16_t>, dim3(b1 - b0), dim3(kThreads), 0, s, a, b0);
-    } else {
-        hipLaunchKernelGGL(sweep_kernel<float>, dim3(sweep_blocks), dim3(kThreads), 0, s, a, b0);
-        hipLaunchKernelGGL(final_kernel<float>, dim3(b1 - b0), dim3(kThreads), 0, s, a, b0);
-    }
+    if (bf16) launch_all<uint16_t>(a, b0, b1, s);
+    else launch_all<float>(a, b0, b1, s);
     return (int)hipGetLastError();
 }
 
