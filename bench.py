@@ -21,6 +21,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
+COPY_BYTES = 1 << 30    # size of the calibration copy (--copy-calibration)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pass1_kernel_traffic_workload4.md")
 
 
@@ -85,6 +86,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain device-to-device copy of COPY_BYTES, so that a "
+                         "counter profile of this command holds a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the verify step "
@@ -119,6 +123,15 @@ def main():
         sv.sv_fill_uniforms(seed, 0, i, B, K, out=u[k])
         sv.spec_verify(x["target"], x["draft"], x["tokens"], u[k], x["temperature"],
                        out=outs[k], workspace=ws)
+
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copy calibration, 3 copies of {COPY_BYTES} bytes")
+        del src, dst
 
     log(f"bench: warmup {args.warmup}")
     for i in range(args.warmup):
