@@ -89,7 +89,6 @@ sv::VerifyArgs make_args(const void* target, const void* draft, const int32_t* t
     a.ns2 = L.ns2;
     sv::chunking2(B, V, a.nchunk2, a.ch2);
     a.desc = ws + L.off_desc;
-    a.wtab = reinterpret_cast<double*>(ws + L.off_wtab);
     a.part1 = reinterpret_cast<sv::RowPartial*>(ws + L.off_part1);
     a.part2 = reinterpret_cast<sv::DrawPartial*>(ws + L.off_part2);
     a.bkt = reinterpret_cast<sv::Bucket*>(ws + L.off_bkt);

@@ -50,21 +50,14 @@ struct alignas(16) Bucket {
     double a, b;
 };
 
-// bf16 weight tables: for each draw row, exp((z - m)/T) for every bf16 value z whose biased
-// exponent is in [kTabE0, kTabE0 + kTabNE), i.e. |z| in [2^-10, 32): kTabHalf positive
-// values then kTabHalf negative ones, in bit-pattern order.
-constexpr int kTabE0 = 117;
-constexpr int kTabNE = 15;
-constexpr int kTabHalf = kTabNE * 128;
-constexpr int kTabLen = 2 * kTabHalf;
-constexpr int kSeqDescBytes = 48;  // room for the draw kernels' per-sequence descriptor
-constexpr int kSubUnit = 1024;  // sub-chunks are multiples of 64 lanes x 16 positions
+constexpr int kSubUnit = 1024;   // draw sub-chunks are multiples of 64 lanes x 16 positions
+constexpr int kSeqDescBytes = 48;  // workspace slot of the resolve's per-sequence result
 
 struct Layout {
     int nchunk1, ch1;  // pass-1 chunks per row and elements per chunk (multiple of 64)
-    int ns2;           // draw chunks per sequence reserved in the workspace (any group's
+    int ns2;           // draw chunks per sequence reserved in the workspace (any launch's
                        // nchunk2 is at most this)
-    size_t off_desc, off_part1, off_part2, off_bkt, off_wtab, total;
+    size_t off_desc, off_part1, off_part2, off_bkt, total;
 };
 
 // Pass-1 chunks of about kChunkBytes1 (long streams per workgroup), more when the batch
@@ -73,7 +66,7 @@ constexpr int64_t kChunkBytes1 = 76 * 1024;
 constexpr int kTargetBlocks1 = 4096;
 constexpr int kMinChunk1 = 4096;
 #ifndef SV_TARGET_BLOCKS2
-#define SV_TARGET_BLOCKS2 4096
+#define SV_TARGET_BLOCKS2 2560
 #endif
 constexpr int kTargetBlocks2 = SV_TARGET_BLOCKS2;
 
@@ -112,6 +105,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // rows_per_seq = 2K+1 for spec_verify, K+1 for spec_verify_greedy.
 inline Layout make_layout(int B, int K, int V, int esize, int rows_per_seq) {
     (void)K;
+    (void)esize;
     Layout L;
     chunking1((int64_t)B * rows_per_seq, V, esize, L.nchunk1, L.ch1);
     L.ns2 = max_chunks2(V);
@@ -124,8 +118,6 @@ inline Layout make_layout(int B, int K, int V, int esize, int rows_per_seq) {
     off = align256(off + sizeof(DrawPartial) * kWaves * (size_t)B * L.ns2);
     L.off_bkt = off;
     off = align256(off + sizeof(Bucket) * kBuckets * kWaves * (size_t)B * L.ns2);
-    L.off_wtab = off;
-    if (esize == 2) off = align256(off + sizeof(double) * 2 * kTabLen * (size_t)B);
     L.total = off;
     return L;
 }
@@ -140,11 +132,10 @@ struct VerifyArgs {
     int nchunk1, ch1;          // pass-1 chunking
     int nchunk2, ch2;          // draw chunking of this launch
     int ns2;                   // draw chunks per sequence in the workspace arrays
-    void* desc;                // [B] resolve results for the draw kernels (kSeqDescBytes each)
+    void* desc;                // [B] the resolve's result per sequence (kSeqDescBytes each)
     RowPartial* part1;         // [B][R][nchunk1]
     DrawPartial* part2;        // [B][ns2][kWaves]
     Bucket* bkt;               // [B][ns2][kWaves][kBuckets]
-    double* wtab;              // bf16: [B][2][kTabLen] weight tables of the draw rows
     int32_t* out_tokens;
     int32_t* out_n;
     float* out_p;

@@ -109,6 +109,7 @@ __device__ __forceinline__ void exp2_table_init(double* t) {
 // below (ln 2 / 512)^5 / 120 = 4e-17 relative: the weights stay fp64-accurate even where
 // p - q cancels to a small fraction of p.  Y below -1080*256 (including -inf) gives 0.
 __device__ __forceinline__ double exp2_256(double Y, const double* t) {
+#pragma clang fp contract(off)
     constexpr double kRound = 6755399441055744.0;  // 1.5 * 2^52: rounds to an integer
     constexpr double kL = 0.6931471805599453 / 256.0;
     Y = fmax(Y, -1080.0 * 256.0);
@@ -121,6 +122,13 @@ __device__ __forceinline__ double exp2_256(double Y, const double* t) {
     p = __builtin_fma(p, F, kL);
     p = __builtin_fma(p, F, 1.0);
     return ldexp(t[k & (kExpTable - 1)] * p, k >> 8);
+}
+
+// (z - ref) * c, never fused into a following add: every caller that evaluates a weight as
+// exp2_256(exp2_arg(...)), tabulated or direct, gets the same bits for the same operands.
+__device__ __forceinline__ double exp2_arg(double z, double ref, double c) {
+#pragma clang fp contract(off)
+    return (z - ref) * c;
 }
 
 // ---------------------------------------------------------------------------------

@@ -1,8 +1,9 @@
 // Pass 2 of the verify step: the resolve and the one categorical draw of each sequence,
-// in three kernels: resolve_kernel (one workgroup per sequence), sweep_kernel ((sequence,
-// chunk) workgroups) and final_kernel (one workgroup per sequence).
+// in two kernels: sweep_kernel over (sequence, chunk) workgroups, then final_kernel with
+// one workgroup per sequence.
 //
-// Resolve: validation, then the left-to-right test r_t < p_t(x_t)/q_t(x_t) of "A Regra
+// Resolve (every workgroup of the sequence, redundantly; the chunk-0 workgroup writes the
+// outputs): validation, then the left-to-right test r_t < p_t(x_t)/q_t(x_t) of "A Regra
 // de Exatidão" (lesson page "Decodificação Especulativa e EAGLE"), evaluated in fp64 log
 // space from the pass-1 row statistics, or for T = 0 the greedy comparison
 // argmax(p_t) == x_t ("Caso ganancioso").  n = the first failing position (K if none).
@@ -11,23 +12,29 @@
 // of the pointwise difference over the whole vocabulary ("A Regra de Exatidão"; the
 // livestream "IA local 202" describes the same clamp-and-normalise at [12:30]); after K
 // acceptances from p_K (the bonus token, "O Conceito" step 4).  Only that row pair (or
-// row) is read again.  It is all fp64: an fp32 weight carries a relative error near 1e-7,
-// which at V ~ 1.5e5 moves CDF edges past many narrow cells and would change the drawn
-// token on a visible fraction of draws.
+// row) is read again.  The weights are fp64: an fp32 weight carries a relative error near
+// 1e-7, which at V ~ 1.5e5 moves CDF edges past many narrow cells and would change the
+// drawn token on a visible fraction of draws.
 //
-// Sweep (each workgroup, one contiguous sub-chunk per wave): a_i = exp((zt_i - mt)/T) and
-// b_i = exp((zd_i - md)/T) in fp64 (a 256-entry LDS table of 2^(j/256) and a Taylor
-// polynomial), their sums S_p, S_q, and the sums A, B of a_i, b_i over the positions whose
-// residual is positive for every rho = S_p/S_q within 1 +- kDelta of the pass-1 estimate
-// rho'.  The sign test uses the logit difference D_i = (zt_i - mt) - (zd_i - md):
-// p_i > q_i exactly when D_i > T ln rho.  Positions whose D_i falls inside the bracket go to
-// buckets of equal D_i (equal D, equal a/b ratio, one residual sign), each with its sums of
-// a_i and b_i.
+// Weights.  a_i = 2^((zt_i - refA) c2), b_i = 2^((zd_i - refB) c2), c2 = log2(e)/T, so that
+// p_i = a_i / S_p and q_i = b_i / S_q.  Both rows share one reference (the larger row
+// maximum) unless that would push the smaller row toward fp64 underflow.  For bf16 logits
+// each workgroup tabulates the weight of every bf16 value with |z| in [2^-10, 32) in LDS
+// (3840 doubles) and looks weights up; other values, and fp32 logits, take the fp64
+// exponential of sv_device.h.  A weight below 2^-70 of its row maximum counts as 0: over
+// any vocabulary that moves the normalisers by less than V 2^-70 relative.
 //
-// Final (final_kernel, one workgroup per sequence, after the sweep): checks rho against rho' (else one exact sweep by this
-// workgroup), forms each sub-chunk's residual mass A/S_p - B/S_q + sum over buckets of
-// (a/S_p - b/S_q)+, scans the masses for u * W, and scans inside the sub-chunk that holds
-// it: token = min{ i : C_i > u * W }, C the prefix sums in index order.
+// Sweep (each workgroup one chunk of the row, each wave one contiguous sub-chunk): S_p,
+// S_q, and the sums A, B of a_i, b_i over the positions whose residual is positive for
+// every normaliser ratio within 1 +- kDelta of the pass-1 estimate.  The sign test is on the
+// logit difference: p_i > q_i exactly when zt_i - zd_i > tau = T ln(S_p/S_q) + refA - refB.
+// Positions whose difference falls inside the bracket go to buckets of equal difference
+// (equal difference, equal a/b ratio, one residual sign), each with its sums of a and b.
+//
+// Final (one workgroup per sequence, after every sweep): exact fp64 normalisers, the check that the estimate bracketed them (else
+// one exact sweep by this workgroup), each sub-chunk's residual mass A/S_p - B/S_q plus the
+// positive bucket masses, a scan of the masses for u * W, and a scan inside the sub-chunk
+// that holds it: token = min{ i : C_i > u * W }, C the prefix sums in index order.
 #include <float.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -40,27 +47,34 @@ namespace sv {
 namespace {
 
 constexpr double kLog2eD = 1.4426950408889634;
-// Classification margin around rho' and the acceptance test of rho: pass-1 normalisers
-// are within ~1e-6 of the fp64 ones, so kDelta / 2 leaves a wide guard.
+// Bracket around the pass-1 normaliser ratio (pass-1 normalisers are within ~1e-6 of the
+// fp64 ones), and the part of it the exact ratio must fall in for the classification to
+// stand.
 constexpr double kDelta = 8e-6;
-// Positions whose a_i and b_i are both below 2^-80 of their row maxima are skipped: over
-// any vocabulary they move the sums and CDF edges by less than V * 2^-80.
-constexpr double kSkipLog2 = -80.0;
+// Weights below 2^-kFlushLog2 of their row maximum count as 0.
+constexpr double kFlushLog2 = 70.0;
+// One shared weight reference for both rows while the row maxima differ by at most this
+// many binary orders of magnitude (then every weight that is not flushed stays normal).
+constexpr double kMaxRefGapLog2 = 900.0;
 // Row statistics of the resolve kept in LDS; rows past this are merged again on demand.
-constexpr int kRowsLds = 2 * kThreads;
+constexpr int kRowsLds = 64;
 
-// Sweep shape: 16-byte vectors per row whose loads are in flight together per lane, and
-// positions whose exponentials are computed together (register pressure against overlap).
-#ifndef SV_SWEEP_VECTORS
-#define SV_SWEEP_VECTORS 2
+// bf16 weight table: bf16 values whose biased exponent is in [kTabE0, kTabE0 + kTabNE),
+// i.e. |z| in [2^-10, 32): kTabHalf positive values, then kTabHalf negative ones, in
+// bit-pattern order.
+constexpr int kTabE0 = 117;
+constexpr int kTabNE = 15;
+constexpr int kTabHalf = kTabNE * 128;
+constexpr int kTabLen = 2 * kTabHalf;
+
+// Waves per SIMD the draw kernel's register allocation must allow (4 workgroups per CU).
+#ifndef SV_DRAW_WAVES
+#define SV_DRAW_WAVES 4
 #endif
-#ifndef SV_SWEEP_POSITIONS
-#define SV_SWEEP_POSITIONS 4
-#endif
-// Waves per SIMD the bf16 sweep's register allocation must allow.
-#ifndef SV_TAB_WAVES
-#define SV_TAB_WAVES 4
-#endif
+
+// 16-byte vectors per row whose loads are in flight together per lane.
+constexpr int kG = 2;
+static_assert(kSubUnit % (64 * kG * 8) == 0, "draw sub-chunks are whole spans of bf16 vectors");
 
 // The resolve's result for one sequence.
 struct SeqDesc {
@@ -71,8 +85,6 @@ struct SeqDesc {
     float mt, md;  // maxima of target row n and draft row n
     double St, Sd; // pass-1 normalisers of those rows: sum exp((z - m) / T)
 };
-static_assert(sizeof(SeqDesc) <= kSeqDescBytes && kSeqDescBytes % alignof(SeqDesc) == 0,
-              "workspace slot of the descriptor");
 
 // ------------------------------------------------------------------------------------
 // the resolve
@@ -126,7 +138,7 @@ __device__ __forceinline__ RowStat merge_row(const VerifyArgs& a, int b, int j, 
 // but the drawn token of a sampled sequence, and its status).  Returns the same SeqDesc
 // in every thread.  Contains __syncthreads().
 template <typename E>
-__device__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool write) {
+__device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool write) {
     __shared__ RowStat rows[kRowsLds];
     __shared__ int shi[kWaves];
     __shared__ SeqDesc sd;
@@ -262,19 +274,53 @@ __device__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool write) {
 // draw weights
 // ------------------------------------------------------------------------------------
 
+// Table index of the bf16 bit pattern h (in the low 16 bits), clamped into the table, and
+// whether h lies inside it.
+__device__ __forceinline__ uint32_t tab_index(uint32_t h, bool& in) {
+    const uint32_t off = (h & 0x7fffu) - (uint32_t)(kTabE0 * 128);
+    in = off < (uint32_t)kTabHalf;
+    return min(off, (uint32_t)(kTabHalf - 1)) + (h >> 15) * (uint32_t)kTabHalf;
+}
+
 template <typename E>
 struct DrawRows {
-    const E* t;          // target row of the draw
-    const E* d;          // draft row (residual; the target row again otherwise)
-    double mt, md, c256; // row maxima, 256 log2(e)/T
-    double inv_sp, inv_sq;
-    int residual;        // 1: (a/S_p - b/S_q)+ ; 0: a (bonus, or the draw from p_n)
-    int vec_ok;          // both rows 16-byte aligned
-    const double* tab;
+    const E* t;            // target row of the draw
+    const E* d;            // draft row (residual; the target row again otherwise)
+    double refA, refB;     // weight references of the two rows
+    double c256;           // 256 log2(e) / T
+    double inv_sp, inv_sq; // 1 / S_p, 1 / S_q once known
+    double tau_lo, tau_hi; // undecided bracket on zt - zd
+    float tau_lo_f, tau_hi_f;  // the same, rounded outward to fp32
+    float thr_t, thr_d;    // z below these weighs 0 (2^-70 of the row maximum)
+    int residual;          // 1: (a/S_p - b/S_q)+ ; 0: a (bonus, or the draw from p_n)
+    int vec_ok;            // both rows 16-byte aligned
+    int use_tab;           // bf16 with one shared reference: weights from the LDS table
+    const double* tab;     // 2^(j/256), LDS
+    const double* wt;      // bf16 weight table, LDS
 
-    // exp((z - m)/T) = 2^((z - m) * 256 log2(e)/T / 256); z - m is exact in fp64
-    __device__ __forceinline__ double a_of(float z) const { return exp2_256(((double)z - mt) * c256, tab); }
-    __device__ __forceinline__ double b_of(float z) const { return exp2_256(((double)z - md) * c256, tab); }
+    // exp((z - ref)/T) = 2^((z - ref) * 256 log2(e)/T / 256); z - ref is exact in fp64
+    __device__ __forceinline__ double a_of(float z) const {
+        if (!(z >= thr_t)) return 0.0;
+        if constexpr (sizeof(E) == 2) {
+            if (use_tab) {
+                bool in;
+                const uint32_t k = tab_index(__float_as_uint(z) >> 16, in);
+                if (in) return wt[k];
+            }
+        }
+        return exp2_256(exp2_arg((double)z, refA, c256), tab);
+    }
+    __device__ __forceinline__ double b_of(float z) const {
+        if (!(z >= thr_d)) return 0.0;
+        if constexpr (sizeof(E) == 2) {
+            if (use_tab) {
+                bool in;
+                const uint32_t k = tab_index(__float_as_uint(z) >> 16, in);
+                if (in) return wt[k];
+            }
+        }
+        return exp2_256(exp2_arg((double)z, refB, c256), tab);
+    }
     __device__ __forceinline__ double weight(float zt, float zd) const {
         const double a = a_of(zt);
         if (!residual) return a;
@@ -283,21 +329,55 @@ struct DrawRows {
     }
 };
 
+// The draw rows of sequence b and their weight parameters (no LDS access).
 template <typename E>
 __device__ __forceinline__ DrawRows<E> draw_rows(const VerifyArgs& a, int b, const SeqDesc& d,
-                                                 const double* tab) {
+                                                 const double* tab, const double* wt) {
     DrawRows<E> r;
     r.residual = d.mode == kModeResidual;
     r.t = static_cast<const E*>(a.target) + ((int64_t)b * (a.K + 1) + d.n) * a.V;
     r.d = r.residual ? static_cast<const E*>(a.draft) + ((int64_t)b * a.K + d.n) * a.V : r.t;
-    r.mt = d.mt;
-    r.md = d.md;
-    r.c256 = 256.0 * kLog2eD / (double)d.T;
+    const double T = (double)d.T;
+    const double c2 = kLog2eD / T;
+    r.c256 = 256.0 * c2;
+    const double mt = (double)d.mt, md = r.residual ? (double)d.md : mt;
+    const bool one_ref = fabs(mt - md) * c2 <= kMaxRefGapLog2;
+    const double M = fmax(mt, md);
+    r.refA = one_ref ? M : mt;
+    r.refB = one_ref ? M : md;
+    r.use_tab = sizeof(E) == 2 && one_ref;
+    r.thr_t = (float)(mt - kFlushLog2 / c2);
+    r.thr_d = r.residual ? (float)(md - kFlushLog2 / c2) : INFINITY;
     r.inv_sp = 1.0;
     r.inv_sq = 1.0;
+    r.tau_lo = r.tau_hi = 0.0;
+    r.tau_lo_f = r.tau_hi_f = 0.0f;
+    if (r.residual) {
+        // p_i > q_i  <=>  zt_i - zd_i > T ln(S_p/S_q) + refA - refB, and in the pass-1 terms
+        // (normalisers St, Sd relative to mt, md) that threshold is T ln(St/Sd) + mt - md
+        const double lr = log(d.St) - log(d.Sd);
+        r.tau_hi = T * (lr + log1p(kDelta)) + (mt - md);
+        r.tau_lo = T * (lr + log1p(-kDelta)) + (mt - md);
+        r.tau_hi_f = __double2float_ru(r.tau_hi);
+        r.tau_lo_f = __double2float_rd(r.tau_lo);
+    }
     r.vec_ok = ((reinterpret_cast<uintptr_t>(r.t) | reinterpret_cast<uintptr_t>(r.d)) & 15) == 0;
     r.tab = tab;
+    r.wt = wt;
     return r;
+}
+
+// Fill the bf16 weight table (kTabLen doubles of LDS) for reference r.refA (= r.refB):
+// entries below both flush thresholds are never read and stay 0.  Contains __syncthreads().
+template <typename E>
+__device__ __forceinline__ void weight_table_init(const DrawRows<E>& r, double* wt) {
+    const float thr = fminf(r.thr_t, r.thr_d);
+    for (int k = threadIdx.x; k < kTabLen; k += kThreads) {
+        const uint32_t h = (k < kTabHalf ? 0u : 0x8000u) | (uint32_t)(kTabE0 * 128 + k % kTabHalf);
+        const float z = __uint_as_float(h << 16);
+        wt[k] = z >= thr ? exp2_256(exp2_arg((double)z, r.refA, r.c256), r.tab) : 0.0;
+    }
+    __syncthreads();
 }
 
 // Logits at positions i .. i+VEC-1: one 16-byte vector when aligned and inside [.., hi),
@@ -315,28 +395,21 @@ __device__ __forceinline__ void load_vec(const E* row, int i, int hi, bool vec_o
 }
 
 // ------------------------------------------------------------------------------------
-// sweep: grid = sequences x nchunk2, each wave one contiguous sub-chunk
+// sweep
 // ------------------------------------------------------------------------------------
 
 struct SweepAcc {
     double sp = 0.0, sq = 0.0;  // this lane's sums of a_i, b_i
     double A = 0.0, B = 0.0;    // over the positions with a certainly positive residual
-    // p_i > q_i  <=>  D_i = (zt_i - mt) - (zd_i - md) > T ln(S_p / S_q).  With the ratio
-    // known to within 1 +- kDelta of rho', D_i above tau_hi is positive for certain and
-    // D_i in [tau_lo, tau_hi] undecided.
-    double tau_hi, tau_lo;
-    // The same bracket on the computed ratio a_i / b_i (tabulated bf16 weights):
-    // a_i > rho_hi b_i is positive for certain, rho_lo b_i <= a_i <= rho_hi b_i undecided.
-    double rho_hi, rho_lo;
     // The wave's buckets of undecided positions, one per lane: lane j holds bucket j
-    // (its D value and sums of a and b).  nbkt is wave-uniform.
+    // (its difference value D and sums of a and b).  nbkt is wave-uniform.
     double bD = 0.0, bA = 0.0, bB = 0.0;
     int nbkt = 0;
     int lane;
 };
 
-// Adds the undecided positions of this call (flag u, values D, a, b per lane) to the
-// wave's buckets, one distinct D value at a time.
+// Adds the undecided positions of this call (flag u, difference D, weights a, b per lane)
+// to the wave's buckets, one distinct D at a time.
 __device__ __forceinline__ void bucket_add(SweepAcc& s, bool u, double D, double av, double bv) {
     uint64_t m = __ballot(u);
     while (m) {  // wave-uniform
@@ -363,140 +436,167 @@ __device__ __forceinline__ void bucket_add(SweepAcc& s, bool u, double D, double
     }
 }
 
-// P positions of this lane.  Every lane of the wave calls this the same number of times
-// (the votes below are wave-wide).
+// Accumulates P positions of this lane with weights av, bv, the fp32 difference Df (exact
+// when dx_ok) and the logits (for the exact difference otherwise).  Wave-wide votes: every
+// lane of the wave calls this the same number of times.
 template <typename E, int P>
-__device__ __forceinline__ void sweep_vec(const DrawRows<E>& r, const float (&zt)[P], const float (&zd)[P],
-                                          SweepAcc& s) {
-    double xt[P], xd[P], yt[P], yd[P];
-    bool need = false;
+__device__ __forceinline__ void accumulate(const DrawRows<E>& r, const double (&av)[P], const double (&bv)[P],
+                                           const float (&zt)[P], const float (&zd)[P],
+                                           const bool (&dx_ok)[P], const bool (&live)[P], SweepAcc& s) {
+    bool pos[P], unc[P];
+    bool any_unc = false, any_inexact = false;
 #pragma unroll
     for (int k = 0; k < P; ++k) {
-        xt[k] = (double)zt[k] - r.mt;
-        xd[k] = r.residual ? (double)zd[k] - r.md : -INFINITY;
-        yt[k] = xt[k] * r.c256;
-        yd[k] = xd[k] * r.c256;
-        need |= fmax(yt[k], yd[k]) >= kSkipLog2 * 256.0;
+        const float Df = zt[k] - zd[k];
+        pos[k] = Df > r.tau_hi_f;
+        unc[k] = !pos[k] && Df >= r.tau_lo_f;
+        any_inexact |= !dx_ok[k];
     }
-    if (!__any(need)) return;  // the whole wave: weights below 2^-80 of the row maxima
-    if (!r.residual) {
-#pragma unroll
-        for (int k = 0; k < P; ++k) s.sp += exp2_256(yt[k], r.tab);
-        return;
-    }
-    double av[P], bv[P], D[P];
-    bool unc[P];
-    bool any_unc = false;
-#pragma unroll
-    for (int k = 0; k < P; ++k) {
-        av[k] = exp2_256(yt[k], r.tab);
-        bv[k] = exp2_256(yd[k], r.tab);
-        s.sp += av[k];
-        s.sq += bv[k];
-        D[k] = xt[k] - xd[k];
-        const bool pos = D[k] > s.tau_hi;
-        unc[k] = !pos && D[k] >= s.tau_lo;
-        any_unc |= unc[k];
-        const double sel = pos ? 1.0 : 0.0;
-        s.A = __builtin_fma(av[k], sel, s.A);
-        s.B = __builtin_fma(bv[k], sel, s.B);
-    }
-    if (__any(any_unc)) {  // rare
-#pragma unroll
-        for (int k = 0; k < P; ++k) bucket_add(s, unc[k], D[k], av[k], bv[k]);
-    }
-}
-
-// ---- the bf16 path: weights looked up in the per-sequence tables (kTabE0 .. kTabNE) ----
-
-// Table index of the bf16 bit pattern h (in the low 16 bits), clamped into the table, and
-// whether h lies inside it.
-__device__ __forceinline__ uint32_t tab_index(uint32_t h, bool& in) {
-    const uint32_t off = (h & 0x7fffu) - (uint32_t)(kTabE0 * 128);
-    in = off < (uint32_t)kTabHalf;
-    return min(off, (uint32_t)(kTabHalf - 1)) + (h >> 15) * (uint32_t)kTabHalf;
-}
-
-__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
-
-// P positions of this lane given as bf16 bit patterns; ta, tb the LDS tables of the target
-// and draft rows.  Logits outside the tables take the polynomial (rare: tiny, very large
-// or infinite values); both give the same fp64 value for the same logit.
-template <bool Residual, int P>
-__device__ __forceinline__ void sweep_tab(const DrawRows<uint16_t>& r, const double* ta, const double* tb,
-                                          const uint32_t (&ht)[P], const uint32_t (&hd)[P], SweepAcc& s) {
-    double av[P], bv[P];
-    bool in_all = true;
-#pragma unroll
-    for (int k = 0; k < P; ++k) {
-        bool it, id = true;
-        av[k] = ta[tab_index(ht[k], it)];
-        if (Residual) bv[k] = tb[tab_index(hd[k], id)];
-        in_all = in_all && it && id;
-    }
-    if (!__all(in_all)) {
+    if (__any(any_inexact)) {  // rare: a logit outside the table range, classify in fp64
 #pragma unroll
         for (int k = 0; k < P; ++k) {
-            bool it, id = true;
-            tab_index(ht[k], it);
-            if (!it) av[k] = r.a_of(bf16_bits_to_float(ht[k]));
-            if (Residual) {
-                tab_index(hd[k], id);
-                if (!id) bv[k] = r.b_of(bf16_bits_to_float(hd[k]));
+            if (!dx_ok[k]) {
+                const double D = (double)zt[k] - (double)zd[k];
+                pos[k] = D > r.tau_hi;
+                unc[k] = !pos[k] && D >= r.tau_lo;
             }
         }
     }
-    if (!Residual) {
-#pragma unroll
-        for (int k = 0; k < P; ++k) s.sp += av[k];
-        return;
-    }
-    bool unc[P];
-    bool any_unc = false;
 #pragma unroll
     for (int k = 0; k < P; ++k) {
+        unc[k] = unc[k] && live[k];
+        any_unc |= unc[k];
         s.sp += av[k];
         s.sq += bv[k];
-        const bool pos = av[k] > s.rho_hi * bv[k];
-        unc[k] = !pos && av[k] > 0.0 && av[k] >= s.rho_lo * bv[k];
-        any_unc |= unc[k];
-        const double sel = pos ? 1.0 : 0.0;
+        const double sel = pos[k] ? 1.0 : 0.0;
         s.A = __builtin_fma(av[k], sel, s.A);
         s.B = __builtin_fma(bv[k], sel, s.B);
     }
     if (__any(any_unc)) {  // rare: bucket by the exact logit difference
 #pragma unroll
-        for (int k = 0; k < P; ++k) {
-            const double D = ((double)bf16_bits_to_float(ht[k]) - r.mt) - ((double)bf16_bits_to_float(hd[k]) - r.md);
-            bucket_add(s, unc[k], D, av[k], bv[k]);
-        }
+        for (int k = 0; k < P; ++k) bucket_add(s, unc[k], (double)zt[k] - (double)zd[k], av[k], bv[k]);
     }
 }
 
-// One wave per sub-chunk of chunk c of the draw row(s) of sequence b, bf16 logits, tables
-// in LDS.
+// Two bf16 positions of each row (one 32-bit word each), weights from the LDS table.
 template <bool Residual>
-__device__ __forceinline__ void sweep_chunk_tab(const VerifyArgs& a, const DrawRows<uint16_t>& r,
-                                                const SeqDesc& d, const double* ta, const double* tb,
-                                                int b, int c) {
-    constexpr int VEC = 8;
-    constexpr int kG = SV_SWEEP_VECTORS;
-    const int V = a.V;
-    const int lane = threadIdx.x & 63, w = (threadIdx.x >> 6) & (kWaves - 1);
-    const int sub = a.ch2 / kWaves;
-    const int lo = min(V, c * a.ch2 + w * sub);
-    const int hi = min(V, lo + sub);
-    const int64_t e = ((int64_t)b * a.ns2 + c) * kWaves + w;
-    SweepAcc acc;
-    acc.tau_hi = acc.tau_lo = 0.0;
-    acc.rho_hi = acc.rho_lo = 1.0;
-    if (Residual) {
-        const double rho1 = d.St / d.Sd;
-        acc.rho_hi = rho1 * (1.0 + kDelta);
-        acc.rho_lo = rho1 * (1.0 - kDelta);
+__device__ __forceinline__ void sweep_word_tab(const DrawRows<uint16_t>& r, uint32_t wt, uint32_t wd,
+                                               SweepAcc& s) {
+    const float zt[2] = {__uint_as_float(wt << 16), __uint_as_float(wt & 0xffff0000u)};
+    const float zd[2] = {__uint_as_float(wd << 16), __uint_as_float(wd & 0xffff0000u)};
+    bool nt[2], nd[2];
+    bool any = false;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        nt[k] = zt[k] >= r.thr_t;
+        nd[k] = Residual && zd[k] >= r.thr_d;
+        any |= nt[k] || nd[k];
     }
-    acc.lane = lane;
+    if (!__any(any)) return;  // the whole wave: every weight flushed
+    double av[2], bv[2];
+    bool it[2], id[2], live[2];
+    bool slow = false;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t kt = tab_index(__float_as_uint(zt[k]) >> 16, it[k]);
+        av[k] = nt[k] ? r.wt[kt] : 0.0;
+        id[k] = true;
+        bv[k] = 0.0;
+        if (Residual) {
+            const uint32_t kd = tab_index(__float_as_uint(zd[k]) >> 16, id[k]);
+            bv[k] = nd[k] ? r.wt[kd] : 0.0;
+        }
+        live[k] = nt[k] || nd[k];
+        slow |= (nt[k] && !it[k]) || (nd[k] && !id[k]);
+    }
+    if (__any(slow)) {  // rare: a weight outside the table range
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if (nt[k] && !it[k]) av[k] = r.a_of(zt[k]);
+            if (Residual && nd[k] && !id[k]) bv[k] = r.b_of(zd[k]);
+        }
+    }
+    if (!Residual) {
+        s.sp += av[0];
+        s.sp += av[1];
+        return;
+    }
+    // a difference of two bf16 values with |z| in [2^-10, 32) is exact in fp32; positions
+    // whose weights are both flushed need no sign
+    const bool dx_ok[2] = {(it[0] && id[0]) || !live[0], (it[1] && id[1]) || !live[1]};
+    accumulate<uint16_t, 2>(r, av, bv, zt, zd, dx_ok, live, s);
+}
 
+// P positions of each row, weights by the fp64 exponential (fp32 logits, or rows that do
+// not share a reference).
+template <typename E, int P>
+__device__ __forceinline__ void sweep_vec_exp(const DrawRows<E>& r, const float (&zt)[P], const float (&zd)[P],
+                                              SweepAcc& s) {
+    bool nt[P], nd[P], live[P];
+    bool any = false;
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+        nt[k] = zt[k] >= r.thr_t;
+        nd[k] = r.residual && zd[k] >= r.thr_d;
+        live[k] = nt[k] || nd[k];
+        any |= live[k];
+    }
+    if (!__any(any)) return;
+    double av[P], bv[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+        av[k] = nt[k] ? exp2_256(exp2_arg((double)zt[k], r.refA, r.c256), r.tab) : 0.0;
+        bv[k] = nd[k] ? exp2_256(exp2_arg((double)zd[k], r.refB, r.c256), r.tab) : 0.0;
+    }
+    if (!r.residual) {
+#pragma unroll
+        for (int k = 0; k < P; ++k) s.sp += av[k];
+        return;
+    }
+    bool dx_ok[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k) dx_ok[k] = !live[k];  // fp32 differences may round: fp64
+    accumulate<E, P>(r, av, bv, zt, zd, dx_ok, live, s);
+}
+
+// Writes the wave's partial (lane 0) and buckets (lanes below nbkt).
+__device__ __forceinline__ void store_partial(const VerifyArgs& a, int64_t e, SweepAcc& acc) {
+    const double sp = wave_sum(acc.sp);
+    const double sq = wave_sum(acc.sq);
+    const double A = wave_sum(acc.A);
+    const double Bm = wave_sum(acc.B);
+    if (acc.lane < acc.nbkt && acc.lane < kBuckets) {
+        Bucket bk;
+        bk.a = acc.bA;
+        bk.b = acc.bB;
+        a.bkt[e * kBuckets + acc.lane] = bk;
+    }
+    if (acc.lane == 0) {
+        DrawPartial dp;
+        dp.sp = sp;
+        dp.sq = sq;
+        dp.A = A;
+        dp.B = Bm;
+        dp.nbkt = acc.nbkt;
+        dp.pad[0] = dp.pad[1] = dp.pad[2] = 0;
+        a.part2[e] = dp;
+    }
+}
+
+// Wave w's sub-chunk of chunk c: [lo, hi).
+__device__ __forceinline__ void sub_range(const VerifyArgs& a, int c, int w, int& lo, int& hi) {
+    const int sub = a.ch2 / kWaves;
+    lo = min(a.V, c * a.ch2 + w * sub);
+    hi = min(a.V, lo + sub);
+}
+
+// bf16 rows with the LDS table: whole spans of 64 lanes x kG vectors per row, the next
+// span's loads issued before the current one is processed; the rest (a partial span at
+// the end, or rows not 16-byte aligned) one position per lane.
+template <bool Residual>
+__device__ __forceinline__ void sweep_sub_tab(const DrawRows<uint16_t>& r, int lo, int hi, SweepAcc& acc) {
+    constexpr int VEC = 8;
+    const int lane = acc.lane;
     const int span = 64 * kG * VEC;
     const int hi_whole = r.vec_ok ? lo + ((hi - lo) / span) * span : lo;
     u32x4 rt[kG], rd[kG];
@@ -505,7 +605,7 @@ __device__ __forceinline__ void sweep_chunk_tab(const VerifyArgs& a, const DrawR
         for (int g = 0; g < kG; ++g) {
             const int i = s0 + (g * 64 + lane) * VEC;
             rt[g] = load16(r.t + i);
-            rd[g] = Residual ? load16(r.d + i) : rt[g];
+            if (Residual) rd[g] = load16(r.d + i);
         }
     };
     if (lo < hi_whole) fetch(lo);
@@ -514,143 +614,72 @@ __device__ __forceinline__ void sweep_chunk_tab(const VerifyArgs& a, const DrawR
 #pragma unroll
         for (int g = 0; g < kG; ++g) {
             wt[g][0] = rt[g].x; wt[g][1] = rt[g].y; wt[g][2] = rt[g].z; wt[g][3] = rt[g].w;
-            wd[g][0] = rd[g].x; wd[g][1] = rd[g].y; wd[g][2] = rd[g].z; wd[g][3] = rd[g].w;
+            if (Residual) {
+                wd[g][0] = rd[g].x; wd[g][1] = rd[g].y; wd[g][2] = rd[g].z; wd[g][3] = rd[g].w;
+            } else {
+                wd[g][0] = wd[g][1] = wd[g][2] = wd[g][3] = 0u;
+            }
         }
         if (s0 + span < hi_whole) fetch(s0 + span);
 #pragma unroll
-        for (int g = 0; g < kG; ++g) {
+        for (int g = 0; g < kG; ++g)
 #pragma unroll
-            for (int q = 0; q < 4; q += 2) {  // 4 positions: two words of two bf16 each
-                const uint32_t ht[4] = {wt[g][q] & 0xffffu, wt[g][q] >> 16, wt[g][q + 1] & 0xffffu, wt[g][q + 1] >> 16};
-                const uint32_t hd[4] = {wd[g][q] & 0xffffu, wd[g][q] >> 16, wd[g][q + 1] & 0xffffu, wd[g][q + 1] >> 16};
-                sweep_tab<Residual>(r, ta, tb, ht, hd, acc);
-            }
-        }
+            for (int q = 0; q < 4; ++q) sweep_word_tab<Residual>(r, wt[g][q], wd[g][q], acc);
     }
-    // the rest (a partial span, or rows not 16-byte aligned): one position per lane; lanes
-    // past the end see -inf (0xff80), which lies outside the tables and weighs 0
 #pragma unroll 1
-    for (int i0 = hi_whole; i0 < hi; i0 += 64) {
-        const int i = i0 + lane;
-        const bool in = i < hi;
-        const uint32_t t1[1] = {in ? (uint32_t)r.t[i] : 0xff80u};
-        const uint32_t d1[1] = {(in && Residual) ? (uint32_t)r.d[i] : 0xff80u};
-        sweep_tab<Residual>(r, ta, tb, t1, d1, acc);
-    }
-    const double sp = wave_sum(acc.sp);
-    const double sq = wave_sum(acc.sq);
-    const double A = wave_sum(acc.A);
-    const double Bm = wave_sum(acc.B);
-    if (lane < acc.nbkt && lane < kBuckets) {
-        Bucket bk;
-        bk.a = acc.bA;
-        bk.b = acc.bB;
-        a.bkt[e * kBuckets + lane] = bk;
-    }
-    if (lane == 0) {
-        DrawPartial dp;
-        dp.sp = sp;
-        dp.sq = sq;
-        dp.A = A;
-        dp.B = Bm;
-        dp.nbkt = acc.nbkt;
-        dp.pad[0] = dp.pad[1] = dp.pad[2] = 0;
-        a.part2[e] = dp;
+    for (int i0 = hi_whole; i0 < hi; i0 += 128) {
+        const int i = i0 + 2 * lane;
+        // lanes past the end see -inf (0xff80), which is flushed
+        const uint32_t t0 = i < hi ? (uint32_t)r.t[i] : 0xff80u;
+        const uint32_t t1 = i + 1 < hi ? (uint32_t)r.t[i + 1] : 0xff80u;
+        uint32_t d0 = 0xff80u, d1 = 0xff80u;
+        if (Residual) {
+            d0 = i < hi ? (uint32_t)r.d[i] : 0xff80u;
+            d1 = i + 1 < hi ? (uint32_t)r.d[i + 1] : 0xff80u;
+        }
+        sweep_word_tab<Residual>(r, t0 | (t1 << 16), d0 | (d1 << 16), acc);
     }
 }
 
-// One wave per sub-chunk of chunk c of the draw row(s) of sequence b.
+// Any logits with the fp64 exponential.
 template <typename E>
-__device__ __forceinline__ void sweep_chunk(const VerifyArgs& a, const DrawRows<E>& r, const SeqDesc& d,
-                                            int b, int c) {
+__device__ __forceinline__ void sweep_sub_exp(const DrawRows<E>& r, int lo, int hi, SweepAcc& acc) {
     constexpr int VEC = Logit<E>::kVec;
-    constexpr int kG = SV_SWEEP_VECTORS;  // 16-byte vectors per row in flight per lane
-    constexpr int P = SV_SWEEP_POSITIONS < VEC ? SV_SWEEP_POSITIONS : VEC;
-
-    const int V = a.V;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int sub = a.ch2 / kWaves;
-    const int lo = min(V, c * a.ch2 + w * sub);
-    const int hi = min(V, lo + sub);
-    const int64_t e = ((int64_t)b * a.ns2 + c) * kWaves + w;
-    SweepAcc acc;
-    acc.tau_hi = acc.tau_lo = 0.0;
-    if (r.residual) {
-        const double rho1 = d.St / d.Sd;
-        acc.tau_hi = (double)d.T * log(rho1 * (1.0 + kDelta));
-        acc.tau_lo = (double)d.T * log(rho1 * (1.0 - kDelta));
-    }
-    acc.lane = lane;
-
-    // whole, aligned spans of 64 lanes x kG vectors per row; the next span's loads are
-    // issued before the current span is processed
-    const int span = 64 * kG * VEC;
+    constexpr int P = 4;
+    const int lane = acc.lane;
+    const int span = 64 * VEC;
     const int hi_whole = r.vec_ok ? lo + ((hi - lo) / span) * span : lo;
-    u32x4 rt[kG], rd[kG];
-    auto fetch = [&](int s0) {
+    for (int s0 = lo; s0 < hi_whole; s0 += span) {
+        const int i = s0 + lane * VEC;
+        float zt[VEC], zd[VEC];
+        Logit<E>::unpack(load16(r.t + i), zt);
+        if (r.residual) Logit<E>::unpack(load16(r.d + i), zd);
+        else
 #pragma unroll
-        for (int g = 0; g < kG; ++g) {
-            const int i = s0 + (g * 64 + lane) * VEC;
-            rt[g] = load16(r.t + i);
-            rd[g] = r.residual ? load16(r.d + i) : rt[g];
-        }
-    };
-    if (lo < hi_whole) fetch(lo);
-    for (int s0 = lo; s0 < hi_whole; s0 += span) {  // wave-uniform trip count
-        float zt[kG][VEC], zd[kG][VEC];
+            for (int k = 0; k < VEC; ++k) zd[k] = -INFINITY;
 #pragma unroll
-        for (int g = 0; g < kG; ++g) {
-            Logit<E>::unpack(rt[g], zt[g]);
-            Logit<E>::unpack(rd[g], zd[g]);
-        }
-        if (s0 + span < hi_whole) fetch(s0 + span);
+        for (int h = 0; h < VEC; h += P) {
+            float tp[P], dp[P];
 #pragma unroll
-        for (int g = 0; g < kG; ++g) {
-#pragma unroll
-            for (int h = 0; h < VEC; h += P) {  // P positions at a time (constant indices)
-                float tp[P], dp[P];
-#pragma unroll
-                for (int k = 0; k < P; ++k) {
-                    tp[k] = zt[g][h + k];
-                    dp[k] = zd[g][h + k];
-                }
-                sweep_vec(r, tp, dp, acc);
+            for (int k = 0; k < P; ++k) {
+                tp[k] = zt[h + k];
+                dp[k] = zd[h + k];
             }
+            sweep_vec_exp<E, P>(r, tp, dp, acc);
         }
     }
-    // the rest (a partial span at the end, or rows not 16-byte aligned): one position per lane
 #pragma unroll 1
     for (int i0 = hi_whole; i0 < hi; i0 += 64) {
         const int i = i0 + lane;
         const bool in = i < hi;
         const float t1[1] = {in ? Logit<E>::at(r.t, i) : -INFINITY};
         const float d1[1] = {(in && r.residual) ? Logit<E>::at(r.d, i) : -INFINITY};
-        sweep_vec(r, t1, d1, acc);
-    }
-    const double sp = wave_sum(acc.sp);
-    const double sq = wave_sum(acc.sq);
-    const double A = wave_sum(acc.A);
-    const double Bm = wave_sum(acc.B);
-    if (lane < acc.nbkt && lane < kBuckets) {
-        Bucket bk;
-        bk.a = acc.bA;
-        bk.b = acc.bB;
-        a.bkt[e * kBuckets + lane] = bk;
-    }
-    if (lane == 0) {
-        DrawPartial dp;
-        dp.sp = sp;
-        dp.sq = sq;
-        dp.A = A;
-        dp.B = Bm;
-        dp.nbkt = acc.nbkt;
-        dp.pad[0] = dp.pad[1] = dp.pad[2] = 0;
-        a.part2[e] = dp;
+        sweep_vec_exp<E, 1>(r, t1, d1, acc);
     }
 }
 
 // ------------------------------------------------------------------------------------
-// final: grid = sequences, one workgroup each
+// final
 // ------------------------------------------------------------------------------------
 
 // Smallest i in [lo, hi) with base + (w_lo + ... + w_i) > target, in tiles of VEC positions
@@ -659,7 +688,7 @@ __device__ __forceinline__ void sweep_chunk(const VerifyArgs& a, const DrawRows<
 // If no index qualifies (rounding), the last index with positive weight; -1 if none.
 // lo must be a multiple of VEC.
 template <typename E>
-__device__ int block_search(const DrawRows<E>& r, int lo, int hi, double base, double target,
+__device__ __forceinline__ int block_search(const DrawRows<E>& r, int lo, int hi, double base, double target,
                             bool standalone, double u) {
     constexpr int VEC = Logit<E>::kVec;
     constexpr int kTile = VEC * kThreads;
@@ -712,49 +741,49 @@ __device__ int block_search(const DrawRows<E>& r, int lo, int hi, double base, d
     return block_max(lastpos, shi);
 }
 
-// The draw of sequence b from the partials of all its chunks.
+// The draw of sequence b from the partials of all its chunks, by one workgroup.
 template <typename E>
-__device__ void final_seq(const VerifyArgs& a, DrawRows<E> r, const SeqDesc& d, int b) {
+__device__ __forceinline__ void final_seq(const VerifyArgs& a, DrawRows<E> r, const SeqDesc& d, int b) {
     __shared__ double shd[kWaves];
     __shared__ int shi[kWaves];
     __shared__ double sh_base;
     const int tid = threadIdx.x;
     const int nsub = a.nchunk2 * kWaves;
-    const int sub = a.ch2 / kWaves;
     const int64_t e0 = (int64_t)b * a.ns2 * kWaves;
     const double u = (double)d.u;
     int status = 0;
 
-    // fp64 normalisers and the check that rho' classified every position
-    bool exact_ok = true;
-    if (r.residual) {
-        double sp = 0.0, sq = 0.0;
-        int over = 0;
-        for (int k = tid; k < nsub; k += kThreads) {
-            const DrawPartial dp = a.part2[e0 + k];
-            sp += dp.sp;
-            sq += dp.sq;
-            over |= dp.nbkt > kBuckets;
-        }
-        sp = block_sum(sp, shd);
-        sq = block_sum(sq, shd);
-        over = block_or(over, shi);
-        r.inv_sp = 1.0 / sp;
-        r.inv_sq = 1.0 / sq;
-        const double rho = sp / sq;
-        const double rho1 = d.St / d.Sd;
-        exact_ok = !over && rho >= rho1 * (1.0 - 0.5 * kDelta) && rho <= rho1 * (1.0 + 0.5 * kDelta);
-#ifdef SV_DEBUG_FINAL
-        if (tid == 0 && a.out_p) {
-            a.out_p[(int64_t)b * a.K] = (float)(rho / rho1 - 1.0);
-            status |= (over ? 128 : 0) | (exact_ok ? 0 : 64);
-        }
-#endif
+    // fp64 normalisers; the classification by the pass-1 estimate stands if the exact
+    // threshold T ln(S_p/S_q) + refA - refB lies well inside the bracket
+    double sp = 0.0, sq = 0.0;
+    int over = 0;
+    for (int k = tid; k < nsub; k += kThreads) {
+        const DrawPartial dp = a.part2[e0 + k];
+        sp += dp.sp;
+        sq += dp.sq;
+        over |= dp.nbkt > kBuckets;
     }
+    sp = block_sum(sp, shd);
+    sq = block_sum(sq, shd);
+    over = block_or(over, shi);
+    bool exact_ok = sp > 0.0;
+    if (r.residual) {
+        exact_ok = exact_ok && sq > 0.0 && !over;
+        if (exact_ok) {
+            const double T = (double)d.T;
+            const double tau = T * (log(sp) - log(sq)) + (r.refA - r.refB);
+            const double mid = 0.5 * (r.tau_lo + r.tau_hi);
+            const double half = 0.5 * (r.tau_hi - r.tau_lo);
+            // keep half of the bracket as the margin, and stay far above fp64 rounding
+            exact_ok = fabs(tau - mid) <= 0.5 * half && half > 1e-12 * (fabs(mid) + 1.0);
+        }
+    }
+    r.inv_sp = 1.0 / sp;
+    r.inv_sq = r.residual ? 1.0 / sq : 1.0;
 
     int y;
     if (!exact_ok) {
-        // the pass-1 estimate was off, or too many undecided positions: one exact sweep
+        // too many undecided positions, or the estimate was off: one exact sweep
         y = block_search(r, 0, a.V, 0.0, 0.0, true, u);
     } else {
         // mass of sub-chunk k in the units of the draw: its certain part and, per bucket of
@@ -780,10 +809,7 @@ __device__ void final_seq(const VerifyArgs& a, DrawRows<E> r, const SeqDesc& d, 
         }
         const double total = carry;
         if (!(total > 0.0)) {
-            // residual without fp64 mass (exact arithmetic rules it out): draw from p_n
-            status |= kSeqNoteFallback;
-            r.residual = 0;
-            y = block_search(r, 0, a.V, 0.0, 0.0, true, u);
+            y = -1;
         } else {
             const double target = u * total;
             carry = 0.0;
@@ -818,11 +844,16 @@ __device__ void final_seq(const VerifyArgs& a, DrawRows<E> r, const SeqDesc& d, 
             } else {
                 base = sh_base;
             }
-            const int c = hit / kWaves, w = hit % kWaves;
-            const int lo = min(a.V, c * a.ch2 + w * sub);
-            const int hi = min(a.V, lo + sub);
+            int lo, hi;
+            sub_range(a, hit / kWaves, hit % kWaves, lo, hi);
             y = block_search(r, lo, hi, base, tgt, false, u);
         }
+    }
+    if (y < 0) {
+        // residual without fp64 mass (exact arithmetic rules it out): draw from p_n
+        status |= kSeqNoteFallback;
+        r.residual = 0;
+        y = block_search(r, 0, a.V, 0.0, 0.0, true, u);
     }
     if (tid == 0) {
         a.out_tokens[(int64_t)b * (a.K + 1) + d.n] = y;
@@ -830,98 +861,88 @@ __device__ void final_seq(const VerifyArgs& a, DrawRows<E> r, const SeqDesc& d, 
     }
 }
 
-
 // ------------------------------------------------------------------------------------
-// the kernels
+// the kernel
 // ------------------------------------------------------------------------------------
 
-// grid = sequences: the resolve; writes its outputs and the sequence's SeqDesc, and for
-// bf16 logits the weight tables of the draw row(s), entry by entry the same fp64 function
-// as DrawRows::a_of / b_of.
 template <typename E>
-__global__ __launch_bounds__(kThreads) void resolve_kernel(VerifyArgs a, int b0) {
-    __shared__ double tab[kExpTable];
-    const int b = b0 + blockIdx.x;
-    const SeqDesc d = resolve_seq<E>(a, b, true);
-    if (threadIdx.x == 0) reinterpret_cast<SeqDesc*>(a.desc)[b] = d;
-    if constexpr (sizeof(E) == 2) {
-        if (d.mode == kModeNone) return;  // whole workgroup
-        exp2_table_init(tab);
-        const DrawRows<E> r = draw_rows<E>(a, b, d, tab);
-        double* dst = a.wtab + (int64_t)b * 2 * kTabLen;
-        for (int k = threadIdx.x; k < kTabLen; k += kThreads) {
-            const uint32_t h = (k < kTabHalf ? 0u : 0x8000u) | (uint32_t)(kTabE0 * 128 + k % kTabHalf);
-            const float z = bf16_bits_to_float(h);
-            dst[k] = r.a_of(z);
-            if (r.residual) dst[kTabLen + k] = r.b_of(z);
-        }
-    }
-}
+struct DrawLds {
+    static constexpr int kWt = sizeof(E) == 2 ? kTabLen : 1;
+};
 
-// Workgroups of the bf16 sweep: kTabChunks chunks of kThreads each, sharing one copy of
-// the weight tables in LDS.
-constexpr int kTabChunks = 2;
+static_assert(sizeof(SeqDesc) <= kSeqDescBytes && kSeqDescBytes % alignof(SeqDesc) == 0,
+              "workspace slot of the descriptor");
 
-// grid = sequences x ceil(nchunk2 / kTabChunks), bf16: the sweep of kTabChunks chunks.
-__global__ __launch_bounds__(kThreads * kTabChunks) __attribute__((amdgpu_waves_per_eu(SV_TAB_WAVES)))
-void sweep_tab_kernel(VerifyArgs a, int b0) {
-    __shared__ double tab[kExpTable];
-    __shared__ double wt[2 * kTabLen];
-    const int ngrp = (a.nchunk2 + kTabChunks - 1) / kTabChunks;
-    const int b = b0 + (int)(blockIdx.x / (unsigned)ngrp);
-    const int c = (int)(blockIdx.x % (unsigned)ngrp) * kTabChunks + (int)(threadIdx.x / kThreads);
-    const SeqDesc d = reinterpret_cast<const SeqDesc*>(a.desc)[b];
-    if (d.mode == kModeNone) return;  // whole workgroup
-    const bool residual = d.mode == kModeResidual;
-    const int n16 = (residual ? 2 * kTabLen : kTabLen) / 2;  // 16-byte pieces
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.wtab + (int64_t)b * 2 * kTabLen);
-    u32x4* dst = reinterpret_cast<u32x4*>(wt);
-    for (int k = threadIdx.x; k < n16; k += blockDim.x) dst[k] = src[k];
-    exp2_table_init(tab);  // its barrier also publishes wt
-    if (c >= a.nchunk2) return;  // no barrier follows
-    const DrawRows<uint16_t> r = draw_rows<uint16_t>(a, b, d, tab);
-    if (residual) sweep_chunk_tab<true>(a, r, d, wt, wt + kTabLen, b, c);
-    else sweep_chunk_tab<false>(a, r, d, wt, wt, b, c);
-}
-
-// grid = sequences x nchunk2, fp32: the sweep of chunk c of the sequence's draw row(s).
+// grid = sequences x nchunk2.  Every workgroup resolves its sequence; the chunk-0
+// workgroup writes the outputs and the sequence's SeqDesc.  Sampled sequences: each
+// workgroup sweeps chunk c of the draw row(s) into its per-wave partials.
 template <typename E>
-__global__ __launch_bounds__(kThreads) void sweep_kernel(VerifyArgs a, int b0) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SV_DRAW_WAVES)))
+void sweep_kernel(VerifyArgs a, int b0) {
     __shared__ double tab[kExpTable];
+    __shared__ double wt[DrawLds<E>::kWt];
     const int b = b0 + (int)(blockIdx.x / (unsigned)a.nchunk2);
     const int c = (int)(blockIdx.x % (unsigned)a.nchunk2);
-    const SeqDesc d = reinterpret_cast<const SeqDesc*>(a.desc)[b];
+    if (c != 0) {
+        // only sampled sequences need more than the chunk-0 workgroup
+        const float T = a.temperature ? a.temperature[b] : 0.0f;
+        if (T == 0.0f) return;  // whole workgroup
+    }
+    const SeqDesc d = resolve_seq<E>(a, b, c == 0);
+    if (c == 0 && threadIdx.x == 0) reinterpret_cast<SeqDesc*>(a.desc)[b] = d;
     if (d.mode == kModeNone) return;  // whole workgroup
     exp2_table_init(tab);
-    sweep_chunk<E>(a, draw_rows<E>(a, b, d, tab), d, b, c);
+    DrawRows<E> r = draw_rows<E>(a, b, d, tab, wt);
+    if constexpr (sizeof(E) == 2) {
+        if (r.use_tab) weight_table_init(r, wt);
+    }
+
+    const int w = threadIdx.x >> 6;
+    SweepAcc acc;
+    acc.lane = threadIdx.x & 63;
+    int lo, hi;
+    sub_range(a, c, w, lo, hi);
+    if constexpr (sizeof(E) == 2) {
+        if (r.use_tab) {
+            if (r.residual) sweep_sub_tab<true>(r, lo, hi, acc);
+            else sweep_sub_tab<false>(r, lo, hi, acc);
+        } else {
+            sweep_sub_exp<E>(r, lo, hi, acc);
+        }
+    } else {
+        sweep_sub_exp<E>(r, lo, hi, acc);
+    }
+    store_partial(a, ((int64_t)b * a.ns2 + c) * kWaves + w, acc);
 }
 
-// grid = sequences: the draw from the partials of all chunks.
+// grid = sequences: the draw of each sampled sequence from the partials of all its chunks.
+// Weights come from the fp64 exponential, which gives exactly the sweep's table values
+// (the table holds the same function of the same arguments).
 template <typename E>
 __global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a, int b0) {
     __shared__ double tab[kExpTable];
-    const int b = b0 + blockIdx.x;
+    const int b = b0 + (int)blockIdx.x;
     const SeqDesc d = reinterpret_cast<const SeqDesc*>(a.desc)[b];
-    if (d.mode == kModeNone) return;
+    if (d.mode == kModeNone) return;  // whole workgroup
     exp2_table_init(tab);
-    final_seq<E>(a, draw_rows<E>(a, b, d, tab), d, b);
+    DrawRows<E> r = draw_rows<E>(a, b, d, tab, nullptr);
+    r.use_tab = 0;
+    final_seq<E>(a, r, d, b);
 }
 
 }  // namespace
 
 template <typename E>
-void launch_all(const VerifyArgs& a, int b0, int b1, hipStream_t s) {
-    hipLaunchKernelGGL(resolve_kernel<E>, dim3(b1 - b0), dim3(kThreads), 0, s, a, b0);
-    if (!a.temperature) return;  // greedy only: the resolve is everything
-    if constexpr (sizeof(E) == 2) {
-        const int ngrp = (a.nchunk2 + kTabChunks - 1) / kTabChunks;
-        const unsigned blocks = (unsigned)((int64_t)(b1 - b0) * ngrp);
-        hipLaunchKernelGGL(sweep_tab_kernel, dim3(blocks), dim3(kThreads * kTabChunks), 0, s, a, b0);
-    } else {
-        const unsigned blocks = (unsigned)((int64_t)(b1 - b0) * a.nchunk2);
-        hipLaunchKernelGGL(sweep_kernel<E>, dim3(blocks), dim3(kThreads), 0, s, a, b0);
+void launch_all(const VerifyArgs& a0, int b0, int b1, hipStream_t s) {
+    VerifyArgs a = a0;
+    if (!a.temperature) {  // greedy only: the resolve is everything, one workgroup each
+        a.nchunk2 = 1;
+        a.ch2 = a.V;
     }
-    hipLaunchKernelGGL(final_kernel<E>, dim3(b1 - b0), dim3(kThreads), 0, s, a, b0);
+    const unsigned blocks = (unsigned)((int64_t)(b1 - b0) * a.nchunk2);
+    hipLaunchKernelGGL(sweep_kernel<E>, dim3(blocks), dim3(kThreads), 0, s, a, b0);
+    if (a.temperature)
+        hipLaunchKernelGGL(final_kernel<E>, dim3((unsigned)(b1 - b0)), dim3(kThreads), 0, s, a, b0);
 }
 
 int launch_draw(const VerifyArgs& a, int bf16, int b0, int b1, void* stream) {
