@@ -64,7 +64,7 @@ size_t workspace_need(int B, int K, int V) {
 
 bool grid_ok(int B, int R, const Layout& L) {
     const __int128 blocks1 = (__int128)B * R * L.nchunk1;
-    const __int128 blocks2 = (__int128)B * L.ns2;
+    const __int128 blocks2 = (__int128)B * L.nseg;
     return blocks1 <= 0x7fffffff && blocks2 <= 0x7fffffff;
 }
 
@@ -86,8 +86,8 @@ sv::VerifyArgs make_args(const void* target, const void* draft, const int32_t* t
     a.R = R;
     a.nchunk1 = L.nchunk1;
     a.ch1 = L.ch1;
-    a.ns2 = L.ns2;
-    sv::chunking2(B, V, a.nchunk2, a.ch2);
+    a.nseg = L.nseg;
+    sv::chunking2(B, V, a.nchunk2, a.spc);
     a.desc = ws + L.off_desc;
     a.part1 = reinterpret_cast<sv::RowPartial*>(ws + L.off_part1);
     a.part2 = reinterpret_cast<sv::DrawPartial*>(ws + L.off_part2);

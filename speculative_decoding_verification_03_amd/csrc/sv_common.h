@@ -24,14 +24,15 @@ constexpr int kModeBonus = 2;     // draw from p_K
 
 // One (row, chunk) result of pass 1.  Greedy rows: m = chunk max, idx = lowest index
 // reaching it.  Sampled rows: m = chunk max, s = sum_i 2^((z_i - m) * c2) over the chunk,
-// c2 = fp32(log2(e) / T) (fp32 exponentials, fp64 sum).
+// c2 = fp32(log2(e) / T) (fp32 exponentials, fp64 sum); idx = the bits of the fp32 logit at
+// the row's draft token when that token lies in the chunk.
 struct alignas(16) RowPartial {
     float m;
     int32_t idx;
     double s;
 };
 
-// Sweep results per (sequence, chunk, wave sub-chunk), fp64, with
+// Sweep results per (sequence, segment of kSeg positions), fp64, with
 //   a_i = exp((zt_i - mt)/T) and b_i = exp((zd_i - md)/T):
 //   sp, sq = sum a_i, sum b_i;
 //   A, B   = sums of a_i, b_i over the positions whose residual is certainly positive;
@@ -50,19 +51,21 @@ struct alignas(16) Bucket {
     double a, b;
 };
 
-constexpr int kSubUnit = 1024;   // draw sub-chunks are multiples of 64 lanes x 16 positions
+constexpr int kSeg = 4096;         // positions per draw segment (one partial each)
 constexpr int kSeqDescBytes = 48;  // workspace slot of the resolve's per-sequence result
 
 struct Layout {
     int nchunk1, ch1;  // pass-1 chunks per row and elements per chunk (multiple of 64)
-    int ns2;           // draw chunks per sequence reserved in the workspace (any launch's
-                       // nchunk2 is at most this)
+    int nseg;          // draw segments per sequence: ceil(V / kSeg)
     size_t off_desc, off_part1, off_part2, off_bkt, total;
 };
 
 // Pass-1 chunks of about kChunkBytes1 (long streams per workgroup), more when the batch
 // is too small to fill the chip, never shorter than kMinChunk1 elements.
-constexpr int64_t kChunkBytes1 = 76 * 1024;
+#ifndef SV_P1_CHUNK_KB
+#define SV_P1_CHUNK_KB 76
+#endif
+constexpr int64_t kChunkBytes1 = SV_P1_CHUNK_KB * 1024;
 constexpr int kTargetBlocks1 = 4096;
 constexpr int kMinChunk1 = 4096;
 #ifndef SV_TARGET_BLOCKS2
@@ -85,19 +88,16 @@ inline void chunking1(int64_t rows, int V, int esize, int& nchunk1, int& ch1) {
     ch1 = (int)ch;
 }
 
-// Most draw chunks a sequence can have: chunks are whole multiples of kWaves sub-chunks of
-// kSubUnit positions.
-inline int max_chunks2(int V) { return (int)ceil_div(V, (int64_t)kWaves * kSubUnit); }
+inline int segments(int V) { return (int)ceil_div(V, (int64_t)kSeg); }
 
-// Draw chunks for a launch over `seqs` sequences: about kTargetBlocks2 workgroups.
-inline void chunking2(int64_t seqs, int V, int& nchunk2, int& ch2) {
-    const int64_t unit = (int64_t)kWaves * kSubUnit;
-    const int64_t maxc = max_chunks2(V);
+// Draw chunks (workgroups) per sequence for a launch over `seqs` sequences: about
+// kTargetBlocks2 workgroups in all; each chunk holds spc whole segments.
+inline void chunking2(int64_t seqs, int V, int& nchunk2, int& spc) {
+    const int64_t nseg = segments(V);
     const int64_t want = seqs > 0 ? ceil_div(kTargetBlocks2, seqs) : 1;
-    const int64_t n = want < 1 ? 1 : (want > maxc ? maxc : want);
-    const int64_t ch = ceil_div(ceil_div(V, n), unit) * unit;
-    nchunk2 = (int)ceil_div(V, ch);
-    ch2 = (int)ch;
+    const int64_t n = want < 1 ? 1 : (want > nseg ? nseg : want);
+    spc = (int)ceil_div(nseg, n);
+    nchunk2 = (int)ceil_div(nseg, spc);
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -108,16 +108,16 @@ inline Layout make_layout(int B, int K, int V, int esize, int rows_per_seq) {
     (void)esize;
     Layout L;
     chunking1((int64_t)B * rows_per_seq, V, esize, L.nchunk1, L.ch1);
-    L.ns2 = max_chunks2(V);
+    L.nseg = segments(V);
     size_t off = 0;
     L.off_desc = off;
     off = align256(off + kSeqDescBytes * (size_t)B);
     L.off_part1 = off;
     off = align256(off + sizeof(RowPartial) * (size_t)B * rows_per_seq * L.nchunk1);
     L.off_part2 = off;
-    off = align256(off + sizeof(DrawPartial) * kWaves * (size_t)B * L.ns2);
+    off = align256(off + sizeof(DrawPartial) * (size_t)B * L.nseg);
     L.off_bkt = off;
-    off = align256(off + sizeof(Bucket) * kBuckets * kWaves * (size_t)B * L.ns2);
+    off = align256(off + sizeof(Bucket) * kBuckets * (size_t)B * L.nseg);
     L.total = off;
     return L;
 }
@@ -130,12 +130,13 @@ struct VerifyArgs {
     const float* temperature;  // [B] (null when greedy-only)
     int B, K, V, R;            // R = rows per sequence handled by pass 1
     int nchunk1, ch1;          // pass-1 chunking
-    int nchunk2, ch2;          // draw chunking of this launch
-    int ns2;                   // draw chunks per sequence in the workspace arrays
+    int nchunk2, spc;          // draw chunking of this launch: chunks per sequence, segments
+                               // per chunk
+    int nseg;                  // draw segments per sequence
     void* desc;                // [B] the resolve's result per sequence (kSeqDescBytes each)
     RowPartial* part1;         // [B][R][nchunk1]
-    DrawPartial* part2;        // [B][ns2][kWaves]
-    Bucket* bkt;               // [B][ns2][kWaves][kBuckets]
+    DrawPartial* part2;        // [B][nseg]
+    Bucket* bkt;               // [B][nseg][kBuckets]
     int32_t* out_tokens;
     int32_t* out_n;
     float* out_p;

@@ -65,8 +65,9 @@ struct Logit<uint16_t> {
 // y = k/256 + f with k = rint(256 y) and |f| <= 1/512;  2^y = 2^(k>>8) * 2^((k&255)/256) * 2^f,
 // the middle factor from a 256-entry table, 2^f from its Taylor series in f*ln2 to degree 4
 // (truncation below 4e-17).  rint comes from adding 1.5 * 2^52, which leaves k in the low
-// word of the sum.  y is clamped at -1080, which maps -inf and every argument that
-// underflows to 0.  Relative error a few 1e-16.
+// word of the sum.  y is clamped to [-1080, 1100], which maps -inf and every argument that
+// underflows to 0, and +inf and every argument that overflows to inf.  Relative error a
+// few 1e-16.
 // ---------------------------------------------------------------------------------
 
 constexpr int kExpTable = 256;
@@ -112,7 +113,7 @@ __device__ __forceinline__ double exp2_256(double Y, const double* t) {
 #pragma clang fp contract(off)
     constexpr double kRound = 6755399441055744.0;  // 1.5 * 2^52: rounds to an integer
     constexpr double kL = 0.6931471805599453 / 256.0;
-    Y = fmax(Y, -1080.0 * 256.0);
+    Y = fmin(fmax(Y, -1080.0 * 256.0), 1100.0 * 256.0);
     const double tk = Y + kRound;
     const int k = __double2loint(tk);
     const double F = Y - (tk - kRound);

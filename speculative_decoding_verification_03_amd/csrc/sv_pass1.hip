@@ -27,7 +27,10 @@ namespace {
 
 constexpr double kLog2eD = 1.4426950408889634;
 constexpr float kRescaleLog2 = 32.0f;
-constexpr int kU = 4;  // 16-byte loads in flight per lane
+#ifndef SV_P1_LOADS
+#define SV_P1_LOADS 4
+#endif
+constexpr int kU = SV_P1_LOADS;  // 16-byte loads in flight per lane
 
 struct SumExpAcc {
     float mx;   // NaN-propagating maximum of everything seen
@@ -120,8 +123,10 @@ __device__ __forceinline__ void stream_tile(const E* row, int lo, int hi, FV&& f
     if (i < hi) fscal(Logit<E>::at(row, i), i);
 }
 
+// xi: the position of the row's draft token if it lies in this tile, else -1; its logit
+// goes into the partial for the resolve.
 template <typename E>
-__device__ void tile_sumexp(const E* row, int lo, int hi, float c2, RowPartial* out) {
+__device__ void tile_sumexp(const E* row, int lo, int hi, float c2, int xi, RowPartial* out) {
     __shared__ float shf[kWaves];
     __shared__ double shd[kWaves];
     SumExpAcc a{-INFINITY, -FLT_MAX, 0.0};
@@ -139,7 +144,7 @@ __device__ void tile_sumexp(const E* row, int lo, int hi, float c2, RowPartial* 
     if (threadIdx.x == 0) {
         RowPartial r;
         r.m = m;
-        r.idx = 0;
+        r.idx = xi >= 0 ? __float_as_int(Logit<E>::at(row, xi)) : 0;
         r.s = s;
         *out = r;
     }
@@ -186,7 +191,16 @@ __global__ __launch_bounds__(kThreads) void pass1_kernel(VerifyArgs a, int b0) {
     const int lo = c * a.ch1;
     const int hi = min(a.V, lo + a.ch1);
     RowPartial* out = a.part1 + ((int64_t)b * a.R + j) * a.nchunk1 + c;
-    if (sampled) tile_sumexp<E>(row, lo, hi, (float)(kLog2eD / (double)T), out);
+    if (sampled) {
+        // target row t < K or draft row t: the draft token x_t, when it falls in this tile
+        const int t = j <= a.K ? j : j - a.K - 1;
+        int xi = -1;
+        if (t < a.K) {
+            const int x = a.tokens[(int64_t)b * a.K + t];
+            if (x >= lo && x < hi) xi = x;
+        }
+        tile_sumexp<E>(row, lo, hi, (float)(kLog2eD / (double)T), xi, out);
+    }
     else tile_argmax<E>(row, lo, hi, out);
 }
 

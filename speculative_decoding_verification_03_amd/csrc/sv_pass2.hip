@@ -49,8 +49,10 @@ namespace {
 constexpr double kLog2eD = 1.4426950408889634;
 // Bracket around the pass-1 normaliser ratio (pass-1 normalisers are within ~1e-6 of the
 // fp64 ones), and the part of it the exact ratio must fall in for the classification to
-// stand.
+// stand: ln(1 + kDelta) and ln(1 - kDelta).
 constexpr double kDelta = 8e-6;
+constexpr double kLnDeltaHi = 7.999968000170666e-06;
+constexpr double kLnDeltaLo = -8.000032000170667e-06;
 // Weights below 2^-kFlushLog2 of their row maximum count as 0.
 constexpr double kFlushLog2 = 70.0;
 // One shared weight reference for both rows while the row maxima differ by at most this
@@ -59,22 +61,30 @@ constexpr double kMaxRefGapLog2 = 900.0;
 // Row statistics of the resolve kept in LDS; rows past this are merged again on demand.
 constexpr int kRowsLds = 64;
 
-// bf16 weight table: bf16 values whose biased exponent is in [kTabE0, kTabE0 + kTabNE),
-// i.e. |z| in [2^-10, 32): kTabHalf positive values, then kTabHalf negative ones, in
-// bit-pattern order.
-constexpr int kTabE0 = 117;
-constexpr int kTabNE = 15;
-constexpr int kTabHalf = kTabNE * 128;
+// bf16 weight table in LDS: two halves of kTabHalf slots (positive, then negative values).
+// Slot q of a half holds the weight of the bf16 value whose 15-bit magnitude field is
+// kTabLo + q, for q in [1, kTabN]: biased exponents 117..131, |z| in [2^-10, 32).  Slots 0
+// and kTabN + 1 hold NaN: a magnitude outside the range is clamped onto them, so a sum
+// that met one turns NaN and its span is redone exactly.
+constexpr uint32_t kTabLo = 117 * 128 - 1;
+constexpr int kTabN = 15 * 128;
+constexpr uint32_t kTabHi = kTabLo + kTabN + 1;
+constexpr int kTabHalf = 2048;
 constexpr int kTabLen = 2 * kTabHalf;
 
-// Waves per SIMD the draw kernel's register allocation must allow (4 workgroups per CU).
+// Waves per SIMD the sweep kernel's register allocation must allow (4 workgroups per CU).
 #ifndef SV_DRAW_WAVES
 #define SV_DRAW_WAVES 4
 #endif
 
-// 16-byte vectors per row whose loads are in flight together per lane.
-constexpr int kG = 2;
-static_assert(kSubUnit % (64 * kG * 8) == 0, "draw sub-chunks are whole spans of bf16 vectors");
+// 16-byte vectors per row whose loads are in flight together per lane; a span is what one
+// wave covers with them.
+#ifndef SV_SWEEP_G
+#define SV_SWEEP_G 2
+#endif
+constexpr int kG = SV_SWEEP_G;
+constexpr int kSpan16 = 64 * kG * 8;
+static_assert(kSeg % kSpan16 == 0 && kSeg / kSpan16 <= 32, "draw segments are whole spans of bf16 vectors");
 
 // The resolve's result for one sequence.
 struct SeqDesc {
@@ -83,7 +93,10 @@ struct SeqDesc {
     float T;       // temperature
     float u;       // uniform of the final draw
     float mt, md;  // maxima of target row n and draft row n
-    double St, Sd; // pass-1 normalisers of those rows: sum exp((z - m) / T)
+    // residual draws: the bracket [tau_lo, tau_hi] on zt_i - zd_i around the sign threshold
+    // T ln(St/Sd) + mt - md, St and Sd the pass-1 normalisers sum exp((z - m) / T) of the
+    // two rows
+    double tau_lo, tau_hi;
 };
 
 // ------------------------------------------------------------------------------------
@@ -102,14 +115,19 @@ struct RowStat {
     float m;   // row maximum (NaN if any chunk saw a NaN)
     int idx;   // greedy rows: lowest index reaching m
     double S;  // sampled rows: sum exp((z - m) / T)
+    float zx;  // sampled rows with a draft token: the logit at it
 };
+
+// ln x for finite x > 0 in fp64 (the resolve's few logarithms).
+__device__ __forceinline__ double ln(double x) { return log(x); }
 
 // Row j (0..K target, K+1..2K draft) of sequence b from its pass-1 chunk partials.
 // Greedy: max and lowest index (chunks in order, strict comparison keeps the earlier
 // chunk on ties).  Sampled: max m and S from partials in the 2^((z - m_c) * c2) form.
-__device__ __forceinline__ RowStat merge_row(const VerifyArgs& a, int b, int j, bool sampled, float c2) {
+__device__ __forceinline__ RowStat merge_row(const VerifyArgs& a, int b, int j, bool sampled, float c2,
+                                             const double* tab) {
     const RowPartial* p = a.part1 + ((int64_t)b * a.R + j) * a.nchunk1;
-    RowStat r{-INFINITY, 0x7fffffff, 0.0};
+    RowStat r{-INFINITY, 0x7fffffff, 0.0, -INFINITY};
     if (!sampled) {
         bool bad = false;
 #pragma unroll 4
@@ -124,12 +142,21 @@ __device__ __forceinline__ RowStat merge_row(const VerifyArgs& a, int b, int j, 
         if (bad) r.m = __builtin_nanf("");
         return r;
     }
+    // the chunk holding this row's draft token recorded the logit there
+    const int t = j <= a.K ? j : j - a.K - 1;
+    int cx = -1;
+    if (t < a.K) {
+        const int x = a.tokens[(int64_t)b * a.K + t];
+        if (x >= 0 && x < a.V) cx = x / a.ch1;
+    }
+    r.zx = -INFINITY;
 #pragma unroll 4
     for (int c = 0; c < a.nchunk1; ++c) r.m = nmax(r.m, p[c].m);
 #pragma unroll 4
     for (int c = 0; c < a.nchunk1; ++c) {
         const RowPartial q = p[c];
-        if (q.s != 0.0) r.S += q.s * exp2(((double)q.m - (double)r.m) * (double)c2);
+        if (q.s != 0.0) r.S += q.s * exp2_256(((double)q.m - (double)r.m) * ((double)c2 * 256.0), tab);
+        if (c == cx) r.zx = __int_as_float(q.idx);
     }
     return r;
 }
@@ -138,7 +165,7 @@ __device__ __forceinline__ RowStat merge_row(const VerifyArgs& a, int b, int j, 
 // but the drawn token of a sampled sequence, and its status).  Returns the same SeqDesc
 // in every thread.  Contains __syncthreads().
 template <typename E>
-__device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool write) {
+__device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool write, const double* tab) {
     __shared__ RowStat rows[kRowsLds];
     __shared__ int shi[kWaves];
     __shared__ SeqDesc sd;
@@ -150,18 +177,11 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
     const float* u = sampled ? a.uniforms + (int64_t)b * (K + 1) : nullptr;
     const float c2 = sampled ? (float)(kLog2eD / (double)T) : 0.0f;
 
-    // loads that do not depend on the row statistics first: tokens, logits at x_t, uniforms
+    // tokens and uniforms (the logits at the tokens come with the pass-1 partials)
     int xt = 0;
-    double zx = 0.0, dx = 0.0;
     float ut = 0.5f;
     int err = 0;
-    if (tid < K) {
-        xt = x[tid];
-        if (sampled && xt >= 0 && xt < V) {
-            zx = (double)Logit<E>::at(static_cast<const E*>(a.target) + ((int64_t)b * (K + 1) + tid) * V, xt);
-            dx = (double)Logit<E>::at(static_cast<const E*>(a.draft) + ((int64_t)b * K + tid) * V, xt);
-        }
-    }
+    if (tid < K) xt = x[tid];
     if (sampled && tid <= K) ut = u[tid];
     for (int t = tid; t < K; t += kThreads) {
         const int v = x[t];
@@ -176,12 +196,12 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
     // row statistics (draft rows only for sampled sequences)
     const int nrows = sampled ? R : K + 1;
     for (int j = tid; j < nrows; j += kThreads) {
-        const RowStat r = merge_row(a, b, j, sampled, c2);
+        const RowStat r = merge_row(a, b, j, sampled, c2, tab);
         if (row_bad(r.m, sampled)) err |= kSeqErrLogit;
         if (j < kRowsLds) rows[j] = r;
     }
     err = block_or(err, shi);  // also orders the rows[] writes before the reads below
-    auto row = [&](int j) -> RowStat { return j < kRowsLds ? rows[j] : merge_row(a, b, j, sampled, c2); };
+    auto row = [&](int j) -> RowStat { return j < kRowsLds ? rows[j] : merge_row(a, b, j, sampled, c2, tab); };
 
     int32_t* tok = a.out_tokens + (int64_t)b * (K + 1);
     float* op = a.out_p ? a.out_p + (int64_t)b * K : nullptr;
@@ -204,15 +224,12 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
     }
 
     // the first position that fails
+    const double c256 = sampled ? 256.0 * kLog2eD / (double)T : 0.0;
     int first = K;
     for (int t = tid; t < K; t += kThreads) {
         if (t >= kThreads) {  // K > kThreads: the early loads above covered t < kThreads only
             xt = x[t];
-            if (sampled) {
-                zx = (double)Logit<E>::at(static_cast<const E*>(a.target) + ((int64_t)b * (K + 1) + t) * V, xt);
-                dx = (double)Logit<E>::at(static_cast<const E*>(a.draft) + ((int64_t)b * K + t) * V, xt);
-                ut = u[t];
-            }
+            if (sampled) ut = u[t];
         }
         if (!sampled) {
             if (row(t).idx != xt) first = min(first, t);
@@ -220,16 +237,17 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
             if (write && oq) oq[t] = __builtin_nanf("");
         } else {
             const RowStat rt = row(t), rd = row(K + 1 + t);
-            const double lp = (zx - (double)rt.m) / (double)T - log(rt.S);
-            const double lq = (dx - (double)rd.m) / (double)T - log(rd.S);
-            if (write && op) op[t] = (float)exp(lp);
-            if (write && oq) oq[t] = (float)exp(lq);
-            // r < p/q in log space; q = 0 with p > 0 accepts, p = 0 rejects
+            // p = 2^((zx - mt) c2) / St and q = 2^((dx - md) c2) / Sd
+            const double ex = (double)rt.zx - (double)rt.m, dxm = (double)rd.zx - (double)rd.m;
+            if (write && op) op[t] = (float)(exp2_256(ex * c256, tab) / rt.S);
+            if (write && oq) oq[t] = (float)(exp2_256(dxm * c256, tab) / rd.S);
+            // r < p/q, i.e. r St < Sd 2^((ex - dxm) c2); q = 0 with p > 0 accepts, p = 0
+            // rejects (2^y saturates to inf above and to 0 below the fp64 range)
             bool accept;
-            if (lp == -INFINITY) accept = false;
-            else if (lq == -INFINITY) accept = true;
+            if (rt.zx == -INFINITY) accept = false;
+            else if (rd.zx == -INFINITY) accept = true;
             else if (ut == 0.0f) accept = true;
-            else accept = log((double)ut) < lp - lq;
+            else accept = (double)ut * rt.S < rd.S * exp2_256((ex - dxm) * c256, tab);
             if (!accept) first = min(first, t);
         }
     }
@@ -251,12 +269,15 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
         } else {
             const RowStat rt = row(n);
             d.mt = rt.m;
-            d.St = rt.S;
+            d.md = rt.m;
+            d.tau_lo = d.tau_hi = 0.0;
             if (n < K) {
                 const RowStat rd = row(K + 1 + n);
                 d.md = rd.m;
-                d.Sd = rd.S;
                 d.mode = kModeResidual;
+                const double base = (double)T * ln(rt.S / rd.S) + ((double)rt.m - (double)rd.m);
+                d.tau_hi = base + (double)T * kLnDeltaHi;
+                d.tau_lo = base + (double)T * kLnDeltaLo;
             } else {
                 d.mode = kModeBonus;
             }
@@ -274,12 +295,18 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
 // draw weights
 // ------------------------------------------------------------------------------------
 
-// Table index of the bf16 bit pattern h (in the low 16 bits), clamped into the table, and
-// whether h lies inside it.
-__device__ __forceinline__ uint32_t tab_index(uint32_t h, bool& in) {
-    const uint32_t off = (h & 0x7fffu) - (uint32_t)(kTabE0 * 128);
-    in = off < (uint32_t)kTabHalf;
-    return min(off, (uint32_t)(kTabHalf - 1)) + (h >> 15) * (uint32_t)kTabHalf;
+// Table slot of the bf16 value in the low 16 bits of x (higher bits ignored); values
+// outside the table land on a NaN slot.
+__device__ __forceinline__ uint32_t tab_slot(uint32_t x) {
+    const uint32_t t = min(max(x & 0x7fffu, kTabLo), kTabHi);
+    return (t - kTabLo) + ((x >> 4) & 0x800u);
+}
+
+// Whether the bf16 value in the low 16 bits of h has a table slot, and that slot.
+__device__ __forceinline__ bool tab_has(uint32_t h, uint32_t& slot) {
+    const uint32_t t = h & 0x7fffu;
+    slot = (t - kTabLo) + ((h >> 4) & 0x800u);
+    return t - (kTabLo + 1) < (uint32_t)kTabN;
 }
 
 template <typename E>
@@ -291,34 +318,29 @@ struct DrawRows {
     double inv_sp, inv_sq; // 1 / S_p, 1 / S_q once known
     double tau_lo, tau_hi; // undecided bracket on zt - zd
     float tau_lo_f, tau_hi_f;  // the same, rounded outward to fp32
-    float thr_t, thr_d;    // z below these weighs 0 (2^-70 of the row maximum)
+    float thr_t, thr_d;    // below these, computed weights are flushed (2^-70 of the row max)
     int residual;          // 1: (a/S_p - b/S_q)+ ; 0: a (bonus, or the draw from p_n)
     int vec_ok;            // both rows 16-byte aligned
     int use_tab;           // bf16 with one shared reference: weights from the LDS table
     const double* tab;     // 2^(j/256), LDS
     const double* wt;      // bf16 weight table, LDS
 
-    // exp((z - ref)/T) = 2^((z - ref) * 256 log2(e)/T / 256); z - ref is exact in fp64
+    // exp((z - ref)/T) = 2^((z - ref) * 256 log2(e)/T / 256); z - ref is exact in fp64.
+    // Table values are that same function of the same operands.
     __device__ __forceinline__ double a_of(float z) const {
-        if (!(z >= thr_t)) return 0.0;
         if constexpr (sizeof(E) == 2) {
-            if (use_tab) {
-                bool in;
-                const uint32_t k = tab_index(__float_as_uint(z) >> 16, in);
-                if (in) return wt[k];
-            }
+            uint32_t k;
+            if (use_tab && tab_has(__float_as_uint(z) >> 16, k)) return wt[k];
         }
+        if (!(z >= thr_t)) return 0.0;
         return exp2_256(exp2_arg((double)z, refA, c256), tab);
     }
     __device__ __forceinline__ double b_of(float z) const {
-        if (!(z >= thr_d)) return 0.0;
         if constexpr (sizeof(E) == 2) {
-            if (use_tab) {
-                bool in;
-                const uint32_t k = tab_index(__float_as_uint(z) >> 16, in);
-                if (in) return wt[k];
-            }
+            uint32_t k;
+            if (use_tab && tab_has(__float_as_uint(z) >> 16, k)) return wt[k];
         }
+        if (!(z >= thr_d)) return 0.0;
         return exp2_256(exp2_arg((double)z, refB, c256), tab);
     }
     __device__ __forceinline__ double weight(float zt, float zd) const {
@@ -345,7 +367,7 @@ __device__ __forceinline__ DrawRows<E> draw_rows(const VerifyArgs& a, int b, con
     const double M = fmax(mt, md);
     r.refA = one_ref ? M : mt;
     r.refB = one_ref ? M : md;
-    r.use_tab = sizeof(E) == 2 && one_ref;
+    r.use_tab = sizeof(E) == 2 && one_ref && wt != nullptr;
     r.thr_t = (float)(mt - kFlushLog2 / c2);
     r.thr_d = r.residual ? (float)(md - kFlushLog2 / c2) : INFINITY;
     r.inv_sp = 1.0;
@@ -353,11 +375,10 @@ __device__ __forceinline__ DrawRows<E> draw_rows(const VerifyArgs& a, int b, con
     r.tau_lo = r.tau_hi = 0.0;
     r.tau_lo_f = r.tau_hi_f = 0.0f;
     if (r.residual) {
-        // p_i > q_i  <=>  zt_i - zd_i > T ln(S_p/S_q) + refA - refB, and in the pass-1 terms
-        // (normalisers St, Sd relative to mt, md) that threshold is T ln(St/Sd) + mt - md
-        const double lr = log(d.St) - log(d.Sd);
-        r.tau_hi = T * (lr + log1p(kDelta)) + (mt - md);
-        r.tau_lo = T * (lr + log1p(-kDelta)) + (mt - md);
+        // p_i > q_i  <=>  zt_i - zd_i > T ln(S_p/S_q) + refA - refB, which in the pass-1
+        // terms is T ln(St/Sd) + mt - md: the resolve's bracket around it
+        r.tau_hi = d.tau_hi;
+        r.tau_lo = d.tau_lo;
         r.tau_hi_f = __double2float_ru(r.tau_hi);
         r.tau_lo_f = __double2float_rd(r.tau_lo);
     }
@@ -368,14 +389,21 @@ __device__ __forceinline__ DrawRows<E> draw_rows(const VerifyArgs& a, int b, con
 }
 
 // Fill the bf16 weight table (kTabLen doubles of LDS) for reference r.refA (= r.refB):
-// entries below both flush thresholds are never read and stay 0.  Contains __syncthreads().
+// each entry is the fp64 exponential of its bf16 value, exactly what DrawRows evaluates
+// without the table.  Consecutive threads write consecutive slots (no bank conflicts).
+// Contains __syncthreads().
 template <typename E>
 __device__ __forceinline__ void weight_table_init(const DrawRows<E>& r, double* wt) {
-    const float thr = fminf(r.thr_t, r.thr_d);
     for (int k = threadIdx.x; k < kTabLen; k += kThreads) {
-        const uint32_t h = (k < kTabHalf ? 0u : 0x8000u) | (uint32_t)(kTabE0 * 128 + k % kTabHalf);
-        const float z = __uint_as_float(h << 16);
-        wt[k] = z >= thr ? exp2_256(exp2_arg((double)z, r.refA, r.c256), r.tab) : 0.0;
+        const uint32_t q = (uint32_t)k & (kTabHalf - 1);
+        double v = 0.0;
+        if (q == 0 || q == (uint32_t)kTabN + 1) {
+            v = __builtin_nan("");
+        } else if (q <= (uint32_t)kTabN) {
+            const uint32_t h = ((uint32_t)k / kTabHalf) << 15 | (kTabLo + q);
+            v = exp2_256(exp2_arg((double)__uint_as_float(h << 16), r.refA, r.c256), r.tab);
+        }
+        wt[k] = v;
     }
     __syncthreads();
 }
@@ -399,13 +427,25 @@ __device__ __forceinline__ void load_vec(const E* row, int i, int hi, bool vec_o
 // ------------------------------------------------------------------------------------
 
 struct SweepAcc {
-    double sp = 0.0, sq = 0.0;  // this lane's sums of a_i, b_i
-    double A = 0.0, B = 0.0;    // over the positions with a certainly positive residual
+    double sp, sq;  // this lane's sums of a_i, b_i
+    double A, B;    // over the positions with a certainly positive residual
     // The wave's buckets of undecided positions, one per lane: lane j holds bucket j
     // (its difference value D and sums of a and b).  nbkt is wave-uniform.
-    double bD = 0.0, bA = 0.0, bB = 0.0;
-    int nbkt = 0;
+    double bD, bA, bB;
+    int nbkt;
     int lane;
+    // fast path: the undecided positions whose difference equals `key` (wave-uniform; NaN
+    // until the first one), and their sums of a and b
+    float key;
+    double kA, kB;
+
+    __device__ __forceinline__ void reset() {
+        sp = sq = A = B = 0.0;
+        bD = bA = bB = 0.0;
+        nbkt = 0;
+        key = __builtin_nanf("");
+        kA = kB = 0.0;
+    }
 };
 
 // Adds the undecided positions of this call (flag u, difference D, weights a, b per lane)
@@ -436,9 +476,9 @@ __device__ __forceinline__ void bucket_add(SweepAcc& s, bool u, double D, double
     }
 }
 
-// Accumulates P positions of this lane with weights av, bv, the fp32 difference Df (exact
-// when dx_ok) and the logits (for the exact difference otherwise).  Wave-wide votes: every
-// lane of the wave calls this the same number of times.
+// The exact path for P positions of this lane: weights av, bv (0 where the position is
+// not live), the fp32 difference Df (exact where dx_ok) or else the fp64 one.  Wave-wide
+// votes: every lane of the wave calls this the same number of times.
 template <typename E, int P>
 __device__ __forceinline__ void accumulate(const DrawRows<E>& r, const double (&av)[P], const double (&bv)[P],
                                            const float (&zt)[P], const float (&zd)[P],
@@ -452,7 +492,7 @@ __device__ __forceinline__ void accumulate(const DrawRows<E>& r, const double (&
         unc[k] = !pos[k] && Df >= r.tau_lo_f;
         any_inexact |= !dx_ok[k];
     }
-    if (__any(any_inexact)) {  // rare: a logit outside the table range, classify in fp64
+    if (__any(any_inexact)) {  // a logit outside the table range: classify in fp64
 #pragma unroll
         for (int k = 0; k < P; ++k) {
             if (!dx_ok[k]) {
@@ -472,59 +512,250 @@ __device__ __forceinline__ void accumulate(const DrawRows<E>& r, const double (&
         s.A = __builtin_fma(av[k], sel, s.A);
         s.B = __builtin_fma(bv[k], sel, s.B);
     }
-    if (__any(any_unc)) {  // rare: bucket by the exact logit difference
+    if (__any(any_unc)) {  // bucket by the exact logit difference
 #pragma unroll
         for (int k = 0; k < P; ++k) bucket_add(s, unc[k], (double)zt[k] - (double)zd[k], av[k], bv[k]);
     }
 }
 
-// Two bf16 positions of each row (one 32-bit word each), weights from the LDS table.
+// Exact path for two bf16 positions of each row (one 32-bit word each).
 template <bool Residual>
-__device__ __forceinline__ void sweep_word_tab(const DrawRows<uint16_t>& r, uint32_t wt, uint32_t wd,
+__device__ __forceinline__ void exact_word_tab(const DrawRows<uint16_t>& r, uint32_t wt, uint32_t wd,
                                                SweepAcc& s) {
     const float zt[2] = {__uint_as_float(wt << 16), __uint_as_float(wt & 0xffff0000u)};
     const float zd[2] = {__uint_as_float(wd << 16), __uint_as_float(wd & 0xffff0000u)};
-    bool nt[2], nd[2];
-    bool any = false;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        nt[k] = zt[k] >= r.thr_t;
-        nd[k] = Residual && zd[k] >= r.thr_d;
-        any |= nt[k] || nd[k];
-    }
-    if (!__any(any)) return;  // the whole wave: every weight flushed
     double av[2], bv[2];
-    bool it[2], id[2], live[2];
-    bool slow = false;
+    bool dx_ok[2], live[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-        const uint32_t kt = tab_index(__float_as_uint(zt[k]) >> 16, it[k]);
-        av[k] = nt[k] ? r.wt[kt] : 0.0;
-        id[k] = true;
+        uint32_t q;
+        const bool it = tab_has(__float_as_uint(zt[k]) >> 16, q);
+        av[k] = r.a_of(zt[k]);
+        bool id = true;
         bv[k] = 0.0;
         if (Residual) {
-            const uint32_t kd = tab_index(__float_as_uint(zd[k]) >> 16, id[k]);
-            bv[k] = nd[k] ? r.wt[kd] : 0.0;
+            id = tab_has(__float_as_uint(zd[k]) >> 16, q);
+            bv[k] = r.b_of(zd[k]);
         }
-        live[k] = nt[k] || nd[k];
-        slow |= (nt[k] && !it[k]) || (nd[k] && !id[k]);
-    }
-    if (__any(slow)) {  // rare: a weight outside the table range
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            if (nt[k] && !it[k]) av[k] = r.a_of(zt[k]);
-            if (Residual && nd[k] && !id[k]) bv[k] = r.b_of(zd[k]);
-        }
+        live[k] = av[k] != 0.0 || bv[k] != 0.0;
+        // a difference of two bf16 values with |z| in [2^-10, 32) is exact in fp32;
+        // positions whose weights are both 0 need no sign
+        dx_ok[k] = (it && id) || !live[k];
     }
     if (!Residual) {
         s.sp += av[0];
         s.sp += av[1];
         return;
     }
-    // a difference of two bf16 values with |z| in [2^-10, 32) is exact in fp32; positions
-    // whose weights are both flushed need no sign
-    const bool dx_ok[2] = {(it[0] && id[0]) || !live[0], (it[1] && id[1]) || !live[1]};
     accumulate<uint16_t, 2>(r, av, bv, zt, zd, dx_ok, live, s);
+}
+
+// Fast path for one word of each row: table weights without range checks (a value outside
+// the table reads NaN), signs from the fp32 difference.  Undecided positions (difference
+// inside the bracket) are summed into s.kA, s.kB when their difference equals the wave's
+// key (set by the first one; typically every undecided position has the same difference,
+// mt - md at low temperature); any other undecided position sets `odd`.
+__device__ __forceinline__ void fast_word_res(const double* wt, uint32_t xt, uint32_t xd, float th, float tl,
+                                              SweepAcc& s, bool& odd) {
+    const float zt0 = __uint_as_float(xt << 16), zt1 = __uint_as_float(xt & 0xffff0000u);
+    const float zd0 = __uint_as_float(xd << 16), zd1 = __uint_as_float(xd & 0xffff0000u);
+    const float D0 = zt0 - zd0, D1 = zt1 - zd1;
+    const bool p0 = D0 > th, p1 = D1 > th;
+    const bool u0 = !p0 && D0 >= tl, u1 = !p1 && D1 >= tl;
+    const double a0 = wt[tab_slot(xt)], a1 = wt[tab_slot(xt >> 16)];
+    const double b0 = wt[tab_slot(xd)], b1 = wt[tab_slot(xd >> 16)];
+    if (__any(u0 || u1)) {
+        if (s.key != s.key) {  // the first undecided difference becomes the key
+            const uint64_t m = __ballot(u0 || u1);
+            const int l = __ffsll((unsigned long long)m) - 1;
+            s.key = __shfl(u0 ? D0 : D1, l, 64);
+        }
+        const bool k0 = u0 && D0 == s.key, k1 = u1 && D1 == s.key;
+        odd = odd || (u0 && !k0) || (u1 && !k1);
+        s.kA = __builtin_fma(a0, k0 ? 1.0 : 0.0, s.kA);
+        s.kB = __builtin_fma(b0, k0 ? 1.0 : 0.0, s.kB);
+        s.kA = __builtin_fma(a1, k1 ? 1.0 : 0.0, s.kA);
+        s.kB = __builtin_fma(b1, k1 ? 1.0 : 0.0, s.kB);
+    }
+    s.sp += a0;
+    s.sq += b0;
+    s.sp += a1;
+    s.sq += b1;
+    const double s0 = p0 ? 1.0 : 0.0, s1 = p1 ? 1.0 : 0.0;
+    s.A = __builtin_fma(a0, s0, s.A);
+    s.B = __builtin_fma(b0, s0, s.B);
+    s.A = __builtin_fma(a1, s1, s.A);
+    s.B = __builtin_fma(b1, s1, s.B);
+    // the sums exist here: no pass may sink this word's arithmetic towards the span end,
+    // which would keep its table values in registers
+    asm volatile("" ::"v"(s.sp), "v"(s.sq), "v"(s.A), "v"(s.B), "v"(s.kA), "v"(s.kB));
+}
+
+__device__ __forceinline__ void fast_word_bonus(const double* wt, uint32_t xt, SweepAcc& s) {
+    s.sp += wt[tab_slot(xt)];
+    s.sp += wt[tab_slot(xt >> 16)];
+    asm volatile("" ::"v"(s.sp));
+}
+
+// Writes a segment's partial (lane 0) and buckets (lanes below nbkt), then clears acc.  The
+// fast path's keyed positions become (or join) the bucket of their difference.
+__device__ __forceinline__ void store_partial(const VerifyArgs& a, int64_t e, SweepAcc& acc) {
+    if (!(acc.key != acc.key)) bucket_add(acc, true, (double)acc.key, acc.kA, acc.kB);
+    const double sp = wave_sum(acc.sp);
+    const double sq = wave_sum(acc.sq);
+    const double A = wave_sum(acc.A);
+    const double Bm = wave_sum(acc.B);
+    if (acc.lane < acc.nbkt && acc.lane < kBuckets) {
+        Bucket bk;
+        bk.a = acc.bA;
+        bk.b = acc.bB;
+        a.bkt[e * kBuckets + acc.lane] = bk;
+    }
+    if (acc.lane == 0) {
+        DrawPartial dp;
+        dp.sp = sp;
+        dp.sq = sq;
+        dp.A = A;
+        dp.B = Bm;
+        dp.nbkt = acc.nbkt;
+        dp.pad[0] = dp.pad[1] = dp.pad[2] = 0;
+        a.part2[e] = dp;
+    }
+    acc.reset();
+}
+
+// Positions of segment k: [k * kSeg, min(V, (k + 1) * kSeg)).
+__device__ __forceinline__ void seg_range(int V, int k, int& lo, int& hi) {
+    lo = min(V, k * kSeg);
+    hi = min(V, lo + kSeg);
+}
+
+// One wave over segments [s0, s1) of sequence b's draw row(s), bf16 with the LDS table.
+// Whole spans of 64 lanes x kG vectors per row go through the fast path, the next span's
+// loads issued before the current one is processed; a span whose sums turned NaN or that
+// held an undecided sign is redone by the exact path from a copy of the sums taken before
+// it.  Positions outside whole spans (a partial last segment, or rows not 16-byte
+// aligned) take the exact path one word per lane.
+// The loads of the first whole span, issued before the weight table is built.
+struct FirstSpan {
+    u32x4 t[kG], d[kG];
+};
+
+template <bool Residual>
+__device__ __forceinline__ void first_span(const DrawRows<uint16_t>& r, int lo, int lane, FirstSpan& f) {
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+        const int i = lo + (g * 64 + lane) * 8;
+        f.t[g] = load16(r.t + i);
+        f.d[g] = Residual ? load16(r.d + i) : f.t[g];
+    }
+}
+
+// Whole spans of the wave's range [s0 * kSeg, ...) start at lo; f holds the first one's
+// loads when have_first.
+template <bool Residual>
+__device__ __forceinline__ void sweep_wave_tab(const VerifyArgs& a, const DrawRows<uint16_t>& r, int b,
+                                               int s0, int s1, SweepAcc& acc, const FirstSpan& f,
+                                               bool have_first) {
+    const int lane = acc.lane;
+    const int lo = min(a.V, s0 * kSeg), hi = min(a.V, s1 * kSeg);
+    const int hi_whole = r.vec_ok ? lo + ((hi - lo) / kSpan16) * kSpan16 : lo;
+    const int64_t e0 = (int64_t)b * a.nseg;
+    const float th = r.tau_hi_f, tl = r.tau_lo_f;
+    // segment by segment: a rolling pipeline over the segment's whole spans (group g of the
+    // next span is loaded into rt[g], rd[g] as soon as group g of the current one has been
+    // taken out of them), then the exact redo of the spans that needed it, with no loads
+    // in flight
+    for (int g0 = lo; g0 < hi_whole;) {
+        const int g1 = min(hi_whole, (g0 / kSeg + 1) * kSeg);
+        u32x4 rt[kG], rd[kG];
+        if (have_first && g0 == lo) {
+#pragma unroll
+            for (int g = 0; g < kG; ++g) {
+                rt[g] = f.t[g];
+                rd[g] = f.d[g];
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < kG; ++g) {
+                const int i = g0 + (g * 64 + lane) * 8;
+                rt[g] = load16(r.t + i);
+                rd[g] = Residual ? load16(r.d + i) : rt[g];
+            }
+        }
+        uint32_t redo = 0;  // wave-uniform: spans of this segment to redo exactly
+        for (int i0 = g0, j = 0; i0 < g1; i0 += kSpan16, ++j) {  // wave-uniform trip count
+            const bool more = i0 + kSpan16 < g1;
+            const double keep_sp = acc.sp, keep_sq = acc.sq, keep_A = acc.A, keep_B = acc.B;
+            const double keep_kA = acc.kA, keep_kB = acc.kB;
+            bool odd = false;
+#pragma unroll
+            for (int g = 0; g < kG; ++g) {
+                const u32x4 ct = rt[g], cd = rd[g];
+                if (more) {
+                    const int i = i0 + kSpan16 + (g * 64 + lane) * 8;
+                    rt[g] = load16(r.t + i);
+                    rd[g] = Residual ? load16(r.d + i) : rt[g];
+                }
+                // one word at a time: the scheduler must not hoist every table read of the
+                // span (the registers they would take are better spent on loads in flight)
+                const uint32_t xt4[4] = {ct.x, ct.y, ct.z, ct.w};
+                const uint32_t xd4[4] = {cd.x, cd.y, cd.z, cd.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (Residual) fast_word_res(r.wt, xt4[q], xd4[q], th, tl, acc, odd);
+                    else fast_word_bonus(r.wt, xt4[q], acc);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if (__any(odd || acc.sp != acc.sp || acc.sq != acc.sq)) {  // rare
+                acc.sp = keep_sp;
+                acc.sq = keep_sq;
+                acc.A = keep_A;
+                acc.B = keep_B;
+                acc.kA = keep_kA;
+                acc.kB = keep_kB;
+                redo |= 1u << j;
+            }
+        }
+        while (redo) {  // wave-uniform
+            const int j = __ffs(redo) - 1;
+            redo &= redo - 1;
+#pragma unroll 1
+            for (int g = 0; g < kG; ++g) {
+                const int i = g0 + j * kSpan16 + (g * 64 + lane) * 8;
+                const u32x4 vt = *reinterpret_cast<const u32x4*>(r.t + i);
+                const u32x4 vd = Residual ? *reinterpret_cast<const u32x4*>(r.d + i) : u32x4{0u, 0u, 0u, 0u};
+                exact_word_tab<Residual>(r, vt.x, vd.x, acc);
+                exact_word_tab<Residual>(r, vt.y, vd.y, acc);
+                exact_word_tab<Residual>(r, vt.z, vd.z, acc);
+                exact_word_tab<Residual>(r, vt.w, vd.w, acc);
+            }
+        }
+        // a segment ends here (or the row does, exactly at a span)
+        if ((g1 & (kSeg - 1)) == 0 || g1 == hi) store_partial(a, e0 + (g0 / kSeg), acc);
+        g0 = g1;
+    }
+    // the rest, segment by segment, one word (two positions) per lane; positions at or
+    // past the end read -inf (0xff80), whose weight is 0
+    for (int t0 = hi_whole; t0 < hi;) {
+        const int k = t0 / kSeg;
+        const int te = min(hi, (k + 1) * kSeg);
+#pragma unroll 1
+        for (int j0 = t0; j0 < te; j0 += 128) {
+            const int i = j0 + 2 * lane;
+            const uint32_t x0 = i < te ? (uint32_t)r.t[i] : 0xff80u;
+            const uint32_t x1 = i + 1 < te ? (uint32_t)r.t[i + 1] : 0xff80u;
+            uint32_t y0 = 0xff80u, y1 = 0xff80u;
+            if (Residual) {
+                y0 = i < te ? (uint32_t)r.d[i] : 0xff80u;
+                y1 = i + 1 < te ? (uint32_t)r.d[i + 1] : 0xff80u;
+            }
+            exact_word_tab<Residual>(r, x0 | (x1 << 16), y0 | (y1 << 16), acc);
+        }
+        store_partial(a, e0 + k, acc);
+        t0 = te;
+    }
 }
 
 // P positions of each row, weights by the fp64 exponential (fp32 logits, or rows that do
@@ -559,104 +790,28 @@ __device__ __forceinline__ void sweep_vec_exp(const DrawRows<E>& r, const float 
     accumulate<E, P>(r, av, bv, zt, zd, dx_ok, live, s);
 }
 
-// Writes the wave's partial (lane 0) and buckets (lanes below nbkt).
-__device__ __forceinline__ void store_partial(const VerifyArgs& a, int64_t e, SweepAcc& acc) {
-    const double sp = wave_sum(acc.sp);
-    const double sq = wave_sum(acc.sq);
-    const double A = wave_sum(acc.A);
-    const double Bm = wave_sum(acc.B);
-    if (acc.lane < acc.nbkt && acc.lane < kBuckets) {
-        Bucket bk;
-        bk.a = acc.bA;
-        bk.b = acc.bB;
-        a.bkt[e * kBuckets + acc.lane] = bk;
-    }
-    if (acc.lane == 0) {
-        DrawPartial dp;
-        dp.sp = sp;
-        dp.sq = sq;
-        dp.A = A;
-        dp.B = Bm;
-        dp.nbkt = acc.nbkt;
-        dp.pad[0] = dp.pad[1] = dp.pad[2] = 0;
-        a.part2[e] = dp;
-    }
-}
-
-// Wave w's sub-chunk of chunk c: [lo, hi).
-__device__ __forceinline__ void sub_range(const VerifyArgs& a, int c, int w, int& lo, int& hi) {
-    const int sub = a.ch2 / kWaves;
-    lo = min(a.V, c * a.ch2 + w * sub);
-    hi = min(a.V, lo + sub);
-}
-
-// bf16 rows with the LDS table: whole spans of 64 lanes x kG vectors per row, the next
-// span's loads issued before the current one is processed; the rest (a partial span at
-// the end, or rows not 16-byte aligned) one position per lane.
-template <bool Residual>
-__device__ __forceinline__ void sweep_sub_tab(const DrawRows<uint16_t>& r, int lo, int hi, SweepAcc& acc) {
-    constexpr int VEC = 8;
-    const int lane = acc.lane;
-    const int span = 64 * kG * VEC;
-    const int hi_whole = r.vec_ok ? lo + ((hi - lo) / span) * span : lo;
-    u32x4 rt[kG], rd[kG];
-    auto fetch = [&](int s0) {
-#pragma unroll
-        for (int g = 0; g < kG; ++g) {
-            const int i = s0 + (g * 64 + lane) * VEC;
-            rt[g] = load16(r.t + i);
-            if (Residual) rd[g] = load16(r.d + i);
-        }
-    };
-    if (lo < hi_whole) fetch(lo);
-    for (int s0 = lo; s0 < hi_whole; s0 += span) {  // wave-uniform trip count
-        uint32_t wt[kG][4], wd[kG][4];
-#pragma unroll
-        for (int g = 0; g < kG; ++g) {
-            wt[g][0] = rt[g].x; wt[g][1] = rt[g].y; wt[g][2] = rt[g].z; wt[g][3] = rt[g].w;
-            if (Residual) {
-                wd[g][0] = rd[g].x; wd[g][1] = rd[g].y; wd[g][2] = rd[g].z; wd[g][3] = rd[g].w;
-            } else {
-                wd[g][0] = wd[g][1] = wd[g][2] = wd[g][3] = 0u;
-            }
-        }
-        if (s0 + span < hi_whole) fetch(s0 + span);
-#pragma unroll
-        for (int g = 0; g < kG; ++g)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) sweep_word_tab<Residual>(r, wt[g][q], wd[g][q], acc);
-    }
-#pragma unroll 1
-    for (int i0 = hi_whole; i0 < hi; i0 += 128) {
-        const int i = i0 + 2 * lane;
-        // lanes past the end see -inf (0xff80), which is flushed
-        const uint32_t t0 = i < hi ? (uint32_t)r.t[i] : 0xff80u;
-        const uint32_t t1 = i + 1 < hi ? (uint32_t)r.t[i + 1] : 0xff80u;
-        uint32_t d0 = 0xff80u, d1 = 0xff80u;
-        if (Residual) {
-            d0 = i < hi ? (uint32_t)r.d[i] : 0xff80u;
-            d1 = i + 1 < hi ? (uint32_t)r.d[i + 1] : 0xff80u;
-        }
-        sweep_word_tab<Residual>(r, t0 | (t1 << 16), d0 | (d1 << 16), acc);
-    }
-}
-
-// Any logits with the fp64 exponential.
+// One wave over segments [s0, s1), weights by the fp64 exponential.
 template <typename E>
-__device__ __forceinline__ void sweep_sub_exp(const DrawRows<E>& r, int lo, int hi, SweepAcc& acc) {
+__device__ __forceinline__ void sweep_wave_exp(const VerifyArgs& a, const DrawRows<E>& r, int b, int s0,
+                                               int s1, SweepAcc& acc) {
     constexpr int VEC = Logit<E>::kVec;
     constexpr int P = 4;
+    constexpr int span = 64 * VEC;
+    static_assert(kSeg % span == 0, "draw segments are whole spans");
     const int lane = acc.lane;
-    const int span = 64 * VEC;
+    const int lo = min(a.V, s0 * kSeg), hi = min(a.V, s1 * kSeg);
     const int hi_whole = r.vec_ok ? lo + ((hi - lo) / span) * span : lo;
-    for (int s0 = lo; s0 < hi_whole; s0 += span) {
-        const int i = s0 + lane * VEC;
+    const int64_t e0 = (int64_t)b * a.nseg;
+    for (int i0 = lo; i0 < hi_whole; i0 += span) {
+        const int i = i0 + lane * VEC;
         float zt[VEC], zd[VEC];
         Logit<E>::unpack(load16(r.t + i), zt);
-        if (r.residual) Logit<E>::unpack(load16(r.d + i), zd);
-        else
+        if (r.residual) {
+            Logit<E>::unpack(load16(r.d + i), zd);
+        } else {
 #pragma unroll
             for (int k = 0; k < VEC; ++k) zd[k] = -INFINITY;
+        }
 #pragma unroll
         for (int h = 0; h < VEC; h += P) {
             float tp[P], dp[P];
@@ -667,14 +822,22 @@ __device__ __forceinline__ void sweep_sub_exp(const DrawRows<E>& r, int lo, int 
             }
             sweep_vec_exp<E, P>(r, tp, dp, acc);
         }
+        // a segment ends here (or the row does, exactly at a span)
+        if (((i0 + span) & (kSeg - 1)) == 0 || i0 + span == hi) store_partial(a, e0 + (i0 / kSeg), acc);
     }
+    for (int t0 = hi_whole; t0 < hi;) {
+        const int k = t0 / kSeg;
+        const int te = min(hi, (k + 1) * kSeg);
 #pragma unroll 1
-    for (int i0 = hi_whole; i0 < hi; i0 += 64) {
-        const int i = i0 + lane;
-        const bool in = i < hi;
-        const float t1[1] = {in ? Logit<E>::at(r.t, i) : -INFINITY};
-        const float d1[1] = {(in && r.residual) ? Logit<E>::at(r.d, i) : -INFINITY};
-        sweep_vec_exp<E, 1>(r, t1, d1, acc);
+        for (int j0 = t0; j0 < te; j0 += 64) {
+            const int i = j0 + lane;
+            const bool in = i < te;
+            const float t1[1] = {in ? Logit<E>::at(r.t, i) : -INFINITY};
+            const float d1[1] = {(in && r.residual) ? Logit<E>::at(r.d, i) : -INFINITY};
+            sweep_vec_exp<E, 1>(r, t1, d1, acc);
+        }
+        store_partial(a, e0 + k, acc);
+        t0 = te;
     }
 }
 
@@ -741,15 +904,15 @@ __device__ __forceinline__ int block_search(const DrawRows<E>& r, int lo, int hi
     return block_max(lastpos, shi);
 }
 
-// The draw of sequence b from the partials of all its chunks, by one workgroup.
+// The draw of sequence b from the partials of all its segments, by one workgroup.
 template <typename E>
 __device__ __forceinline__ void final_seq(const VerifyArgs& a, DrawRows<E> r, const SeqDesc& d, int b) {
     __shared__ double shd[kWaves];
     __shared__ int shi[kWaves];
     __shared__ double sh_base;
     const int tid = threadIdx.x;
-    const int nsub = a.nchunk2 * kWaves;
-    const int64_t e0 = (int64_t)b * a.ns2 * kWaves;
+    const int nsub = a.nseg;
+    const int64_t e0 = (int64_t)b * a.nseg;
     const double u = (double)d.u;
     int status = 0;
 
@@ -845,7 +1008,7 @@ __device__ __forceinline__ void final_seq(const VerifyArgs& a, DrawRows<E> r, co
                 base = sh_base;
             }
             int lo, hi;
-            sub_range(a, hit / kWaves, hit % kWaves, lo, hi);
+            seg_range(a.V, hit, lo, hi);
             y = block_search(r, lo, hi, base, tgt, false, u);
         }
     }
@@ -874,8 +1037,9 @@ static_assert(sizeof(SeqDesc) <= kSeqDescBytes && kSeqDescBytes % alignof(SeqDes
               "workspace slot of the descriptor");
 
 // grid = sequences x nchunk2.  Every workgroup resolves its sequence; the chunk-0
-// workgroup writes the outputs and the sequence's SeqDesc.  Sampled sequences: each
-// workgroup sweeps chunk c of the draw row(s) into its per-wave partials.
+// workgroup writes the outputs and the sequence's SeqDesc.  Sampled sequences: workgroup c
+// sweeps segments [c spc, (c + 1) spc) of the draw row(s), each wave a contiguous run of
+// them, into per-segment partials.
 template <typename E>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SV_DRAW_WAVES)))
 void sweep_kernel(VerifyArgs a, int b0) {
@@ -888,36 +1052,42 @@ void sweep_kernel(VerifyArgs a, int b0) {
         const float T = a.temperature ? a.temperature[b] : 0.0f;
         if (T == 0.0f) return;  // whole workgroup
     }
-    const SeqDesc d = resolve_seq<E>(a, b, c == 0);
+    exp2_table_init(tab);
+    const SeqDesc d = resolve_seq<E>(a, b, c == 0, tab);
     if (c == 0 && threadIdx.x == 0) reinterpret_cast<SeqDesc*>(a.desc)[b] = d;
     if (d.mode == kModeNone) return;  // whole workgroup
-    exp2_table_init(tab);
     DrawRows<E> r = draw_rows<E>(a, b, d, tab, wt);
-    if constexpr (sizeof(E) == 2) {
-        if (r.use_tab) weight_table_init(r, wt);
-    }
-
     const int w = threadIdx.x >> 6;
     SweepAcc acc;
     acc.lane = threadIdx.x & 63;
-    int lo, hi;
-    sub_range(a, c, w, lo, hi);
+    acc.reset();
+    const int c0 = c * a.spc, c1 = min(a.nseg, c0 + a.spc);
+    const int per = (c1 - c0 + kWaves - 1) / kWaves;
+    const int s0 = min(c1, c0 + w * per), s1 = min(c1, s0 + per);
     if constexpr (sizeof(E) == 2) {
         if (r.use_tab) {
-            if (r.residual) sweep_sub_tab<true>(r, lo, hi, acc);
-            else sweep_sub_tab<false>(r, lo, hi, acc);
-        } else {
-            sweep_sub_exp<E>(r, lo, hi, acc);
+            // the wave's first loads go out before the table is built
+            const int lo = min(a.V, s0 * kSeg), hi = min(a.V, s1 * kSeg);
+            const bool have_first = r.vec_ok && hi - lo >= kSpan16;
+            FirstSpan f;
+            if (have_first) {
+                if (r.residual) first_span<true>(r, lo, acc.lane, f);
+                else first_span<false>(r, lo, acc.lane, f);
+            }
+            weight_table_init(r, wt);
+            if (s0 >= s1) return;  // no barrier follows
+            if (r.residual) sweep_wave_tab<true>(a, r, b, s0, s1, acc, f, have_first);
+            else sweep_wave_tab<false>(a, r, b, s0, s1, acc, f, have_first);
+            return;
         }
-    } else {
-        sweep_sub_exp<E>(r, lo, hi, acc);
     }
-    store_partial(a, ((int64_t)b * a.ns2 + c) * kWaves + w, acc);
+    if (s0 >= s1) return;
+    sweep_wave_exp<E>(a, r, b, s0, s1, acc);
 }
 
-// grid = sequences: the draw of each sampled sequence from the partials of all its chunks.
+// grid = sequences: the draw of each sampled sequence from the partials of all its segments.
 // Weights come from the fp64 exponential, which gives exactly the sweep's table values
-// (the table holds the same function of the same arguments).
+// (the table holds the same function of the same operands).
 template <typename E>
 __global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a, int b0) {
     __shared__ double tab[kExpTable];
@@ -925,8 +1095,7 @@ __global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a, int b0) {
     const SeqDesc d = reinterpret_cast<const SeqDesc*>(a.desc)[b];
     if (d.mode == kModeNone) return;  // whole workgroup
     exp2_table_init(tab);
-    DrawRows<E> r = draw_rows<E>(a, b, d, tab, nullptr);
-    r.use_tab = 0;
+    const DrawRows<E> r = draw_rows<E>(a, b, d, tab, nullptr);
     final_seq<E>(a, r, d, b);
 }
 
@@ -937,7 +1106,7 @@ void launch_all(const VerifyArgs& a0, int b0, int b1, hipStream_t s) {
     VerifyArgs a = a0;
     if (!a.temperature) {  // greedy only: the resolve is everything, one workgroup each
         a.nchunk2 = 1;
-        a.ch2 = a.V;
+        a.spc = a.nseg;
     }
     const unsigned blocks = (unsigned)((int64_t)(b1 - b0) * a.nchunk2);
     hipLaunchKernelGGL(sweep_kernel<E>, dim3(blocks), dim3(kThreads), 0, s, a, b0);
