@@ -52,12 +52,13 @@ struct alignas(16) Bucket {
 };
 
 constexpr int kSeg = 4096;         // positions per draw segment (one partial each)
+constexpr int kWtabLen = 4096;     // doubles per sequence of the bf16 weight table
 constexpr int kSeqDescBytes = 48;  // workspace slot of the resolve's per-sequence result
 
 struct Layout {
     int nchunk1, ch1;  // pass-1 chunks per row and elements per chunk (multiple of 64)
     int nseg;          // draw segments per sequence: ceil(V / kSeg)
-    size_t off_desc, off_part1, off_part2, off_bkt, total;
+    size_t off_desc, off_part1, off_part2, off_bkt, off_wtab, total;
 };
 
 // Pass-1 chunks of about kChunkBytes1 (long streams per workgroup), more when the batch
@@ -105,7 +106,6 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // rows_per_seq = 2K+1 for spec_verify, K+1 for spec_verify_greedy.
 inline Layout make_layout(int B, int K, int V, int esize, int rows_per_seq) {
     (void)K;
-    (void)esize;
     Layout L;
     chunking1((int64_t)B * rows_per_seq, V, esize, L.nchunk1, L.ch1);
     L.nseg = segments(V);
@@ -118,6 +118,8 @@ inline Layout make_layout(int B, int K, int V, int esize, int rows_per_seq) {
     off = align256(off + sizeof(DrawPartial) * (size_t)B * L.nseg);
     L.off_bkt = off;
     off = align256(off + sizeof(Bucket) * kBuckets * (size_t)B * L.nseg);
+    L.off_wtab = off;
+    if (esize == 2) off = align256(off + sizeof(double) * kWtabLen * (size_t)B);
     L.total = off;
     return L;
 }
@@ -137,6 +139,7 @@ struct VerifyArgs {
     RowPartial* part1;         // [B][R][nchunk1]
     DrawPartial* part2;        // [B][nseg]
     Bucket* bkt;               // [B][nseg][kBuckets]
+    double* wtab;              // bf16: [B][kWtabLen] weight table of each sequence's draw
     int32_t* out_tokens;
     int32_t* out_n;
     float* out_p;

@@ -27,6 +27,7 @@ namespace {
 
 constexpr double kLog2eD = 1.4426950408889634;
 constexpr float kRescaleLog2 = 32.0f;
+constexpr float kSkipLog2 = 50.0f;
 #ifndef SV_P1_LOADS
 #define SV_P1_LOADS 4
 #endif
@@ -56,12 +57,19 @@ __device__ __forceinline__ void sumexp_vec(const float (&z)[N], float c2, SumExp
 #pragma unroll
     for (int k = 1; k < N; ++k) tm = nmax(tm, z[k]);
     a.mx = nmax(a.mx, tm);
-    if (__builtin_fmaf(tm, c2, -a.R) > kRescaleLog2) {
+    const float top = __builtin_fmaf(tm, c2, -a.R);
+    if (top > kRescaleLog2) {
         // rare: move the reference up to this vector's maximum (exact in fp64)
         const float Rn = tm * c2;
         if (a.s != 0.0) a.s *= exp2((double)a.R - (double)Rn);
         a.R = Rn;
     }
+#ifndef SV_P1_NOSKIP
+    // the whole wave's terms are below 2^-kSkipLog2 of its references (each reference is at
+    // most the row maximum times c2): over any row they add less than V 2^-kSkipLog2
+    // relative to the sum, far below the fp32 rounding of the terms themselves
+    if (__all(top < -kSkipLog2)) return;
+#endif
     float e[N];
 #pragma unroll
     for (int k = 0; k < N; ++k) e[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[k], c2, -a.R));

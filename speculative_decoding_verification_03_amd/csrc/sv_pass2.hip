@@ -1,9 +1,8 @@
 // Pass 2 of the verify step: the resolve and the one categorical draw of each sequence,
-// in two kernels: sweep_kernel over (sequence, chunk) workgroups, then final_kernel with
-// one workgroup per sequence.
+// in three kernels: resolve_kernel (one workgroup per sequence), sweep_kernel over
+// (sequence, chunk) workgroups, then final_kernel (one workgroup per sequence).
 //
-// Resolve (every workgroup of the sequence, redundantly; the chunk-0 workgroup writes the
-// outputs): validation, then the left-to-right test r_t < p_t(x_t)/q_t(x_t) of "A Regra
+// Resolve: validation, then the left-to-right test r_t < p_t(x_t)/q_t(x_t) of "A Regra
 // de Exatidão" (lesson page "Decodificação Especulativa e EAGLE"), evaluated in fp64 log
 // space from the pass-1 row statistics, or for T = 0 the greedy comparison
 // argmax(p_t) == x_t ("Caso ganancioso").  n = the first failing position (K if none).
@@ -321,6 +320,7 @@ struct DrawRows {
     float thr_t, thr_d;    // below these, computed weights are flushed (2^-70 of the row max)
     int residual;          // 1: (a/S_p - b/S_q)+ ; 0: a (bonus, or the draw from p_n)
     int vec_ok;            // both rows 16-byte aligned
+    int one_ref;           // both rows share the reference (bf16: the table applies)
     int use_tab;           // bf16 with one shared reference: weights from the LDS table
     const double* tab;     // 2^(j/256), LDS
     const double* wt;      // bf16 weight table, LDS
@@ -367,6 +367,7 @@ __device__ __forceinline__ DrawRows<E> draw_rows(const VerifyArgs& a, int b, con
     const double M = fmax(mt, md);
     r.refA = one_ref ? M : mt;
     r.refB = one_ref ? M : md;
+    r.one_ref = one_ref;
     r.use_tab = sizeof(E) == 2 && one_ref && wt != nullptr;
     r.thr_t = (float)(mt - kFlushLog2 / c2);
     r.thr_d = r.residual ? (float)(md - kFlushLog2 / c2) : INFINITY;
@@ -388,12 +389,13 @@ __device__ __forceinline__ DrawRows<E> draw_rows(const VerifyArgs& a, int b, con
     return r;
 }
 
-// Fill the bf16 weight table (kTabLen doubles of LDS) for reference r.refA (= r.refB):
-// each entry is the fp64 exponential of its bf16 value, exactly what DrawRows evaluates
-// without the table.  Consecutive threads write consecutive slots (no bank conflicts).
-// Contains __syncthreads().
+static_assert(kTabLen == kWtabLen, "workspace slot of the weight table");
+
+// The bf16 weight table of a sequence (kTabLen doubles) for reference r.refA (= r.refB),
+// written to `dst`: each entry is the fp64 exponential of its bf16 value, exactly what
+// DrawRows evaluates without the table.
 template <typename E>
-__device__ __forceinline__ void weight_table_init(const DrawRows<E>& r, double* wt) {
+__device__ __forceinline__ void weight_table_write(const DrawRows<E>& r, double* dst) {
     for (int k = threadIdx.x; k < kTabLen; k += kThreads) {
         const uint32_t q = (uint32_t)k & (kTabHalf - 1);
         double v = 0.0;
@@ -403,9 +405,17 @@ __device__ __forceinline__ void weight_table_init(const DrawRows<E>& r, double* 
             const uint32_t h = ((uint32_t)k / kTabHalf) << 15 | (kTabLo + q);
             v = exp2_256(exp2_arg((double)__uint_as_float(h << 16), r.refA, r.c256), r.tab);
         }
-        wt[k] = v;
+        dst[k] = v;
     }
-    __syncthreads();
+}
+
+// Copy a sequence's weight table from the workspace into LDS (16-byte pieces; the caller's
+// next __syncthreads() publishes it).
+__device__ __forceinline__ void weight_table_load(const double* src, double* wt) {
+    const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+    u32x4* d4 = reinterpret_cast<u32x4*>(wt);
+#pragma unroll
+    for (int k = threadIdx.x; k < kTabLen / 2; k += kThreads) d4[k] = s4[k];
 }
 
 // Logits at positions i .. i+VEC-1: one 16-byte vector when aligned and inside [.., hi),
@@ -1036,10 +1046,26 @@ struct DrawLds {
 static_assert(sizeof(SeqDesc) <= kSeqDescBytes && kSeqDescBytes % alignof(SeqDesc) == 0,
               "workspace slot of the descriptor");
 
-// grid = sequences x nchunk2.  Every workgroup resolves its sequence; the chunk-0
-// workgroup writes the outputs and the sequence's SeqDesc.  Sampled sequences: workgroup c
-// sweeps segments [c spc, (c + 1) spc) of the draw row(s), each wave a contiguous run of
-// them, into per-segment partials.
+// grid = sequences: the resolve.  Writes the outputs (all but a sampled sequence's drawn
+// token and status), the sequence's SeqDesc and, for bf16 draws with one reference, the
+// sequence's weight table.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void resolve_kernel(VerifyArgs a, int b0) {
+    __shared__ double tab[kExpTable];
+    const int b = b0 + (int)blockIdx.x;
+    exp2_table_init(tab);
+    const SeqDesc d = resolve_seq<E>(a, b, true, tab);
+    if (threadIdx.x == 0) reinterpret_cast<SeqDesc*>(a.desc)[b] = d;
+    if constexpr (sizeof(E) == 2) {
+        if (d.mode == kModeNone) return;
+        const DrawRows<E> r = draw_rows<E>(a, b, d, tab, nullptr);
+        if (r.one_ref) weight_table_write(r, a.wtab + (int64_t)b * kWtabLen);
+    }
+}
+
+// grid = sequences x nchunk2.  Sampled sequences: workgroup c sweeps segments
+// [c spc, (c + 1) spc) of the draw row(s), each wave a contiguous run of them, into
+// per-segment partials.
 template <typename E>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SV_DRAW_WAVES)))
 void sweep_kernel(VerifyArgs a, int b0) {
@@ -1047,14 +1073,7 @@ void sweep_kernel(VerifyArgs a, int b0) {
     __shared__ double wt[DrawLds<E>::kWt];
     const int b = b0 + (int)(blockIdx.x / (unsigned)a.nchunk2);
     const int c = (int)(blockIdx.x % (unsigned)a.nchunk2);
-    if (c != 0) {
-        // only sampled sequences need more than the chunk-0 workgroup
-        const float T = a.temperature ? a.temperature[b] : 0.0f;
-        if (T == 0.0f) return;  // whole workgroup
-    }
-    exp2_table_init(tab);
-    const SeqDesc d = resolve_seq<E>(a, b, c == 0, tab);
-    if (c == 0 && threadIdx.x == 0) reinterpret_cast<SeqDesc*>(a.desc)[b] = d;
+    const SeqDesc d = reinterpret_cast<const SeqDesc*>(a.desc)[b];
     if (d.mode == kModeNone) return;  // whole workgroup
     DrawRows<E> r = draw_rows<E>(a, b, d, tab, wt);
     const int w = threadIdx.x >> 6;
@@ -1064,9 +1083,10 @@ void sweep_kernel(VerifyArgs a, int b0) {
     const int c0 = c * a.spc, c1 = min(a.nseg, c0 + a.spc);
     const int per = (c1 - c0 + kWaves - 1) / kWaves;
     const int s0 = min(c1, c0 + w * per), s1 = min(c1, s0 + per);
+    bool done = false;
     if constexpr (sizeof(E) == 2) {
         if (r.use_tab) {
-            // the wave's first loads go out before the table is built
+            // the wave's first loads go out before the tables reach LDS
             const int lo = min(a.V, s0 * kSeg), hi = min(a.V, s1 * kSeg);
             const bool have_first = r.vec_ok && hi - lo >= kSpan16;
             FirstSpan f;
@@ -1074,15 +1094,19 @@ void sweep_kernel(VerifyArgs a, int b0) {
                 if (r.residual) first_span<true>(r, lo, acc.lane, f);
                 else first_span<false>(r, lo, acc.lane, f);
             }
-            weight_table_init(r, wt);
-            if (s0 >= s1) return;  // no barrier follows
-            if (r.residual) sweep_wave_tab<true>(a, r, b, s0, s1, acc, f, have_first);
-            else sweep_wave_tab<false>(a, r, b, s0, s1, acc, f, have_first);
-            return;
+            weight_table_load(a.wtab + (int64_t)b * kWtabLen, wt);
+            exp2_table_init(tab);  // its barrier also publishes wt
+            if (s0 < s1) {
+                if (r.residual) sweep_wave_tab<true>(a, r, b, s0, s1, acc, f, have_first);
+                else sweep_wave_tab<false>(a, r, b, s0, s1, acc, f, have_first);
+            }
+            done = true;
         }
     }
-    if (s0 >= s1) return;
-    sweep_wave_exp<E>(a, r, b, s0, s1, acc);
+    if (!done) {
+        exp2_table_init(tab);
+        if (s0 < s1) sweep_wave_exp<E>(a, r, b, s0, s1, acc);
+    }
 }
 
 // grid = sequences: the draw of each sampled sequence from the partials of all its segments.
@@ -1102,16 +1126,12 @@ __global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a, int b0) {
 }  // namespace
 
 template <typename E>
-void launch_all(const VerifyArgs& a0, int b0, int b1, hipStream_t s) {
-    VerifyArgs a = a0;
-    if (!a.temperature) {  // greedy only: the resolve is everything, one workgroup each
-        a.nchunk2 = 1;
-        a.spc = a.nseg;
-    }
+void launch_all(const VerifyArgs& a, int b0, int b1, hipStream_t s) {
+    hipLaunchKernelGGL(resolve_kernel<E>, dim3((unsigned)(b1 - b0)), dim3(kThreads), 0, s, a, b0);
+    if (!a.temperature) return;  // greedy only: the resolve is everything
     const unsigned blocks = (unsigned)((int64_t)(b1 - b0) * a.nchunk2);
     hipLaunchKernelGGL(sweep_kernel<E>, dim3(blocks), dim3(kThreads), 0, s, a, b0);
-    if (a.temperature)
-        hipLaunchKernelGGL(final_kernel<E>, dim3((unsigned)(b1 - b0)), dim3(kThreads), 0, s, a, b0);
+    hipLaunchKernelGGL(final_kernel<E>, dim3((unsigned)(b1 - b0)), dim3(kThreads), 0, s, a, b0);
 }
 
 int launch_draw(const VerifyArgs& a, int bf16, int b0, int b1, void* stream) {
