@@ -914,6 +914,159 @@ __device__ __forceinline__ int block_search(const DrawRows<E>& r, int lo, int hi
     return block_max(lastpos, shi);
 }
 
+// Smallest i in [lo, hi) (hi - lo <= kSeg, lo a multiple of kSeg) with
+// base + (w_lo + ... + w_i) > target, in one tile: each thread takes kSeg / kThreads
+// consecutive positions (a thread-local prefix, then a workgroup exclusive scan of the
+// thread totals).  If no index qualifies (rounding), the last index with positive weight;
+// -1 if none.
+template <typename E>
+__device__ __forceinline__ int segment_search(const DrawRows<E>& r, int lo, int hi, double base, double target) {
+    constexpr int VEC = Logit<E>::kVec;
+    constexpr int PER = kSeg / kThreads;  // positions per thread
+    static_assert(PER % VEC == 0, "whole vectors per thread");
+    __shared__ double shd[kWaves];
+    __shared__ int shi[kWaves];
+    const int i0 = lo + PER * (int)threadIdx.x;
+    double w[PER];
+    double run = 0.0;
+    int lastpos = -1;
+#pragma unroll
+    for (int v = 0; v < PER; v += VEC) {
+        float zt[VEC], zd[VEC];
+        load_vec(r.t, i0 + v, hi, r.vec_ok, zt);
+        if (r.residual) load_vec(r.d, i0 + v, hi, r.vec_ok, zd);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            w[v + k] = r.weight(zt[k], r.residual ? zd[k] : 0.0f);
+            run += w[v + k];
+            if (w[v + k] > 0.0) lastpos = i0 + v + k;
+        }
+    }
+    double tot;
+    double acc = base + block_exclusive_scan(run, tot, shd);
+    int found = 0x7fffffff;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        acc += w[k];
+        if (found == 0x7fffffff && w[k] > 0.0 && acc > target) found = i0 + k;
+    }
+    const int f = block_min(found, shi);
+    if (f != 0x7fffffff) return f;
+    return block_max(lastpos, shi);
+}
+
+// Sums of two doubles and an OR over the workgroup, with one round of barriers.
+__device__ __forceinline__ void block_sum2_or(double& x, double& y, int& o, double* sh, int* shi) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    x = wave_sum(x);
+    y = wave_sum(y);
+    o = wave_or(o);
+    if (lane == 0) {
+        sh[w] = x;
+        sh[kWaves + w] = y;
+        shi[w] = o;
+    }
+    __syncthreads();
+    x = sh[0];
+    y = sh[kWaves];
+    o = shi[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) {
+        x += sh[k];
+        y += sh[kWaves + k];
+        o |= shi[k];
+    }
+    __syncthreads();
+}
+
+// The draw when the sequence has at most kThreads segments: thread k holds segment k's
+// partial, loaded once; one reduction, one scan, one segment search.
+template <typename E>
+__device__ __forceinline__ void final_seq_small(const VerifyArgs& a, DrawRows<E> r, const SeqDesc& d, int b) {
+    __shared__ double shd[2 * kWaves];
+    __shared__ int shi[kWaves];
+    __shared__ double sh_base;
+    const int tid = threadIdx.x;
+    const int nsub = a.nseg;
+    const int64_t e0 = (int64_t)b * a.nseg;
+    const double u = (double)d.u;
+    int status = 0;
+
+    DrawPartial dp{};
+    if (tid < nsub) dp = a.part2[e0 + tid];
+    double sp = dp.sp, sq = dp.sq;
+    int over = dp.nbkt > kBuckets;
+    block_sum2_or(sp, sq, over, shd, shi);
+    // the classification by the pass-1 estimate stands if the exact threshold
+    // T ln(S_p/S_q) + refA - refB lies well inside the bracket
+    bool exact_ok = sp > 0.0;
+    if (r.residual) {
+        exact_ok = exact_ok && sq > 0.0 && !over;
+        if (exact_ok) {
+            const double T = (double)d.T;
+            const double tau = T * (log(sp) - log(sq)) + (r.refA - r.refB);
+            const double mid = 0.5 * (r.tau_lo + r.tau_hi);
+            const double half = 0.5 * (r.tau_hi - r.tau_lo);
+            exact_ok = fabs(tau - mid) <= 0.5 * half && half > 1e-12 * (fabs(mid) + 1.0);
+        }
+    }
+    r.inv_sp = 1.0 / sp;
+    r.inv_sq = r.residual ? 1.0 / sq : 1.0;
+
+    int y = -1;
+    if (!exact_ok) {
+        // too many undecided positions, or the estimate was off: one exact sweep
+        y = block_search(r, 0, a.V, 0.0, 0.0, true, u);
+    } else {
+        // this segment's mass in the units of the draw: its certain part and, per bucket
+        // of undecided positions (one residual sign each), the bucket's residual if positive
+        double v = 0.0;
+        if (tid < nsub) {
+            if (!r.residual) {
+                v = dp.sp;
+            } else {
+                v = dp.A * r.inv_sp - dp.B * r.inv_sq;
+                const Bucket* bk = a.bkt + (e0 + tid) * kBuckets;
+                for (int q = 0; q < dp.nbkt; ++q) {
+                    const double t = bk[q].a * r.inv_sp - bk[q].b * r.inv_sq;
+                    if (t > 0.0) v += t;
+                }
+                v = v > 0.0 ? v : 0.0;
+            }
+        }
+        double total;
+        const double ex = block_exclusive_scan(v, total, shd);
+        if (total > 0.0) {
+            const double target = u * total;
+            // a segment without mass never holds the first crossing (guards rounding)
+            int hit = block_min((tid < nsub && v > 0.0 && ex + v > target) ? tid : 0x7fffffff, shi);
+            double tgt = target;
+            if (hit == 0x7fffffff) {
+                // rounding put u*W past every prefix: the last segment with mass, last index
+                hit = block_max((tid < nsub && v > 0.0) ? tid : -1, shi);
+                tgt = INFINITY;
+                status |= kSeqNoteFallback;
+            }
+            if (tid == hit) sh_base = ex;
+            __syncthreads();
+            const double base = sh_base;
+            int lo, hi;
+            seg_range(a.V, hit, lo, hi);
+            y = segment_search(r, lo, hi, base, tgt);
+        }
+    }
+    if (y < 0) {
+        // residual without fp64 mass (exact arithmetic rules it out): draw from p_n
+        status |= kSeqNoteFallback;
+        r.residual = 0;
+        y = block_search(r, 0, a.V, 0.0, 0.0, true, u);
+    }
+    if (tid == 0) {
+        a.out_tokens[(int64_t)b * (a.K + 1) + d.n] = y;
+        a.out_status[b] = status;
+    }
+}
+
 // The draw of sequence b from the partials of all its segments, by one workgroup.
 template <typename E>
 __device__ __forceinline__ void final_seq(const VerifyArgs& a, DrawRows<E> r, const SeqDesc& d, int b) {
@@ -1120,7 +1273,8 @@ __global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a, int b0) {
     if (d.mode == kModeNone) return;  // whole workgroup
     exp2_table_init(tab);
     const DrawRows<E> r = draw_rows<E>(a, b, d, tab, nullptr);
-    final_seq<E>(a, r, d, b);
+    if (a.nseg <= kThreads) final_seq_small<E>(a, r, d, b);
+    else final_seq<E>(a, r, d, b);
 }
 
 }  // namespace
