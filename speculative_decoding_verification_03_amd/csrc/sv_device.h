@@ -184,10 +184,11 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 }
 
 // ---------------------------------------------------------------------------------
-// workgroup reductions over kThreads threads; every thread gets the result.
-// `sh` must hold kWaves entries of the value type.  Contains __syncthreads().
+// workgroup reductions over NW waves (NW * 64 threads); every thread gets the result.
+// `sh` must hold NW entries of the value type.  Contains __syncthreads().
 // ---------------------------------------------------------------------------------
 
+template <int NW = kWaves>
 __device__ __forceinline__ double block_sum(double v, double* sh) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     v = wave_sum(v);
@@ -195,11 +196,12 @@ __device__ __forceinline__ double block_sum(double v, double* sh) {
     __syncthreads();
     double t = sh[0];
 #pragma unroll
-    for (int k = 1; k < kWaves; ++k) t += sh[k];
+    for (int k = 1; k < NW; ++k) t += sh[k];
     __syncthreads();
     return t;
 }
 
+template <int NW = kWaves>
 __device__ __forceinline__ float block_nmax(float v, float* sh) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     v = wave_nmax(v);
@@ -207,11 +209,12 @@ __device__ __forceinline__ float block_nmax(float v, float* sh) {
     __syncthreads();
     float t = sh[0];
 #pragma unroll
-    for (int k = 1; k < kWaves; ++k) t = nmax(t, sh[k]);
+    for (int k = 1; k < NW; ++k) t = nmax(t, sh[k]);
     __syncthreads();
     return t;
 }
 
+template <int NW = kWaves>
 __device__ __forceinline__ int block_min(int v, int* sh) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     v = wave_min(v);
@@ -219,11 +222,12 @@ __device__ __forceinline__ int block_min(int v, int* sh) {
     __syncthreads();
     int t = sh[0];
 #pragma unroll
-    for (int k = 1; k < kWaves; ++k) t = min(t, sh[k]);
+    for (int k = 1; k < NW; ++k) t = min(t, sh[k]);
     __syncthreads();
     return t;
 }
 
+template <int NW = kWaves>
 __device__ __forceinline__ int block_max(int v, int* sh) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     v = wave_max(v);
@@ -231,11 +235,12 @@ __device__ __forceinline__ int block_max(int v, int* sh) {
     __syncthreads();
     int t = sh[0];
 #pragma unroll
-    for (int k = 1; k < kWaves; ++k) t = max(t, sh[k]);
+    for (int k = 1; k < NW; ++k) t = max(t, sh[k]);
     __syncthreads();
     return t;
 }
 
+template <int NW = kWaves>
 __device__ __forceinline__ int block_or(int v, int* sh) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     v = wave_or(v);
@@ -243,11 +248,12 @@ __device__ __forceinline__ int block_or(int v, int* sh) {
     __syncthreads();
     int t = sh[0];
 #pragma unroll
-    for (int k = 1; k < kWaves; ++k) t |= sh[k];
+    for (int k = 1; k < NW; ++k) t |= sh[k];
     __syncthreads();
     return t;
 }
 
+template <int NW = kWaves>
 __device__ __forceinline__ void block_argmax(float& v, int& i, float* shv, int* shi) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     wave_argmax(v, i);
@@ -259,13 +265,14 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, float* shv, int* 
     v = shv[0];
     i = shi[0];
 #pragma unroll
-    for (int k = 1; k < kWaves; ++k) argmax_merge(v, i, shv[k], shi[k]);
+    for (int k = 1; k < NW; ++k) argmax_merge(v, i, shv[k], shi[k]);
     __syncthreads();
 }
 
 // Exclusive prefix sum of one fp64 value per thread, in thread order; also returns
 // the workgroup total.  Fixed combination order (Hillis-Steele inside each wave, then
 // wave totals left to right), so results are reproducible.
+template <int NW = kWaves>
 __device__ __forceinline__ double block_exclusive_scan(double v, double& total, double* sh) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     double incl = v;
@@ -278,7 +285,7 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double& total, 
     __syncthreads();
     double before = 0.0, tot = 0.0;
 #pragma unroll
-    for (int k = 0; k < kWaves; ++k) {
+    for (int k = 0; k < NW; ++k) {
         if (k < w) before += sh[k];
         tot += sh[k];
     }

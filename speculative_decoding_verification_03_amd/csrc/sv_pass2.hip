@@ -85,6 +85,7 @@ constexpr int kG = SV_SWEEP_G;
 constexpr int kSpan16 = 64 * kG * 8;
 static_assert(kSeg % kSpan16 == 0 && kSeg / kSpan16 <= 32, "draw segments are whole spans of bf16 vectors");
 
+
 // The resolve's result for one sequence.
 struct SeqDesc {
     int mode;      // kMode*
@@ -160,13 +161,14 @@ __device__ __forceinline__ RowStat merge_row(const VerifyArgs& a, int b, int j, 
     return r;
 }
 
-// The resolve of sequence b by the whole workgroup.  write: also write the outputs (all
-// but the drawn token of a sampled sequence, and its status).  Returns the same SeqDesc
-// in every thread.  Contains __syncthreads().
-template <typename E>
+// The resolve of sequence b by the whole workgroup of NT threads.  write: also write the
+// outputs (all but the drawn token of a sampled sequence, and its status).  Returns the
+// same SeqDesc in every thread.  Contains __syncthreads().
+template <typename E, int NT = kThreads>
 __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool write, const double* tab) {
+    constexpr int NW = NT / 64;
     __shared__ RowStat rows[kRowsLds];
-    __shared__ int shi[kWaves];
+    __shared__ int shi[NW];
     __shared__ SeqDesc sd;
     const int tid = threadIdx.x;
     const int K = a.K, V = a.V, R = a.R;
@@ -182,24 +184,24 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
     int err = 0;
     if (tid < K) xt = x[tid];
     if (sampled && tid <= K) ut = u[tid];
-    for (int t = tid; t < K; t += kThreads) {
+    for (int t = tid; t < K; t += NT) {
         const int v = x[t];
         if (v < 0 || v >= V) err |= kSeqErrToken;
     }
     if (sampled)
-        for (int t = tid; t <= K; t += kThreads) {
+        for (int t = tid; t <= K; t += NT) {
             const float v = u[t];
             if (!(v >= 0.0f && v < 1.0f)) err |= kSeqErrUniform;
         }
     if (tid == 0 && temperature_bad(T)) err |= kSeqErrTemperature;
     // row statistics (draft rows only for sampled sequences)
     const int nrows = sampled ? R : K + 1;
-    for (int j = tid; j < nrows; j += kThreads) {
+    for (int j = tid; j < nrows; j += NT) {
         const RowStat r = merge_row(a, b, j, sampled, c2, tab);
         if (row_bad(r.m, sampled)) err |= kSeqErrLogit;
         if (j < kRowsLds) rows[j] = r;
     }
-    err = block_or(err, shi);  // also orders the rows[] writes before the reads below
+    err = block_or<NW>(err, shi);  // also orders the rows[] writes before the reads below
     auto row = [&](int j) -> RowStat { return j < kRowsLds ? rows[j] : merge_row(a, b, j, sampled, c2, tab); };
 
     int32_t* tok = a.out_tokens + (int64_t)b * (K + 1);
@@ -207,8 +209,8 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
     float* oq = a.out_q ? a.out_q + (int64_t)b * K : nullptr;
     if (err) {
         if (write) {
-            for (int t = tid; t <= K; t += kThreads) tok[t] = -1;
-            for (int t = tid; t < K; t += kThreads) {
+            for (int t = tid; t <= K; t += NT) tok[t] = -1;
+            for (int t = tid; t < K; t += NT) {
                 if (op) op[t] = __builtin_nanf("");
                 if (oq) oq[t] = __builtin_nanf("");
             }
@@ -225,8 +227,8 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
     // the first position that fails
     const double c256 = sampled ? 256.0 * kLog2eD / (double)T : 0.0;
     int first = K;
-    for (int t = tid; t < K; t += kThreads) {
-        if (t >= kThreads) {  // K > kThreads: the early loads above covered t < kThreads only
+    for (int t = tid; t < K; t += NT) {
+        if (t >= NT) {  // K > NT: the early loads above covered t < NT only
             xt = x[t];
             if (sampled) ut = u[t];
         }
@@ -250,9 +252,9 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
             if (!accept) first = min(first, t);
         }
     }
-    const int n = block_min(first, shi);
+    const int n = block_min<NW>(first, shi);
     if (write)
-        for (int t = tid; t <= K; t += kThreads)
+        for (int t = tid; t <= K; t += NT)
             if (t != n) tok[t] = t < n ? x[t] : -1;
     if (tid == 0) {
         SeqDesc d{};
@@ -394,9 +396,9 @@ static_assert(kTabLen == kWtabLen, "workspace slot of the weight table");
 // The bf16 weight table of a sequence (kTabLen doubles) for reference r.refA (= r.refB),
 // written to `dst`: each entry is the fp64 exponential of its bf16 value, exactly what
 // DrawRows evaluates without the table.
-template <typename E>
+template <typename E, int NT = kThreads>
 __device__ __forceinline__ void weight_table_write(const DrawRows<E>& r, double* dst) {
-    for (int k = threadIdx.x; k < kTabLen; k += kThreads) {
+    for (int k = threadIdx.x; k < kTabLen; k += NT) {
         const uint32_t q = (uint32_t)k & (kTabHalf - 1);
         double v = 0.0;
         if (q == 0 || q == (uint32_t)kTabN + 1) {
@@ -609,7 +611,7 @@ __device__ __forceinline__ void fast_word_bonus(const double* wt, uint32_t xt, S
 
 // Writes a segment's partial (lane 0) and buckets (lanes below nbkt), then clears acc.  The
 // fast path's keyed positions become (or join) the bucket of their difference.
-__device__ __forceinline__ void store_partial(const VerifyArgs& a, int64_t e, SweepAcc& acc) {
+__device__ __forceinline__ void store_partial(DrawPartial* part, Bucket* bkt, int e, SweepAcc& acc) {
     if (!(acc.key != acc.key)) bucket_add(acc, true, (double)acc.key, acc.kA, acc.kB);
     const double sp = wave_sum(acc.sp);
     const double sq = wave_sum(acc.sq);
@@ -619,7 +621,7 @@ __device__ __forceinline__ void store_partial(const VerifyArgs& a, int64_t e, Sw
         Bucket bk;
         bk.a = acc.bA;
         bk.b = acc.bB;
-        a.bkt[e * kBuckets + acc.lane] = bk;
+        bkt[e * kBuckets + acc.lane] = bk;
     }
     if (acc.lane == 0) {
         DrawPartial dp;
@@ -629,23 +631,17 @@ __device__ __forceinline__ void store_partial(const VerifyArgs& a, int64_t e, Sw
         dp.B = Bm;
         dp.nbkt = acc.nbkt;
         dp.pad[0] = dp.pad[1] = dp.pad[2] = 0;
-        a.part2[e] = dp;
+        part[e] = dp;
     }
     acc.reset();
 }
 
-// Positions of segment k: [k * kSeg, min(V, (k + 1) * kSeg)).
-__device__ __forceinline__ void seg_range(int V, int k, int& lo, int& hi) {
-    lo = min(V, k * kSeg);
-    hi = min(V, lo + kSeg);
+// Positions of segment k of length L: [k * L, min(V, (k + 1) * L)).
+__device__ __forceinline__ void seg_range(int V, int L, int k, int& lo, int& hi) {
+    lo = min(V, k * L);
+    hi = min(V, lo + L);
 }
 
-// One wave over segments [s0, s1) of sequence b's draw row(s), bf16 with the LDS table.
-// Whole spans of 64 lanes x kG vectors per row go through the fast path, the next span's
-// loads issued before the current one is processed; a span whose sums turned NaN or that
-// held an undecided sign is redone by the exact path from a copy of the sums taken before
-// it.  Positions outside whole spans (a partial last segment, or rows not 16-byte
-// aligned) take the exact path one word per lane.
 // The loads of the first whole span, issued before the weight table is built.
 struct FirstSpan {
     u32x4 t[kG], d[kG];
@@ -661,23 +657,27 @@ __device__ __forceinline__ void first_span(const DrawRows<uint16_t>& r, int lo, 
     }
 }
 
-// Whole spans of the wave's range [s0 * kSeg, ...) start at lo; f holds the first one's
-// loads when have_first.
+// One wave over positions [lo, hi) of the draw row(s), bf16 with the LDS table, in
+// segments of L positions (L a multiple of a span; lo a multiple of L): the partial of
+// segment k goes to part[k], bkt[k * kBuckets ...].  Whole spans of 64 lanes x kG vectors
+// per row go through the fast path, the next span's loads issued before the current one
+// is processed; a span whose sums turned NaN or that held an undecided sign is redone by
+// the exact path from a copy of the sums taken before it.  Positions outside whole spans
+// (a partial last segment, or rows not 16-byte aligned) take the exact path one word per
+// lane.  f holds the first whole span's loads when have_first.
 template <bool Residual>
-__device__ __forceinline__ void sweep_wave_tab(const VerifyArgs& a, const DrawRows<uint16_t>& r, int b,
-                                               int s0, int s1, SweepAcc& acc, const FirstSpan& f,
-                                               bool have_first) {
+__device__ __forceinline__ void sweep_wave_tab(const DrawRows<uint16_t>& r, int lo, int hi, int L,
+                                               DrawPartial* part, Bucket* bkt, SweepAcc& acc,
+                                               const FirstSpan& f, bool have_first) {
     const int lane = acc.lane;
-    const int lo = min(a.V, s0 * kSeg), hi = min(a.V, s1 * kSeg);
     const int hi_whole = r.vec_ok ? lo + ((hi - lo) / kSpan16) * kSpan16 : lo;
-    const int64_t e0 = (int64_t)b * a.nseg;
     const float th = r.tau_hi_f, tl = r.tau_lo_f;
     // segment by segment: a rolling pipeline over the segment's whole spans (group g of the
     // next span is loaded into rt[g], rd[g] as soon as group g of the current one has been
     // taken out of them), then the exact redo of the spans that needed it, with no loads
     // in flight
     for (int g0 = lo; g0 < hi_whole;) {
-        const int g1 = min(hi_whole, (g0 / kSeg + 1) * kSeg);
+        const int g1 = min(hi_whole, (g0 / L + 1) * L);
         u32x4 rt[kG], rd[kG];
         if (have_first && g0 == lo) {
 #pragma unroll
@@ -743,14 +743,14 @@ __device__ __forceinline__ void sweep_wave_tab(const VerifyArgs& a, const DrawRo
             }
         }
         // a segment ends here (or the row does, exactly at a span)
-        if ((g1 & (kSeg - 1)) == 0 || g1 == hi) store_partial(a, e0 + (g0 / kSeg), acc);
+        if (g1 % L == 0 || g1 == hi) store_partial(part, bkt, g0 / L, acc);
         g0 = g1;
     }
     // the rest, segment by segment, one word (two positions) per lane; positions at or
     // past the end read -inf (0xff80), whose weight is 0
     for (int t0 = hi_whole; t0 < hi;) {
-        const int k = t0 / kSeg;
-        const int te = min(hi, (k + 1) * kSeg);
+        const int k = t0 / L;
+        const int te = min(hi, (k + 1) * L);
 #pragma unroll 1
         for (int j0 = t0; j0 < te; j0 += 128) {
             const int i = j0 + 2 * lane;
@@ -763,7 +763,7 @@ __device__ __forceinline__ void sweep_wave_tab(const VerifyArgs& a, const DrawRo
             }
             exact_word_tab<Residual>(r, x0 | (x1 << 16), y0 | (y1 << 16), acc);
         }
-        store_partial(a, e0 + k, acc);
+        store_partial(part, bkt, k, acc);
         t0 = te;
     }
 }
@@ -800,18 +800,16 @@ __device__ __forceinline__ void sweep_vec_exp(const DrawRows<E>& r, const float 
     accumulate<E, P>(r, av, bv, zt, zd, dx_ok, live, s);
 }
 
-// One wave over segments [s0, s1), weights by the fp64 exponential.
+// One wave over positions [lo, hi) in segments of L, weights by the fp64 exponential.
 template <typename E>
-__device__ __forceinline__ void sweep_wave_exp(const VerifyArgs& a, const DrawRows<E>& r, int b, int s0,
-                                               int s1, SweepAcc& acc) {
+__device__ __forceinline__ void sweep_wave_exp(const DrawRows<E>& r, int lo, int hi, int L, DrawPartial* part,
+                                               Bucket* bkt, SweepAcc& acc) {
     constexpr int VEC = Logit<E>::kVec;
     constexpr int P = 4;
     constexpr int span = 64 * VEC;
-    static_assert(kSeg % span == 0, "draw segments are whole spans");
+    static_assert(kSpan16 % span == 0, "draw segments are whole spans");
     const int lane = acc.lane;
-    const int lo = min(a.V, s0 * kSeg), hi = min(a.V, s1 * kSeg);
     const int hi_whole = r.vec_ok ? lo + ((hi - lo) / span) * span : lo;
-    const int64_t e0 = (int64_t)b * a.nseg;
     for (int i0 = lo; i0 < hi_whole; i0 += span) {
         const int i = i0 + lane * VEC;
         float zt[VEC], zd[VEC];
@@ -833,11 +831,11 @@ __device__ __forceinline__ void sweep_wave_exp(const VerifyArgs& a, const DrawRo
             sweep_vec_exp<E, P>(r, tp, dp, acc);
         }
         // a segment ends here (or the row does, exactly at a span)
-        if (((i0 + span) & (kSeg - 1)) == 0 || i0 + span == hi) store_partial(a, e0 + (i0 / kSeg), acc);
+        if ((i0 + span) % L == 0 || i0 + span == hi) store_partial(part, bkt, i0 / L, acc);
     }
     for (int t0 = hi_whole; t0 < hi;) {
-        const int k = t0 / kSeg;
-        const int te = min(hi, (k + 1) * kSeg);
+        const int k = t0 / L;
+        const int te = min(hi, (k + 1) * L);
 #pragma unroll 1
         for (int j0 = t0; j0 < te; j0 += 64) {
             const int i = j0 + lane;
@@ -846,7 +844,7 @@ __device__ __forceinline__ void sweep_wave_exp(const VerifyArgs& a, const DrawRo
             const float d1[1] = {(in && r.residual) ? Logit<E>::at(r.d, i) : -INFINITY};
             sweep_vec_exp<E, 1>(r, t1, d1, acc);
         }
-        store_partial(a, e0 + k, acc);
+        store_partial(part, bkt, k, acc);
         t0 = te;
     }
 }
@@ -860,13 +858,14 @@ __device__ __forceinline__ void sweep_wave_exp(const VerifyArgs& a, const DrawRo
 // standalone: base = 0 and target = u * (sum over the range), taken by a first sweep.
 // If no index qualifies (rounding), the last index with positive weight; -1 if none.
 // lo must be a multiple of VEC.
-template <typename E>
+template <typename E, int NT = kThreads>
 __device__ __forceinline__ int block_search(const DrawRows<E>& r, int lo, int hi, double base, double target,
                             bool standalone, double u) {
     constexpr int VEC = Logit<E>::kVec;
-    constexpr int kTile = VEC * kThreads;
-    __shared__ double shd[kWaves];
-    __shared__ int shi[kWaves];
+    constexpr int NW = NT / 64;
+    constexpr int kTile = VEC * NT;
+    __shared__ double shd[NW];
+    __shared__ int shi[NW];
     const int tid = threadIdx.x;
     if (standalone) {
         double tot = 0.0;
@@ -878,7 +877,7 @@ __device__ __forceinline__ int block_search(const DrawRows<E>& r, int lo, int hi
             double s = 0.0;
 #pragma unroll
             for (int k = 0; k < VEC; ++k) s += r.weight(zt[k], r.residual ? zd[k] : 0.0f);
-            tot += block_sum(s, shd);
+            tot += block_sum<NW>(s, shd);
         }
         base = 0.0;
         target = u * tot;
@@ -899,7 +898,7 @@ __device__ __forceinline__ int block_search(const DrawRows<E>& r, int lo, int hi
             if (w[k] > 0.0) lastpos = i + k;
         }
         double tile_tot;
-        const double ex = block_exclusive_scan(run, tile_tot, shd);
+        const double ex = block_exclusive_scan<NW>(run, tile_tot, shd);
         double acc = base + carry + ex;
         int found = 0x7fffffff;
 #pragma unroll
@@ -907,25 +906,25 @@ __device__ __forceinline__ int block_search(const DrawRows<E>& r, int lo, int hi
             acc += w[k];
             if (found == 0x7fffffff && w[k] > 0.0 && acc > target) found = i + k;
         }
-        const int f = block_min(found, shi);
+        const int f = block_min<NW>(found, shi);
         if (f != 0x7fffffff) return f;
         carry += tile_tot;
     }
-    return block_max(lastpos, shi);
+    return block_max<NW>(lastpos, shi);
 }
 
-// Smallest i in [lo, hi) (hi - lo <= kSeg, lo a multiple of kSeg) with
-// base + (w_lo + ... + w_i) > target, in one tile: each thread takes kSeg / kThreads
-// consecutive positions (a thread-local prefix, then a workgroup exclusive scan of the
-// thread totals).  If no index qualifies (rounding), the last index with positive weight;
-// -1 if none.
-template <typename E>
+// Smallest i in [lo, hi) (hi - lo <= PER * NT, lo a multiple of 16 bytes' worth of
+// logits) with base + (w_lo + ... + w_i) > target, in one tile: each of the NT threads
+// takes PER consecutive positions (a thread-local prefix, then a workgroup exclusive scan
+// of the thread totals).  If no index qualifies (rounding), the last index with positive
+// weight; -1 if none.
+template <typename E, int NT, int PER>
 __device__ __forceinline__ int segment_search(const DrawRows<E>& r, int lo, int hi, double base, double target) {
     constexpr int VEC = Logit<E>::kVec;
-    constexpr int PER = kSeg / kThreads;  // positions per thread
+    constexpr int NW = NT / 64;
     static_assert(PER % VEC == 0, "whole vectors per thread");
-    __shared__ double shd[kWaves];
-    __shared__ int shi[kWaves];
+    __shared__ double shd[NW];
+    __shared__ int shi[NW];
     const int i0 = lo + PER * (int)threadIdx.x;
     double w[PER];
     double run = 0.0;
@@ -943,19 +942,21 @@ __device__ __forceinline__ int segment_search(const DrawRows<E>& r, int lo, int 
         }
     }
     double tot;
-    double acc = base + block_exclusive_scan(run, tot, shd);
+    double acc = base + block_exclusive_scan<NW>(run, tot, shd);
     int found = 0x7fffffff;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         acc += w[k];
         if (found == 0x7fffffff && w[k] > 0.0 && acc > target) found = i0 + k;
     }
-    const int f = block_min(found, shi);
+    const int f = block_min<NW>(found, shi);
     if (f != 0x7fffffff) return f;
-    return block_max(lastpos, shi);
+    return block_max<NW>(lastpos, shi);
 }
 
-// Sums of two doubles and an OR over the workgroup, with one round of barriers.
+// Sums of two doubles and an OR over the workgroup (NW waves), with one round of barriers.
+// sh holds 2 NW doubles, shi NW ints.
+template <int NW>
 __device__ __forceinline__ void block_sum2_or(double& x, double& y, int& o, double* sh, int* shi) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     x = wave_sum(x);
@@ -963,40 +964,41 @@ __device__ __forceinline__ void block_sum2_or(double& x, double& y, int& o, doub
     o = wave_or(o);
     if (lane == 0) {
         sh[w] = x;
-        sh[kWaves + w] = y;
+        sh[NW + w] = y;
         shi[w] = o;
     }
     __syncthreads();
     x = sh[0];
-    y = sh[kWaves];
+    y = sh[NW];
     o = shi[0];
 #pragma unroll
-    for (int k = 1; k < kWaves; ++k) {
+    for (int k = 1; k < NW; ++k) {
         x += sh[k];
-        y += sh[kWaves + k];
+        y += sh[NW + k];
         o |= shi[k];
     }
     __syncthreads();
 }
 
-// The draw when the sequence has at most kThreads segments: thread k holds segment k's
-// partial, loaded once; one reduction, one scan, one segment search.
-template <typename E>
-__device__ __forceinline__ void final_seq_small(const VerifyArgs& a, DrawRows<E> r, const SeqDesc& d, int b) {
-    __shared__ double shd[2 * kWaves];
-    __shared__ int shi[kWaves];
+// The draw of sequence b by a workgroup of NT threads when the sequence has at most NT
+// segments of L positions (L <= PER * NT): thread k holds segment k's partial (part[k],
+// bkt[k * kBuckets ...]), loaded once; one reduction, one scan, one segment search.
+template <typename E, int NT, int PER>
+__device__ __forceinline__ void final_seq_small(const VerifyArgs& a, DrawRows<E> r, const SeqDesc& d, int b,
+                                                const DrawPartial* part, const Bucket* bkt, int nsub, int L) {
+    constexpr int NW = NT / 64;
+    __shared__ double shd[2 * NW];
+    __shared__ int shi[NW];
     __shared__ double sh_base;
     const int tid = threadIdx.x;
-    const int nsub = a.nseg;
-    const int64_t e0 = (int64_t)b * a.nseg;
     const double u = (double)d.u;
     int status = 0;
 
     DrawPartial dp{};
-    if (tid < nsub) dp = a.part2[e0 + tid];
+    if (tid < nsub) dp = part[tid];
     double sp = dp.sp, sq = dp.sq;
     int over = dp.nbkt > kBuckets;
-    block_sum2_or(sp, sq, over, shd, shi);
+    block_sum2_or<NW>(sp, sq, over, shd, shi);
     // the classification by the pass-1 estimate stands if the exact threshold
     // T ln(S_p/S_q) + refA - refB lies well inside the bracket
     bool exact_ok = sp > 0.0;
@@ -1016,7 +1018,7 @@ __device__ __forceinline__ void final_seq_small(const VerifyArgs& a, DrawRows<E>
     int y = -1;
     if (!exact_ok) {
         // too many undecided positions, or the estimate was off: one exact sweep
-        y = block_search(r, 0, a.V, 0.0, 0.0, true, u);
+        y = block_search<E, NT>(r, 0, a.V, 0.0, 0.0, true, u);
     } else {
         // this segment's mass in the units of the draw: its certain part and, per bucket
         // of undecided positions (one residual sign each), the bucket's residual if positive
@@ -1026,7 +1028,7 @@ __device__ __forceinline__ void final_seq_small(const VerifyArgs& a, DrawRows<E>
                 v = dp.sp;
             } else {
                 v = dp.A * r.inv_sp - dp.B * r.inv_sq;
-                const Bucket* bk = a.bkt + (e0 + tid) * kBuckets;
+                const Bucket* bk = bkt + tid * kBuckets;
                 for (int q = 0; q < dp.nbkt; ++q) {
                     const double t = bk[q].a * r.inv_sp - bk[q].b * r.inv_sq;
                     if (t > 0.0) v += t;
@@ -1035,15 +1037,15 @@ __device__ __forceinline__ void final_seq_small(const VerifyArgs& a, DrawRows<E>
             }
         }
         double total;
-        const double ex = block_exclusive_scan(v, total, shd);
+        const double ex = block_exclusive_scan<NW>(v, total, shd);
         if (total > 0.0) {
             const double target = u * total;
             // a segment without mass never holds the first crossing (guards rounding)
-            int hit = block_min((tid < nsub && v > 0.0 && ex + v > target) ? tid : 0x7fffffff, shi);
+            int hit = block_min<NW>((tid < nsub && v > 0.0 && ex + v > target) ? tid : 0x7fffffff, shi);
             double tgt = target;
             if (hit == 0x7fffffff) {
                 // rounding put u*W past every prefix: the last segment with mass, last index
-                hit = block_max((tid < nsub && v > 0.0) ? tid : -1, shi);
+                hit = block_max<NW>((tid < nsub && v > 0.0) ? tid : -1, shi);
                 tgt = INFINITY;
                 status |= kSeqNoteFallback;
             }
@@ -1051,15 +1053,15 @@ __device__ __forceinline__ void final_seq_small(const VerifyArgs& a, DrawRows<E>
             __syncthreads();
             const double base = sh_base;
             int lo, hi;
-            seg_range(a.V, hit, lo, hi);
-            y = segment_search(r, lo, hi, base, tgt);
+            seg_range(a.V, L, hit, lo, hi);
+            y = segment_search<E, NT, PER>(r, lo, hi, base, tgt);
         }
     }
     if (y < 0) {
         // residual without fp64 mass (exact arithmetic rules it out): draw from p_n
         status |= kSeqNoteFallback;
         r.residual = 0;
-        y = block_search(r, 0, a.V, 0.0, 0.0, true, u);
+        y = block_search<E, NT>(r, 0, a.V, 0.0, 0.0, true, u);
     }
     if (tid == 0) {
         a.out_tokens[(int64_t)b * (a.K + 1) + d.n] = y;
@@ -1171,7 +1173,7 @@ __device__ __forceinline__ void final_seq(const VerifyArgs& a, DrawRows<E> r, co
                 base = sh_base;
             }
             int lo, hi;
-            seg_range(a.V, hit, lo, hi);
+            seg_range(a.V, kSeg, hit, lo, hi);
             y = block_search(r, lo, hi, base, tgt, false, u);
         }
     }
@@ -1236,6 +1238,8 @@ void sweep_kernel(VerifyArgs a, int b0) {
     const int c0 = c * a.spc, c1 = min(a.nseg, c0 + a.spc);
     const int per = (c1 - c0 + kWaves - 1) / kWaves;
     const int s0 = min(c1, c0 + w * per), s1 = min(c1, s0 + per);
+    DrawPartial* part = a.part2 + (int64_t)b * a.nseg;
+    Bucket* bkt = a.bkt + (int64_t)b * a.nseg * kBuckets;
     bool done = false;
     if constexpr (sizeof(E) == 2) {
         if (r.use_tab) {
@@ -1250,15 +1254,15 @@ void sweep_kernel(VerifyArgs a, int b0) {
             weight_table_load(a.wtab + (int64_t)b * kWtabLen, wt);
             exp2_table_init(tab);  // its barrier also publishes wt
             if (s0 < s1) {
-                if (r.residual) sweep_wave_tab<true>(a, r, b, s0, s1, acc, f, have_first);
-                else sweep_wave_tab<false>(a, r, b, s0, s1, acc, f, have_first);
+                if (r.residual) sweep_wave_tab<true>(r, lo, hi, kSeg, part, bkt, acc, f, have_first);
+                else sweep_wave_tab<false>(r, lo, hi, kSeg, part, bkt, acc, f, have_first);
             }
             done = true;
         }
     }
     if (!done) {
         exp2_table_init(tab);
-        if (s0 < s1) sweep_wave_exp<E>(a, r, b, s0, s1, acc);
+        if (s0 < s1) sweep_wave_exp<E>(r, min(a.V, s0 * kSeg), min(a.V, s1 * kSeg), kSeg, part, bkt, acc);
     }
 }
 
@@ -1273,8 +1277,11 @@ __global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a, int b0) {
     if (d.mode == kModeNone) return;  // whole workgroup
     exp2_table_init(tab);
     const DrawRows<E> r = draw_rows<E>(a, b, d, tab, nullptr);
-    if (a.nseg <= kThreads) final_seq_small<E>(a, r, d, b);
-    else final_seq<E>(a, r, d, b);
+    if (a.nseg <= kThreads)
+        final_seq_small<E, kThreads, kSeg / kThreads>(a, r, d, b, a.part2 + (int64_t)b * a.nseg,
+                                                      a.bkt + (int64_t)b * a.nseg * kBuckets, a.nseg, kSeg);
+    else
+        final_seq<E>(a, r, d, b);
 }
 
 }  // namespace
