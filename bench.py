@@ -2,12 +2,17 @@
 """Benchmark of the batched speculative-sampling verify step on one MI355X.
 
 One step = the whole hot path over one batch resident in HBM: the counter-based
-uniforms (sv_fill_uniforms) and spec_verify (pass 1 row streaming + resolve, pass 2
+uniforms (sv_fill_uniforms) and spec_verify (pass 1 row streaming; pass 2 resolve and
 categorical draws).  Default workload: B=256 sequences, K=8 drafted tokens,
 V=152064 bf16 logits, Zipf(1.1)-offset target logits, T ~ U[0, 1.2] with a quarter of
 the sequences greedy (T = 0).  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload 4] [--no-cpu-baseline]
+                    [--path verify|ragged|sample]
+
+--path ragged: spec_verify_ragged on the same rows with K_b uniform on 1..K per sequence
+(packed layout); --path sample: sv_sample on the B draft rows of position 0 (one draw per
+row from softmax(z / T)).  Both print the same JSON contract for their own workload.
 """
 import argparse
 import hashlib
@@ -50,6 +55,57 @@ def measured_traffic(workload):
     return float(m_bytes.group(1))
 
 
+def host_logits(x):
+    import numpy as np
+    import torch
+    x = x.detach().cpu()
+    return x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.numpy()
+
+
+def cpu_baseline_ragged(packs, us, budget_s=15.0):
+    """The oracle on whole sequences of the ragged batches, about budget_s s of CPU time."""
+    import numpy as np
+
+    from oracle import spec_verify_oracle as O
+    B = packs[0]["B"]
+    hosts = []
+    for P, u in zip(packs, us):
+        hosts.append(dict(t=host_logits(P["target"]), d=host_logits(P["draft"]),
+                          cu=P["cu"].cpu().numpy(), x=P["tokens"].cpu().numpy(),
+                          u=u.cpu().numpy(), T=P["temperature"].cpu().numpy(), K=P["K_max"]))
+    done, pos, t_total = 0, 0, 0.0
+    while t_total < budget_s:
+        h = hosts[(done // B) % len(hosts)]
+        b = done % B
+        t0 = time.perf_counter()
+        r = O.verify_ragged(h["t"], h["d"], h["cu"], h["x"], h["u"], h["T"], h["K"], seqs=[b])
+        t_total += time.perf_counter() - t0
+        pos += int(r["K"][b]) + 1
+        done += 1
+    del np
+    return dict(value=pos / t_total, unit="positions/s", cores=1, kind="oracle",
+                sample=f"{done} sequences ({pos} positions) of the ragged batches, fp64 numpy "
+                       f"oracle, one thread, {t_total:.1f} s of CPU time")
+
+
+def cpu_baseline_sample(rows, us, Ts, budget_s=15.0):
+    """The oracle's sampler on rows of the timed batches, about budget_s s of CPU time."""
+    from oracle import spec_verify_oracle as O
+    hosts = [(host_logits(z), u.cpu().numpy(), T.cpu().numpy()) for z, u, T in zip(rows, us, Ts)]
+    B = hosts[0][0].shape[0]
+    done, t_total = 0, 0.0
+    while t_total < budget_s:
+        z, u, T = hosts[(done // B) % len(hosts)]
+        b = done % B
+        t0 = time.perf_counter()
+        O.sample(z[b:b + 1], u[b:b + 1], T[b:b + 1])
+        t_total += time.perf_counter() - t0
+        done += 1
+    return dict(value=done / t_total, unit="draws/s", cores=1, kind="oracle",
+                sample=f"{done} rows of the timed batches, fp64 numpy oracle, one thread, "
+                       f"{t_total:.1f} s of CPU time")
+
+
 def cpu_baseline(sets, us, budget_s=15.0):
     """The fp64 oracle as it stands, on the host: whole sequences of the timed batches,
     cycling through them until about budget_s seconds of CPU work (one thread: numpy)."""
@@ -88,6 +144,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", default="verify", choices=["verify", "ragged", "sample"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain device-to-device copy of COPY_BYTES, so that a "
                          "counter profile of this command holds a kernel of known traffic")
@@ -118,6 +175,9 @@ def main():
                  status=torch.empty((B,), dtype=torch.int32, device=dev)) for _ in range(nsets)]
     ws = sv.Workspace(dev)
     seed = 1000 + cfg
+    temps = sets[0]["temperature"]
+    positions = B * (K + 1)
+    p1_bytes = W.logit_bytes(B, K, V, c["dtype"], temps)
 
     def step(i):
         k = i % nsets
@@ -125,6 +185,45 @@ def main():
         sv.sv_fill_uniforms(seed, 0, i, B, K, out=u[k])
         sv.spec_verify(x["target"], x["draft"], x["tokens"], u[k], x["temperature"],
                        out=outs[k], workspace=ws)
+
+    if args.path == "ragged":
+        packs = []
+        for s_, x in enumerate(sets):
+            packs.append(W.pack_ragged(x, W.draft_counts(B, K, 4000 + s_)))
+        del sets[:]
+        torch.cuda.empty_cache()
+        u = [torch.empty((P["total"] + B,), dtype=torch.float32, device=dev) for P in packs]
+        outs = [dict(tokens=torch.empty((P["total"] + B,), dtype=torch.int32, device=dev),
+                     accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
+                     p=torch.empty((P["total"],), dtype=torch.float32, device=dev),
+                     q=torch.empty((P["total"],), dtype=torch.float32, device=dev),
+                     status=torch.empty((B,), dtype=torch.int32, device=dev)) for P in packs]
+        positions = sum(P["total"] + B for P in packs) / nsets
+        p1_bytes = sum(W.ragged_logit_bytes(P["kb"], V, c["dtype"], P["temperature"])
+                       for P in packs) / nsets
+
+        def step(i):  # noqa: F811
+            k = i % nsets
+            P = packs[k]
+            sv.sv_fill_uniforms_ragged(seed, 0, i, P["cu"], P["total"], K, out=u[k])
+            sv.spec_verify_ragged(P["target"], P["draft"], P["cu"], P["tokens"], u[k],
+                                  P["temperature"], K, out=outs[k], workspace=ws)
+    elif args.path == "sample":
+        rows = [x["draft"][:, 0].contiguous() for x in sets]
+        Ts = [x["temperature"] for x in sets]
+        del sets[:]
+        torch.cuda.empty_cache()
+        u = [torch.empty((B,), dtype=torch.float32, device=dev) for _ in range(nsets)]
+        outs = [dict(tokens=torch.empty((B,), dtype=torch.int32, device=dev),
+                     status=torch.empty((B,), dtype=torch.int32, device=dev))
+                for _ in range(nsets)]
+        positions = B
+        p1_bytes = B * V * (2 if c["dtype"] == torch.bfloat16 else 4)
+
+        def step(i):  # noqa: F811
+            k = i % nsets
+            sv.sv_fill_uniforms(seed, 1, i, B, 0, out=u[k].view(B, 1))
+            sv.sv_sample(rows[k], u[k], Ts[k], out=outs[k], workspace=ws)
 
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -167,11 +266,8 @@ def main():
     ms_pass1 = ms_p1 / calls
     ms_pass2 = ms_p2 / calls
 
-    temps = sets[0]["temperature"]
-    p1_bytes = W.logit_bytes(B, K, V, c["dtype"], temps)
-    acc = torch.cat([o["accept_len"].float() for o in outs])
-    bad = int(sum(int((o["status"] & 15).ne(0).sum()) for o in outs))
-    positions = B * (K + 1)
+    acc = torch.cat([o["accept_len"].float() for o in outs]) if "accept_len" in outs[0] else None
+    bad = int(sum(int((o["status"] & ~16).ne(0).sum()) for o in outs))
     value = positions / (ms_step * 1e-3)
     achieved = p1_bytes / (ms_pass1 * 1e-3) / 1e9
     traffic = measured_traffic(cfg)
@@ -203,10 +299,10 @@ def main():
         "ms_pass1": ms_pass1,
         "ms_pass2": ms_pass2,
         "ms_per_step_profiled": ms_step_profiled,
-        "mean_accept_len": float(acc.mean()),
+        "mean_accept_len": None if acc is None else float(acc.mean()),
         "sequences_with_data_errors": bad,
         "roofline": {
-            "kernel": "pass1_kernel (logit row streaming + resolve)",
+            "kernel": "pass1_kernel (logit row streaming)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
@@ -216,9 +312,32 @@ def main():
             "algorithmic_bytes_per_launch": p1_bytes,
         },
     }
+    if args.path == "ragged":
+        kbs = [k for P in packs for k in P["kb"]]
+        result["metric"] = "verified positions/sec at ragged K_b (adaptive verification)"
+        result["config"]["workload"] = (
+            f"ragged: {W.describe(cfg)} rows packed with K_b uniform on 1..{K} "
+            f"(mean {sum(kbs) / len(kbs):.2f}), workload-4 row recipe")
+        result["config"]["K_max"] = K
+        result["config"]["mean_positions"] = positions
+        traffic = None
+        result["roofline"]["traffic"] = None
+    elif args.path == "sample":
+        result["metric"] = "sampled tokens/sec (draft-side sampler)"
+        result["unit"] = "draws/s"
+        result["config"]["workload"] = (f"sampler: B={B} rows of V={V} "
+                                       f"{'bf16' if c['dtype'] == torch.bfloat16 else 'fp32'} "
+                                       "draft logits (workload-4 recipe), T~U[0,1.2], 25% greedy")
+        result["config"]["K"] = 0
+        result["roofline"]["traffic"] = None
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(sets, u)
+        if args.path == "ragged":
+            result["cpu_baseline"] = cpu_baseline_ragged(packs, u)
+        elif args.path == "sample":
+            result["cpu_baseline"] = cpu_baseline_sample(rows, u, Ts)
+        else:
+            result["cpu_baseline"] = cpu_baseline(sets, u)
     print(json.dumps(result), flush=True)
 
 

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 1
+#define SV_ABI_VERSION 2
 
 /* Host-side return codes. */
 typedef enum sv_status {
@@ -72,6 +72,8 @@ typedef enum sv_dtype {
 #define SV_SEQ_ERR_TEMPERATURE  4   /* T NaN, negative, infinite, or in (0, FLT_MIN)                */
 #define SV_SEQ_ERR_UNIFORM      8   /* (sampled sequences) u NaN or outside [0, 1)                  */
 #define SV_SEQ_NOTE_FALLBACK   16   /* not an error: a categorical draw fell back (see above)       */
+#define SV_SEQ_ERR_OFFSETS     32   /* (ragged calls) cu[b], cu[b+1] not 0 <= cu[b] <= cu[b+1] <=
+                                       total_drafts with cu[b+1] - cu[b] <= K_max                   */
 
 /* Returns SV_ABI_VERSION of the loaded library. */
 int sv_abi_version(void);
@@ -134,6 +136,72 @@ sv_status spec_verify_greedy(const void* target_logits, int dtype,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Ragged verify: a different number of drafts K_b per sequence, in the packed layout an
+ * engine's flattened verify batch has.  This serves adaptive verification, where each
+ * request is verified on as many drafted tokens as is worth it (the Speculators talk in
+ * the livestream "IA local 202", [44:15]-[45:16]); the rule applied to each sequence is
+ * the one of spec_verify with K = K_b.  Rows past a sequence's K_b are never read.
+ *
+ *   cu_drafts      device, [B+1] int32 offsets: sequence b has K_b = cu[b+1] - cu[b]
+ *                  drafts; its draft rows, draft tokens, out_p and out_q entries start at
+ *                  index cu[b], its K_b + 1 target rows, uniforms and out_tokens entries at
+ *                  index cu[b] + b.  Expected: cu[0] = 0, non-decreasing, cu[B] = total.
+ *   total_drafts   host int, the number of packed draft rows (sum of K_b).
+ *   K_max          host int, a bound on every K_b (sizes the launch and the workspace).
+ *   target_logits  device, [total_drafts + B][V]; draft_logits device, [total_drafts][V]
+ *                  (rows of T == 0 sequences are not read; NULL allowed iff total == 0).
+ *   draft_tokens   device, [total_drafts] int32 (NULL allowed iff total == 0).
+ *   uniforms       device, [total_drafts + B] fp32: u of test t of sequence b at
+ *                  cu[b] + b + t, the final draw's at cu[b] + b + K_b.
+ *   out_tokens     device, [total_drafts + B] int32: per sequence x_0..x_{n-1}, the
+ *                  drawn token, then -1, over its K_b + 1 slots.
+ *   out_p, out_q   device, [total_drafts] fp32, or NULL.
+ *   temperature, out_accept_len, out_status: [B], as for spec_verify.
+ *   workspace      at least sv_workspace_bytes(B, K_max, V).
+ * A sequence whose offsets break the rule above is flagged SV_SEQ_ERR_OFFSETS, reads
+ * nothing and writes only out_accept_len[b] = -1 and out_status[b]; every other sequence
+ * reads and writes only inside the packed arrays (if cu decreases somewhere, sequences
+ * may overlap and their outputs are unspecified).  Host errors: as spec_verify, plus
+ * SV_ERR_ARG for total_drafts < 0, K_max < 0, a NULL cu_drafts, or sizes that overflow.
+ */
+sv_status spec_verify_ragged(const void* target_logits, const void* draft_logits, int dtype,
+                             const int32_t* cu_drafts, int total_drafts, int K_max,
+                             const int32_t* draft_tokens, const float* uniforms,
+                             const float* temperature, int B, int V,
+                             int32_t* out_tokens, int32_t* out_accept_len,
+                             float* out_p, float* out_q, int32_t* out_status,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Greedy verify in the ragged layout of spec_verify_ragged (target rows only; the rule
+ * of spec_verify_greedy with K = K_b per sequence).
+ */
+sv_status spec_verify_greedy_ragged(const void* target_logits, int dtype,
+                                    const int32_t* cu_drafts, int total_drafts, int K_max,
+                                    const int32_t* draft_tokens, int B, int V,
+                                    int32_t* out_tokens, int32_t* out_accept_len,
+                                    int32_t* out_status,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Draft-side sampler: one token per row from softmax(z / T), the temperature softmax the
+ * draft applies before its draw in the "Desenvolva" listing ("Decodificação Especulativa
+ * e EAGLE"; "Hãy xây dựng nó" on the Vietnamese page), by the categorical-draw rule above
+ * (fp64 weights, smallest i whose prefix exceeds u * sum); at T == 0 the lowest-index
+ * argmax.  The same computation as spec_verify with K = 0.
+ *
+ *   logits         device, [B][V] of `dtype`.
+ *   uniforms       device, [B] fp32 in [0, 1) (not read for T == 0).
+ *   temperature    device, [B] fp32.
+ *   out_tokens     device, [B] int32 (-1 for a sequence with a data error).
+ *   out_status     device, [B] int32, SV_SEQ_* flags.
+ *   workspace      at least sv_workspace_bytes(B, 0, V).
+ */
+sv_status sv_sample(const void* logits, int dtype, const float* uniforms,
+                    const float* temperature, int B, int V, int32_t* out_tokens,
+                    int32_t* out_status, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Fill uniforms[B][K+1] (device, fp32) with the counter-based draws of the exact
  * rule's r ~ Uniform(0, 1) ("A Regra de Exatidão") and of the final categorical draw:
  *   u[b][t] = (w0 >> 40) * 2^-24,   (w0, w1, w2, w3) = Philox4x64-10(counter, key),
@@ -146,10 +214,19 @@ sv_status sv_fill_uniforms(uint64_t seed, uint64_t domain, uint64_t step, int B,
                            float* uniforms, void* stream);
 
 /*
+ * The same draws in the ragged layout: uniforms[cu[b] + b + t] (device, [total_drafts + B])
+ * = the u that sv_fill_uniforms gives for (b, t), for t <= K_b, for every sequence whose
+ * offsets are valid (see spec_verify_ragged; other sequences' slots are not written).
+ */
+sv_status sv_fill_uniforms_ragged(uint64_t seed, uint64_t domain, uint64_t step, int B,
+                                  const int32_t* cu_drafts, int total_drafts, int K_max,
+                                  float* uniforms, void* stream);
+
+/*
  * Kernel timing for benchmarks (host state, not thread-safe).
- * sv_profile_begin: until sv_profile_end, every spec_verify / spec_verify_greedy call
- * records HIP events on its stream around its pass-1 kernel (streaming of the logit
- * rows, the resolve) and around its pass-2 kernels (the categorical draws).
+ * sv_profile_begin: until sv_profile_end, every verify or sampling call records HIP
+ * events on its stream around its pass-1 kernel (streaming of the logit rows) and around
+ * its pass-2 kernels (the resolve and the categorical draw).
  * sv_profile_end: waits for those events, writes the number of calls and the summed
  * milliseconds of each phase (any pointer may be NULL), and stops recording.  Returns
  * SV_ERR_HIP if an event could not be created, recorded or read.

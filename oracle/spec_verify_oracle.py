@@ -62,7 +62,9 @@ SEQ_ERR_LOGIT = 2
 SEQ_ERR_TEMPERATURE = 4
 SEQ_ERR_UNIFORM = 8
 SEQ_NOTE_FALLBACK = 16
-SEQ_ERROR_MASK = SEQ_ERR_TOKEN | SEQ_ERR_LOGIT | SEQ_ERR_TEMPERATURE | SEQ_ERR_UNIFORM
+SEQ_ERR_OFFSETS = 32
+SEQ_ERROR_MASK = (SEQ_ERR_TOKEN | SEQ_ERR_LOGIT | SEQ_ERR_TEMPERATURE | SEQ_ERR_UNIFORM
+                  | SEQ_ERR_OFFSETS)
 
 FP32_MIN_NORMAL = 2.0 ** -126
 
@@ -329,3 +331,77 @@ def verify_greedy(target_logits, draft_tokens, seqs=None):
     B = target_logits.shape[0]
     r = verify(target_logits, None, draft_tokens, None, np.zeros(B, dtype=np.float32), seqs)
     return dict(tokens=r["tokens"], accept_len=r["accept_len"], status=r["status"])
+
+
+# ----------------------------------------------------------------------------
+# Ragged batches and plain sampling
+# ----------------------------------------------------------------------------
+
+def verify_ragged(target_logits, draft_logits, cu_drafts, draft_tokens, uniforms,
+                  temperature, K_max, seqs=None):
+    """Verify with a different number of drafts per sequence (packed layout).
+
+    Adaptive verification (the Speculators talk in the livestream "IA local 202",
+    [44:15]-[45:16]) verifies each request on its own number of drafted tokens K_b; the
+    rule per sequence is the one above with K = K_b.  Layout: sequence b owns draft rows,
+    draft tokens and p/q slots cu[b] .. cu[b+1]-1, and target rows, uniforms and output
+    token slots cu[b]+b .. cu[b+1]+b.  Offsets with cu[b] < 0, cu[b+1] < cu[b],
+    cu[b+1] > total or K_b > K_max flag ERR_OFFSETS (accept length -1, nothing else
+    written for that sequence).
+
+    Returns dict: tokens [total+B] int32 (-1 where unwritten), accept_len [B],
+    p, q [total] float32, status [B], draws {b: list}, and K [B] (K_b, or -1).
+    """
+    cu = [int(v) for v in cu_drafts]
+    B = len(cu) - 1
+    total = len(draft_tokens)
+    out_tokens = np.full(total + B, -1, dtype=np.int32)
+    out_n = np.full(B, -1, dtype=np.int32)
+    out_p = np.full(total, np.nan, dtype=np.float32)
+    out_q = np.full(total, np.nan, dtype=np.float32)
+    out_status = np.full(B, -1, dtype=np.int32)
+    ks = np.full(B, -1, dtype=np.int64)
+    draws = {}
+    for b in (range(B) if seqs is None else seqs):
+        c0, c1 = cu[b], cu[b + 1]
+        if c0 < 0 or c1 < c0 or c1 > total or c1 - c0 > K_max:
+            out_status[b] = SEQ_ERR_OFFSETS
+            draws[b] = []
+            continue
+        K = c1 - c0
+        ks[b] = K
+        T = float(np.float32(temperature[b]))
+        zd = None if T == 0.0 else draft_logits[c0:c1]
+        u = None if T == 0.0 else uniforms[c0 + b:c1 + b + 1]
+        r = verify_sequence(target_logits[c0 + b:c1 + b + 1], zd, draft_tokens[c0:c1], u, T)
+        out_tokens[c0 + b:c1 + b + 1] = r["tokens"]
+        out_n[b] = r["n"]
+        if K:
+            out_p[c0:c1] = np.asarray(r["p"], dtype=np.float64).astype(np.float32)
+            out_q[c0:c1] = np.asarray(r["q"], dtype=np.float64).astype(np.float32)
+        out_status[b] = r["status"]
+        draws[b] = r["draws"]
+    return dict(tokens=out_tokens, accept_len=out_n, p=out_p, q=out_q, status=out_status,
+                draws=draws, K=ks)
+
+
+def sample(logits, uniforms, temperature):
+    """One token per row from softmax(z / T) by the categorical-draw rule, argmax at T = 0.
+
+    This is the draft model's own draw in the "Desenvolva" / "Hãy xây dựng nó" listing
+    (temperature softmax, then a categorical draw), and exactly the verify step with no
+    drafts: the bonus draw from p_0.  Returns dict: tokens [B] int32, status [B] int32,
+    draws {b: list}.
+    """
+    logits = np.asarray(logits)
+    B = logits.shape[0]
+    tokens = np.full(B, -1, dtype=np.int32)
+    status = np.zeros(B, dtype=np.int32)
+    draws = {}
+    for b in range(B):
+        T = float(np.float32(temperature[b]))
+        r = verify_sequence(logits[b:b + 1], None, [], None if T == 0.0 else [uniforms[b]], T)
+        tokens[b] = r["tokens"][0]
+        status[b] = r["status"]
+        draws[b] = r["draws"]
+    return dict(tokens=tokens, status=status, draws=draws)

@@ -12,17 +12,19 @@ __all__ = [
     "LibraryMissing", "SpecVerifyError", "lib", "lib_path",
     "sv_abi_version", "sv_status_string", "sv_workspace_bytes",
     "spec_verify", "spec_verify_greedy", "sv_fill_uniforms", "Workspace",
+    "spec_verify_ragged", "spec_verify_greedy_ragged", "sv_fill_uniforms_ragged", "sv_sample",
     "sv_profile_begin", "sv_profile_end",
     "SV_OK", "SV_ERR_ARG", "SV_ERR_DTYPE", "SV_ERR_WORKSPACE", "SV_ERR_HIP",
     "SV_DTYPE_F32", "SV_DTYPE_BF16",
     "SV_SEQ_ERR_TOKEN", "SV_SEQ_ERR_LOGIT", "SV_SEQ_ERR_TEMPERATURE", "SV_SEQ_ERR_UNIFORM",
-    "SV_SEQ_NOTE_FALLBACK",
+    "SV_SEQ_NOTE_FALLBACK", "SV_SEQ_ERR_OFFSETS",
 ]
 
 SV_OK, SV_ERR_ARG, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_HIP = 0, 1, 2, 3, 4
 SV_DTYPE_F32, SV_DTYPE_BF16 = 0, 1
 SV_SEQ_ERR_TOKEN, SV_SEQ_ERR_LOGIT, SV_SEQ_ERR_TEMPERATURE, SV_SEQ_ERR_UNIFORM = 1, 2, 4, 8
 SV_SEQ_NOTE_FALLBACK = 16
+SV_SEQ_ERR_OFFSETS = 32
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libspecverify.so")
@@ -64,6 +66,16 @@ def lib():
     L.spec_verify_greedy.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.sv_fill_uniforms.restype = i32
     L.sv_fill_uniforms.argtypes = [u64, u64, u64, i32, i32, vp, vp]
+    L.spec_verify_ragged.restype = i32
+    L.spec_verify_ragged.argtypes = [vp, vp, i32, vp, i32, i32, vp, vp, vp, i32, i32,
+                                     vp, vp, vp, vp, vp, vp, sz, vp]
+    L.spec_verify_greedy_ragged.restype = i32
+    L.spec_verify_greedy_ragged.argtypes = [vp, i32, vp, i32, i32, vp, i32, i32,
+                                            vp, vp, vp, vp, sz, vp]
+    L.sv_sample.restype = i32
+    L.sv_sample.argtypes = [vp, i32, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+    L.sv_fill_uniforms_ragged.restype = i32
+    L.sv_fill_uniforms_ragged.argtypes = [u64, u64, u64, i32, vp, i32, i32, vp, vp]
     L.sv_profile_begin.restype = i32
     L.sv_profile_begin.argtypes = []
     L.sv_profile_end.restype = i32
@@ -216,6 +228,112 @@ def spec_verify_greedy(target_logits, draft_tokens, out=None, workspace=None, st
         _ptr(out["accept_len"]), _ptr(out["status"]), _ptr(ws), ws.numel(), _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy")
+    return out
+
+
+def spec_verify_ragged(target_logits, draft_logits, cu_drafts, draft_tokens, uniforms,
+                       temperature, K_max, out=None, with_probs=True, workspace=None,
+                       stream=None):
+    """Ragged verify (packed layout, K_b = cu[b+1] - cu[b] drafts for sequence b).
+
+    target_logits [total+B][V], draft_logits [total][V] (same dtype), cu_drafts [B+1] int32,
+    draft_tokens [total] int32, uniforms [total+B] fp32, temperature [B] fp32, K_max a host
+    bound on every K_b.  total = draft_tokens.shape[0].  Returns dict(tokens [total+B],
+    accept_len [B], p, q [total] or None, status [B]).
+    """
+    torch = _torch()
+    total = int(draft_tokens.shape[0])
+    B = int(cu_drafts.shape[0]) - 1
+    V = int(target_logits.shape[-1])
+    code = _dtype_code(target_logits)
+    _check(target_logits, "target_logits", None, (total + B, V))
+    _check(draft_logits, "draft_logits", target_logits.dtype, (total, V))
+    _check(cu_drafts, "cu_drafts", torch.int32, (B + 1,))
+    _check(draft_tokens, "draft_tokens", torch.int32, (total,))
+    _check(uniforms, "uniforms", torch.float32, (total + B,))
+    _check(temperature, "temperature", torch.float32, (B,))
+    dev = target_logits.device
+    if out is None:
+        out = dict(
+            tokens=torch.empty((total + B,), dtype=torch.int32, device=dev),
+            accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
+            p=torch.empty((total,), dtype=torch.float32, device=dev) if with_probs else None,
+            q=torch.empty((total,), dtype=torch.float32, device=dev) if with_probs else None,
+            status=torch.empty((B,), dtype=torch.int32, device=dev),
+        )
+    ws = _workspace(workspace, dev, B, K_max, V)
+    st = lib().spec_verify_ragged(
+        _ptr(target_logits), _ptr(draft_logits), code, _ptr(cu_drafts), total, int(K_max),
+        _ptr(draft_tokens), _ptr(uniforms), _ptr(temperature), B, V, _ptr(out["tokens"]),
+        _ptr(out["accept_len"]), _ptr(out["p"]), _ptr(out["q"]), _ptr(out["status"]),
+        _ptr(ws), ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_ragged")
+    return out
+
+
+def spec_verify_greedy_ragged(target_logits, cu_drafts, draft_tokens, K_max, out=None,
+                              workspace=None, stream=None):
+    """Greedy verify in the packed layout of spec_verify_ragged."""
+    torch = _torch()
+    total = int(draft_tokens.shape[0])
+    B = int(cu_drafts.shape[0]) - 1
+    V = int(target_logits.shape[-1])
+    code = _dtype_code(target_logits)
+    _check(target_logits, "target_logits", None, (total + B, V))
+    _check(cu_drafts, "cu_drafts", torch.int32, (B + 1,))
+    _check(draft_tokens, "draft_tokens", torch.int32, (total,))
+    dev = target_logits.device
+    if out is None:
+        out = dict(
+            tokens=torch.empty((total + B,), dtype=torch.int32, device=dev),
+            accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
+            status=torch.empty((B,), dtype=torch.int32, device=dev),
+        )
+    ws = _workspace(workspace, dev, B, K_max, V)
+    st = lib().spec_verify_greedy_ragged(
+        _ptr(target_logits), code, _ptr(cu_drafts), total, int(K_max), _ptr(draft_tokens), B, V,
+        _ptr(out["tokens"]), _ptr(out["accept_len"]), _ptr(out["status"]), _ptr(ws),
+        ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_greedy_ragged")
+    return out
+
+
+def sv_sample(logits, uniforms, temperature, out=None, workspace=None, stream=None):
+    """Draft-side sampler: logits [B][V], uniforms [B], temperature [B] -> dict(tokens, status)."""
+    torch = _torch()
+    B, V = logits.shape
+    code = _dtype_code(logits)
+    _check(logits, "logits")
+    _check(uniforms, "uniforms", torch.float32, (B,))
+    _check(temperature, "temperature", torch.float32, (B,))
+    dev = logits.device
+    if out is None:
+        out = dict(tokens=torch.empty((B,), dtype=torch.int32, device=dev),
+                   status=torch.empty((B,), dtype=torch.int32, device=dev))
+    ws = _workspace(workspace, dev, B, 0, V)
+    st = lib().sv_sample(_ptr(logits), code, _ptr(uniforms), _ptr(temperature), B, V,
+                         _ptr(out["tokens"]), _ptr(out["status"]), _ptr(ws), ws.numel(),
+                         _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_sample")
+    return out
+
+
+def sv_fill_uniforms_ragged(seed, domain, step, cu_drafts, total, K_max, out=None,
+                            stream=None):
+    """uniforms [total+B] fp32 in the packed layout (see include/spec_verify.h)."""
+    torch = _torch()
+    B = int(cu_drafts.shape[0]) - 1
+    _check(cu_drafts, "cu_drafts", torch.int32, (B + 1,))
+    if out is None:
+        out = torch.empty((total + B,), dtype=torch.float32, device=cu_drafts.device)
+    _check(out, "uniforms", torch.float32, (total + B,))
+    st = lib().sv_fill_uniforms_ragged(int(seed), int(domain), int(step), B, _ptr(cu_drafts),
+                                       int(total), int(K_max), _ptr(out), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_fill_uniforms_ragged")
     return out
 
 

@@ -80,6 +80,8 @@ sv::VerifyArgs make_args(const void* target, const void* draft, const int32_t* t
     a.tokens = tokens;
     a.uniforms = uniforms;
     a.temperature = temperature;
+    a.cu = nullptr;
+    a.total = 0;
     a.B = B;
     a.K = K;
     a.V = V;
@@ -99,6 +101,30 @@ sv::VerifyArgs make_args(const void* target, const void* draft, const int32_t* t
     a.out_q = out_q;
     a.out_status = out_status;
     return a;
+}
+
+// pass 1, then the resolve and draws, with the benchmark events around each
+sv_status launch(const sv::VerifyArgs& a, int bf16, void* stream) {
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    if (g_prof.on) {
+        for (auto& e : ev) e = g_prof.next();
+        g_prof.calls++;
+        g_prof.record(ev[0], stream);
+    }
+    if (sv::launch_pass1(a, bf16, 0, a.B, stream) != 0) return SV_ERR_HIP;
+    if (g_prof.on) g_prof.record(ev[1], stream);
+    if (sv::launch_draw(a, bf16, 0, a.B, stream) != 0) return SV_ERR_HIP;
+    if (g_prof.on) g_prof.record(ev[2], stream);
+    return SV_OK;
+}
+
+// Packed-layout sizes: (total + B) target rows of V elements must fit comfortably.
+bool packed_shape_ok(int B, int K, int total, int V) {
+    if (B < 0 || K < 0 || total < 0 || V < 1) return false;
+    const __int128 cells = ((__int128)total + B) * V;
+    if (cells > (__int128)INT64_MAX / 8) return false;
+    if ((__int128)total + B > 0x7fffffff) return false;
+    return shape_ok(B, K, V);
 }
 
 }  // namespace
@@ -156,18 +182,64 @@ sv_status spec_verify(const void* target_logits, const void* draft_logits, int d
     const sv::VerifyArgs a = make_args(target_logits, draft_logits, draft_tokens, uniforms,
                                        temperature, B, K, V, R, L, workspace, out_tokens,
                                        out_accept_len, out_p, out_q, out_status);
-    const int bf16 = dtype == SV_DTYPE_BF16;
-    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
-    if (g_prof.on) {
-        for (auto& e : ev) e = g_prof.next();
-        g_prof.calls++;
-    }
-    if (g_prof.on) g_prof.record(ev[0], stream);
-    if (sv::launch_pass1(a, bf16, 0, B, stream) != 0) return SV_ERR_HIP;
-    if (g_prof.on) g_prof.record(ev[1], stream);
-    if (sv::launch_draw(a, bf16, 0, B, stream) != 0) return SV_ERR_HIP;
-    if (g_prof.on) g_prof.record(ev[2], stream);
-    return SV_OK;
+    return launch(a, dtype == SV_DTYPE_BF16, stream);
+}
+
+sv_status spec_verify_ragged(const void* target_logits, const void* draft_logits, int dtype,
+                             const int32_t* cu_drafts, int total_drafts, int K_max,
+                             const int32_t* draft_tokens, const float* uniforms,
+                             const float* temperature, int B, int V,
+                             int32_t* out_tokens, int32_t* out_accept_len,
+                             float* out_p, float* out_q, int32_t* out_status,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_DTYPE;
+    if (!packed_shape_ok(B, K_max, total_drafts, V)) return SV_ERR_ARG;
+    if (B == 0) return SV_OK;
+    const size_t esz = dtype == SV_DTYPE_BF16 ? 2 : 4;
+    if (!target_logits || !cu_drafts || !uniforms || !temperature || !out_tokens ||
+        !out_accept_len || !out_status)
+        return SV_ERR_ARG;
+    if (total_drafts > 0 && (!draft_logits || !draft_tokens)) return SV_ERR_ARG;
+    if (!aligned(target_logits, esz) || (draft_logits && !aligned(draft_logits, esz)))
+        return SV_ERR_ARG;
+    if (!aligned(cu_drafts, 4) || !aligned(uniforms, 4) || !aligned(temperature, 4) ||
+        !aligned(out_tokens, 4) || !aligned(out_accept_len, 4) || !aligned(out_status, 4) ||
+        (draft_tokens && !aligned(draft_tokens, 4)) || (out_p && !aligned(out_p, 4)) ||
+        (out_q && !aligned(out_q, 4)))
+        return SV_ERR_ARG;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < workspace_need(B, K_max, V))
+        return SV_ERR_WORKSPACE;
+    const int R = 2 * K_max + 1;
+    const Layout L = sv::make_layout(B, K_max, V, (int)esz, R);
+    if (!grid_ok(B, R, L)) return SV_ERR_ARG;
+    sv::VerifyArgs a = make_args(target_logits, draft_logits, draft_tokens, uniforms,
+                                 temperature, B, K_max, V, R, L, workspace, out_tokens,
+                                 out_accept_len, out_p, out_q, out_status);
+    a.cu = cu_drafts;
+    a.total = total_drafts;
+    return launch(a, dtype == SV_DTYPE_BF16, stream);
+}
+
+sv_status sv_sample(const void* logits, int dtype, const float* uniforms,
+                    const float* temperature, int B, int V, int32_t* out_tokens,
+                    int32_t* out_status, void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_DTYPE;
+    if (!shape_ok(B, 0, V)) return SV_ERR_ARG;
+    if (B == 0) return SV_OK;
+    const size_t esz = dtype == SV_DTYPE_BF16 ? 2 : 4;
+    if (!logits || !uniforms || !temperature || !out_tokens || !out_status) return SV_ERR_ARG;
+    if (!aligned(logits, esz) || !aligned(uniforms, 4) || !aligned(temperature, 4) ||
+        !aligned(out_tokens, 4) || !aligned(out_status, 4))
+        return SV_ERR_ARG;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < workspace_need(B, 0, V))
+        return SV_ERR_WORKSPACE;
+    const Layout L = sv::make_layout(B, 0, V, (int)esz, 1);
+    if (!grid_ok(B, 1, L)) return SV_ERR_ARG;
+    // the verify step with no drafts: the bonus draw from p_0, or its argmax at T = 0
+    const sv::VerifyArgs a = make_args(logits, nullptr, nullptr, uniforms, temperature, B, 0, V,
+                                       1, L, workspace, out_tokens, nullptr, nullptr, nullptr,
+                                       out_status);
+    return launch(a, dtype == SV_DTYPE_BF16, stream);
 }
 
 sv_status spec_verify_greedy(const void* target_logits, int dtype,
@@ -194,18 +266,37 @@ sv_status spec_verify_greedy(const void* target_logits, int dtype,
     const sv::VerifyArgs a = make_args(target_logits, nullptr, draft_tokens, nullptr, nullptr, B,
                                        K, V, R, L, workspace, out_tokens, out_accept_len, nullptr,
                                        nullptr, out_status);
-    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
-    if (g_prof.on) {
-        for (auto& e : ev) e = g_prof.next();
-        g_prof.calls++;
-    }
-    const int bf16 = dtype == SV_DTYPE_BF16;
-    if (g_prof.on) g_prof.record(ev[0], stream);
-    if (sv::launch_pass1(a, bf16, 0, B, stream) != 0) return SV_ERR_HIP;
-    if (g_prof.on) g_prof.record(ev[1], stream);
-    if (sv::launch_draw(a, bf16, 0, B, stream) != 0) return SV_ERR_HIP;
-    if (g_prof.on) g_prof.record(ev[2], stream);
-    return SV_OK;
+    return launch(a, dtype == SV_DTYPE_BF16, stream);
+}
+
+sv_status spec_verify_greedy_ragged(const void* target_logits, int dtype,
+                                    const int32_t* cu_drafts, int total_drafts, int K_max,
+                                    const int32_t* draft_tokens, int B, int V,
+                                    int32_t* out_tokens, int32_t* out_accept_len,
+                                    int32_t* out_status,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_DTYPE;
+    if (!packed_shape_ok(B, K_max, total_drafts, V)) return SV_ERR_ARG;
+    if (B == 0) return SV_OK;
+    const size_t esz = dtype == SV_DTYPE_BF16 ? 2 : 4;
+    if (!target_logits || !cu_drafts || !out_tokens || !out_accept_len || !out_status)
+        return SV_ERR_ARG;
+    if (total_drafts > 0 && !draft_tokens) return SV_ERR_ARG;
+    if (!aligned(target_logits, esz) || !aligned(cu_drafts, 4) || !aligned(out_tokens, 4) ||
+        !aligned(out_accept_len, 4) || !aligned(out_status, 4) ||
+        (draft_tokens && !aligned(draft_tokens, 4)))
+        return SV_ERR_ARG;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < workspace_need(B, K_max, V))
+        return SV_ERR_WORKSPACE;
+    const int R = K_max + 1;
+    const Layout L = sv::make_layout(B, K_max, V, (int)esz, R);
+    if (!grid_ok(B, R, L)) return SV_ERR_ARG;
+    sv::VerifyArgs a = make_args(target_logits, nullptr, draft_tokens, nullptr, nullptr, B, K_max,
+                                 V, R, L, workspace, out_tokens, out_accept_len, nullptr, nullptr,
+                                 out_status);
+    a.cu = cu_drafts;
+    a.total = total_drafts;
+    return launch(a, dtype == SV_DTYPE_BF16, stream);
 }
 
 sv_status sv_fill_uniforms(uint64_t seed, uint64_t domain, uint64_t step, int B, int K,
@@ -215,6 +306,21 @@ sv_status sv_fill_uniforms(uint64_t seed, uint64_t domain, uint64_t step, int B,
     if (B == 0) return SV_OK;
     if (!uniforms || !aligned(uniforms, 4)) return SV_ERR_ARG;
     if (sv::launch_uniforms(seed, domain, step, B, K, uniforms, stream) != 0) return SV_ERR_HIP;
+    return SV_OK;
+}
+
+sv_status sv_fill_uniforms_ragged(uint64_t seed, uint64_t domain, uint64_t step, int B,
+                                  const int32_t* cu_drafts, int total_drafts, int K_max,
+                                  float* uniforms, void* stream) {
+    if (B < 0 || K_max < 0 || total_drafts < 0) return SV_ERR_ARG;
+    if ((__int128)B * (K_max + 1) > (__int128)0x7fffffff * sv::kThreads) return SV_ERR_ARG;
+    if ((__int128)total_drafts + B > 0x7fffffff) return SV_ERR_ARG;
+    if (B == 0) return SV_OK;
+    if (!cu_drafts || !uniforms || !aligned(cu_drafts, 4) || !aligned(uniforms, 4))
+        return SV_ERR_ARG;
+    if (sv::launch_uniforms_packed(seed, domain, step, B, K_max, cu_drafts, total_drafts,
+                                   uniforms, stream) != 0)
+        return SV_ERR_HIP;
     return SV_OK;
 }
 

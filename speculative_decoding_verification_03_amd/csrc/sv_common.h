@@ -16,6 +16,7 @@ constexpr int kSeqErrLogit = 2;
 constexpr int kSeqErrTemperature = 4;
 constexpr int kSeqErrUniform = 8;
 constexpr int kSeqNoteFallback = 16;
+constexpr int kSeqErrOffsets = 32;
 
 // Draw modes handed from the resolve to the sweep and final kernels.
 constexpr int kModeNone = 0;      // greedy or failed: outputs complete after the resolve
@@ -53,7 +54,7 @@ struct alignas(16) Bucket {
 
 constexpr int kSeg = 4096;         // positions per draw segment (one partial each)
 constexpr int kWtabLen = 4096;     // doubles per sequence of the bf16 weight table
-constexpr int kSeqDescBytes = 48;  // workspace slot of the resolve's per-sequence result
+constexpr int kSeqDescBytes = 64;  // workspace slot of the resolve's per-sequence result
 
 struct Layout {
     int nchunk1, ch1;  // pass-1 chunks per row and elements per chunk (multiple of 64)
@@ -124,12 +125,19 @@ inline Layout make_layout(int B, int K, int V, int esize, int rows_per_seq) {
     return L;
 }
 
+// Row layout.  Dense calls (cu == nullptr): every sequence has K drafts; target rows
+// [B][K+1], draft rows, tokens, p and q [B][K], uniforms and output tokens [B][K+1].
+// Packed calls: sequence b has K_b = cu[b+1] - cu[b] <= K drafts; its draft rows, tokens,
+// p and q start at index cu[b], its target rows, uniforms and output tokens at cu[b] + b.
+// Workspace slots keep the dense [B][R] shape either way (R = 2K+1 or K+1, K the bound).
 struct VerifyArgs {
-    const void* target;        // [B][K+1][V]
-    const void* draft;         // [B][K][V] (may be null when greedy-only or K == 0)
-    const int32_t* tokens;     // [B][K]
-    const float* uniforms;     // [B][K+1] (null when greedy-only)
+    const void* target;        // target rows
+    const void* draft;         // draft rows (may be null when greedy-only or K == 0)
+    const int32_t* tokens;     // draft tokens
+    const float* uniforms;     // (null when greedy-only)
     const float* temperature;  // [B] (null when greedy-only)
+    const int32_t* cu;         // [B+1] packed offsets, or null (dense)
+    int total;                 // packed calls: draft rows in all (cu[B] when valid)
     int B, K, V, R;            // R = rows per sequence handled by pass 1
     int nchunk1, ch1;          // pass-1 chunking
     int nchunk2, spc;          // draw chunking of this launch: chunks per sequence, segments
@@ -141,7 +149,7 @@ struct VerifyArgs {
     Bucket* bkt;               // [B][nseg][kBuckets]
     double* wtab;              // bf16: [B][kWtabLen] weight table of each sequence's draw
     int32_t* out_tokens;
-    int32_t* out_n;
+    int32_t* out_n;            // may be null (plain sampling)
     float* out_p;
     float* out_q;
     int32_t* out_status;
@@ -154,5 +162,8 @@ int launch_pass1(const VerifyArgs& a, int bf16, int b0, int b1, void* stream);
 int launch_draw(const VerifyArgs& a, int bf16, int b0, int b1, void* stream);
 int launch_uniforms(uint64_t seed, uint64_t domain, uint64_t step, int B, int K, float* u,
                     void* stream);
+// Packed layout: u[cu[b] + b + t] for t <= K_b of each sequence with valid offsets.
+int launch_uniforms_packed(uint64_t seed, uint64_t domain, uint64_t step, int B, int K,
+                           const int32_t* cu, int total, float* u, void* stream);
 
 }  // namespace sv

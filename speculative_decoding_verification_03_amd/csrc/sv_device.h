@@ -133,6 +133,38 @@ __device__ __forceinline__ double exp2_arg(double z, double ref, double c) {
 }
 
 // ---------------------------------------------------------------------------------
+// where a sequence's rows live (dense or packed layout, see VerifyArgs)
+// ---------------------------------------------------------------------------------
+
+struct SeqRows {
+    int K;       // drafts of the sequence; -1 when its packed offsets are invalid
+    int64_t t0;  // index of its target row 0 (also of its first uniform and output token)
+    int64_t d0;  // index of its draft row 0 (also of its first draft token, p and q)
+};
+
+// Packed offsets are valid when 0 <= cu[b] <= cu[b+1] <= total and K_b <= K: then every
+// row, token, uniform and output slot the sequence touches lies inside the packed arrays.
+__device__ __forceinline__ SeqRows seq_rows(const VerifyArgs& a, int b) {
+    SeqRows s;
+    if (!a.cu) {
+        s.K = a.K;
+        s.d0 = (int64_t)b * a.K;
+        s.t0 = s.d0 + b;
+        return s;
+    }
+    const int c0 = a.cu[b], c1 = a.cu[b + 1];
+    if (c0 < 0 || c1 < c0 || c1 > a.total || c1 - c0 > a.K) {
+        s.K = -1;
+        s.t0 = s.d0 = 0;
+        return s;
+    }
+    s.K = c1 - c0;
+    s.d0 = c0;
+    s.t0 = (int64_t)c0 + b;
+    return s;
+}
+
+// ---------------------------------------------------------------------------------
 // wavefront reductions (butterfly: every lane ends with the same value)
 // ---------------------------------------------------------------------------------
 

@@ -189,22 +189,24 @@ __global__ __launch_bounds__(kThreads) void pass1_kernel(VerifyArgs a, int b0) {
     const int r = (int)(blk / a.nchunk1);
     const int c = (int)(blk - (int64_t)r * a.nchunk1);
     const int b = b0 + r / a.R;
-    const int j = r % a.R;
+    const int j = r % a.R;  // 0..K target rows, K+1..2K draft rows (K the bound)
     const float T = a.temperature ? a.temperature[b] : 0.0f;
     const bool sampled = !(T == 0.0f);
     if (j > a.K && !sampled) return;  // greedy sequences never read draft rows
-    const E* row = j <= a.K
-                       ? static_cast<const E*>(a.target) + ((int64_t)b * (a.K + 1) + j) * a.V
-                       : static_cast<const E*>(a.draft) + ((int64_t)b * a.K + (j - a.K - 1)) * a.V;
+    const SeqRows s = seq_rows(a, b);
+    const bool is_target = j <= a.K;
+    const int t = is_target ? j : j - a.K - 1;
+    if (t > s.K || (!is_target && t == s.K)) return;  // past this sequence's drafts, or bad offsets
+    const E* row = is_target ? static_cast<const E*>(a.target) + (s.t0 + t) * a.V
+                             : static_cast<const E*>(a.draft) + (s.d0 + t) * a.V;
     const int lo = c * a.ch1;
     const int hi = min(a.V, lo + a.ch1);
     RowPartial* out = a.part1 + ((int64_t)b * a.R + j) * a.nchunk1 + c;
     if (sampled) {
-        // target row t < K or draft row t: the draft token x_t, when it falls in this tile
-        const int t = j <= a.K ? j : j - a.K - 1;
+        // target row t < K_b or draft row t: the draft token x_t, when it falls in this tile
         int xi = -1;
-        if (t < a.K) {
-            const int x = a.tokens[(int64_t)b * a.K + t];
+        if (t < s.K) {
+            const int x = a.tokens[s.d0 + t];
             if (x >= lo && x < hi) xi = x;
         }
         tile_sumexp<E>(row, lo, hi, (float)(kLog2eD / (double)T), xi, out);

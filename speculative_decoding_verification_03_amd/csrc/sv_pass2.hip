@@ -97,6 +97,8 @@ struct SeqDesc {
     // T ln(St/Sd) + mt - md, St and Sd the pass-1 normalisers sum exp((z - m) / T) of the
     // two rows
     double tau_lo, tau_hi;
+    int64_t trow;  // target row of the draw (also the output slot of the drawn token)
+    int64_t drow;  // draft row of the draw (residual draws)
 };
 
 // ------------------------------------------------------------------------------------
@@ -121,11 +123,14 @@ struct RowStat {
 // ln x for finite x > 0 in fp64 (the resolve's few logarithms).
 __device__ __forceinline__ double ln(double x) { return log(x); }
 
-// Row j (0..K target, K+1..2K draft) of sequence b from its pass-1 chunk partials.
-// Greedy: max and lowest index (chunks in order, strict comparison keeps the earlier
-// chunk on ties).  Sampled: max m and S from partials in the 2^((z - m_c) * c2) form.
-__device__ __forceinline__ RowStat merge_row(const VerifyArgs& a, int b, int j, bool sampled, float c2,
-                                             const double* tab) {
+// Row i (0..K_b target rows, K_b+1..2K_b draft rows) of sequence b from its pass-1 chunk
+// partials.  Greedy: max and lowest index (chunks in order, strict comparison keeps the
+// earlier chunk on ties).  Sampled: max m and S from partials in the 2^((z - m_c) * c2) form.
+__device__ __forceinline__ RowStat merge_row(const VerifyArgs& a, int b, const SeqRows& s, int i,
+                                             bool sampled, float c2, const double* tab) {
+    const bool is_target = i <= s.K;
+    const int t = is_target ? i : i - s.K - 1;
+    const int j = is_target ? t : a.K + 1 + t;  // workspace slot (dense layout, K the bound)
     const RowPartial* p = a.part1 + ((int64_t)b * a.R + j) * a.nchunk1;
     RowStat r{-INFINITY, 0x7fffffff, 0.0, -INFINITY};
     if (!sampled) {
@@ -143,10 +148,9 @@ __device__ __forceinline__ RowStat merge_row(const VerifyArgs& a, int b, int j, 
         return r;
     }
     // the chunk holding this row's draft token recorded the logit there
-    const int t = j <= a.K ? j : j - a.K - 1;
     int cx = -1;
-    if (t < a.K) {
-        const int x = a.tokens[(int64_t)b * a.K + t];
+    if (t < s.K) {
+        const int x = a.tokens[s.d0 + t];
         if (x >= 0 && x < a.V) cx = x / a.ch1;
     }
     r.zx = -INFINITY;
@@ -171,11 +175,22 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
     __shared__ int shi[NW];
     __shared__ SeqDesc sd;
     const int tid = threadIdx.x;
-    const int K = a.K, V = a.V, R = a.R;
+    const SeqRows s = seq_rows(a, b);
+    if (s.K < 0) {
+        // packed offsets that do not describe a sequence: nothing of it can be located
+        if (write && tid == 0) {
+            if (a.out_n) a.out_n[b] = -1;
+            a.out_status[b] = kSeqErrOffsets;
+        }
+        SeqDesc d{};
+        d.mode = kModeNone;
+        return d;
+    }
+    const int K = s.K, V = a.V;
     const float T = a.temperature ? a.temperature[b] : 0.0f;
     const bool sampled = !(T == 0.0f);
-    const int32_t* x = a.tokens + (int64_t)b * K;
-    const float* u = sampled ? a.uniforms + (int64_t)b * (K + 1) : nullptr;
+    const int32_t* x = a.tokens + s.d0;
+    const float* u = sampled ? a.uniforms + s.t0 : nullptr;
     const float c2 = sampled ? (float)(kLog2eD / (double)T) : 0.0f;
 
     // tokens and uniforms (the logits at the tokens come with the pass-1 partials)
@@ -195,18 +210,18 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
         }
     if (tid == 0 && temperature_bad(T)) err |= kSeqErrTemperature;
     // row statistics (draft rows only for sampled sequences)
-    const int nrows = sampled ? R : K + 1;
-    for (int j = tid; j < nrows; j += NT) {
-        const RowStat r = merge_row(a, b, j, sampled, c2, tab);
+    const int nrows = sampled ? 2 * K + 1 : K + 1;
+    for (int i = tid; i < nrows; i += NT) {
+        const RowStat r = merge_row(a, b, s, i, sampled, c2, tab);
         if (row_bad(r.m, sampled)) err |= kSeqErrLogit;
-        if (j < kRowsLds) rows[j] = r;
+        if (i < kRowsLds) rows[i] = r;
     }
     err = block_or<NW>(err, shi);  // also orders the rows[] writes before the reads below
-    auto row = [&](int j) -> RowStat { return j < kRowsLds ? rows[j] : merge_row(a, b, j, sampled, c2, tab); };
+    auto row = [&](int i) -> RowStat { return i < kRowsLds ? rows[i] : merge_row(a, b, s, i, sampled, c2, tab); };
 
-    int32_t* tok = a.out_tokens + (int64_t)b * (K + 1);
-    float* op = a.out_p ? a.out_p + (int64_t)b * K : nullptr;
-    float* oq = a.out_q ? a.out_q + (int64_t)b * K : nullptr;
+    int32_t* tok = a.out_tokens + s.t0;
+    float* op = a.out_p ? a.out_p + s.d0 : nullptr;
+    float* oq = a.out_q ? a.out_q + s.d0 : nullptr;
     if (err) {
         if (write) {
             for (int t = tid; t <= K; t += NT) tok[t] = -1;
@@ -215,7 +230,7 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
                 if (oq) oq[t] = __builtin_nanf("");
             }
             if (tid == 0) {
-                a.out_n[b] = -1;
+                if (a.out_n) a.out_n[b] = -1;
                 a.out_status[b] = err;
             }
         }
@@ -260,7 +275,9 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
         SeqDesc d{};
         d.n = n;
         d.T = T;
-        if (write) a.out_n[b] = n;
+        d.trow = s.t0 + n;
+        d.drow = s.d0 + n;
+        if (write && a.out_n) a.out_n[b] = n;
         if (!sampled) {
             if (write) {
                 tok[n] = row(n).idx;
@@ -282,7 +299,7 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
             } else {
                 d.mode = kModeBonus;
             }
-            d.u = a.uniforms[(int64_t)b * (K + 1) + K];
+            d.u = u[K];
         }
         sd = d;
     }
@@ -359,8 +376,8 @@ __device__ __forceinline__ DrawRows<E> draw_rows(const VerifyArgs& a, int b, con
                                                  const double* tab, const double* wt) {
     DrawRows<E> r;
     r.residual = d.mode == kModeResidual;
-    r.t = static_cast<const E*>(a.target) + ((int64_t)b * (a.K + 1) + d.n) * a.V;
-    r.d = r.residual ? static_cast<const E*>(a.draft) + ((int64_t)b * a.K + d.n) * a.V : r.t;
+    r.t = static_cast<const E*>(a.target) + d.trow * a.V;
+    r.d = r.residual ? static_cast<const E*>(a.draft) + d.drow * a.V : r.t;
     const double T = (double)d.T;
     const double c2 = kLog2eD / T;
     r.c256 = 256.0 * c2;
@@ -1064,7 +1081,7 @@ __device__ __forceinline__ void final_seq_small(const VerifyArgs& a, DrawRows<E>
         y = block_search<E, NT>(r, 0, a.V, 0.0, 0.0, true, u);
     }
     if (tid == 0) {
-        a.out_tokens[(int64_t)b * (a.K + 1) + d.n] = y;
+        a.out_tokens[d.trow] = y;
         a.out_status[b] = status;
     }
 }
@@ -1184,7 +1201,7 @@ __device__ __forceinline__ void final_seq(const VerifyArgs& a, DrawRows<E> r, co
         y = block_search(r, 0, a.V, 0.0, 0.0, true, u);
     }
     if (tid == 0) {
-        a.out_tokens[(int64_t)b * (a.K + 1) + d.n] = y;
+        a.out_tokens[d.trow] = y;
         a.out_status[b] = status;
     }
 }

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include "sv_common.h"
+#include "sv_device.h"
 
 namespace sv {
 
@@ -19,12 +20,10 @@ constexpr uint64_t kM1 = 0xCA5A826395121157ull;
 constexpr uint64_t kW0 = 0x9E3779B97F4A7C15ull;
 constexpr uint64_t kW1 = 0xBB67AE8584CAA73Bull;
 
-__global__ __launch_bounds__(kThreads) void uniforms_kernel(uint64_t seed, uint64_t domain,
-                                                            uint64_t step, int64_t total, int K1,
-                                                            float* __restrict__ u) {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= total) return;
-    uint64_t c0 = (uint64_t)(i % K1), c1 = (uint64_t)(i / K1), c2 = step, c3 = 0;
+// u for counter (t, b, step, 0) under key (seed, domain).
+__device__ __forceinline__ float philox_uniform(uint64_t seed, uint64_t domain, uint64_t t,
+                                                uint64_t b, uint64_t step) {
+    uint64_t c0 = t, c1 = b, c2 = step, c3 = 0;
     uint64_t k0 = seed, k1 = domain;
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
@@ -38,7 +37,30 @@ __global__ __launch_bounds__(kThreads) void uniforms_kernel(uint64_t seed, uint6
         k0 += kW0;
         k1 += kW1;
     }
-    u[i] = (float)(uint32_t)(c0 >> 40) * 0x1p-24f;
+    return (float)(uint32_t)(c0 >> 40) * 0x1p-24f;
+}
+
+// dense [B][K1]: thread i is (b, t) = (i / K1, i % K1)
+__global__ __launch_bounds__(kThreads) void uniforms_kernel(uint64_t seed, uint64_t domain,
+                                                            uint64_t step, int64_t total, int K1,
+                                                            float* __restrict__ u) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= total) return;
+    u[i] = philox_uniform(seed, domain, (uint64_t)(i % K1), (uint64_t)(i / K1), step);
+}
+
+// packed: thread i is (b, t) = (i / (K+1), i % (K+1)), K the bound on the drafts; writes
+// u[cu[b] + b + t] for t <= K_b of sequences whose offsets are valid
+__global__ __launch_bounds__(kThreads) void uniforms_packed_kernel(VerifyArgs a, uint64_t seed,
+                                                                   uint64_t domain, uint64_t step,
+                                                                   float* __restrict__ u) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int K1 = a.K + 1;
+    if (i >= (int64_t)a.B * K1) return;
+    const int b = (int)(i / K1), t = (int)(i % K1);
+    const SeqRows s = seq_rows(a, b);
+    if (t > s.K) return;  // also when the offsets are invalid (s.K = -1)
+    u[s.t0 + t] = philox_uniform(seed, domain, (uint64_t)t, (uint64_t)b, step);
 }
 
 }  // namespace
@@ -50,6 +72,21 @@ int launch_uniforms(uint64_t seed, uint64_t domain, uint64_t step, int B, int K,
     const int64_t blocks = (total + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(uniforms_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), seed, domain, step, total, K + 1, u);
+    return (int)hipGetLastError();
+}
+
+int launch_uniforms_packed(uint64_t seed, uint64_t domain, uint64_t step, int B, int K,
+                           const int32_t* cu, int total, float* u, void* stream) {
+    const int64_t n = (int64_t)B * (K + 1);
+    if (n == 0) return 0;
+    VerifyArgs a{};
+    a.cu = cu;
+    a.total = total;
+    a.B = B;
+    a.K = K;
+    const int64_t blocks = (n + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(uniforms_packed_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), a, seed, domain, step, u);
     return (int)hipGetLastError();
 }
 

@@ -23,6 +23,10 @@ Workloads (V = vocabulary size, K = drafted tokens, B = sequences):
                                    64 smallest target logits of each row (q sits where
                                    p is tiny, so the first draft is rejected)
 The sigma values come from the oracle-side calibration script (oracle/calibrate_sigma.py).
+
+Ragged batches (adaptive verification, a number of drafts K_b per sequence) are packed
+from a dense batch: sequence b keeps its first K_b draft rows and K_b + 1 target rows.
+The ragged workload draws K_b uniformly from {1, ..., K} on workload 4's rows.
 """
 import math
 
@@ -132,11 +136,47 @@ def make_inputs(cfg, step=0, device="cuda", B=None, seed=None):
                 cfg=cfg, B=B, K=K, V=V)
 
 
+def draft_counts(B, K, seed, kmin=1):
+    """K_b for each sequence, uniform on {kmin, ..., K} (host generator, seeded)."""
+    gh = torch.Generator().manual_seed(int(seed) + 29)
+    return torch.randint(kmin, K + 1, (B,), generator=gh).tolist()
+
+
+def pack_ragged(inp, kb):
+    """Packed inputs from dense ones: kb[b] <= K drafts kept for sequence b.
+
+    Returns dict(target [total+B][V], draft [total][V], tokens [total] int32,
+    cu [B+1] int32 (device), kb (list), temperature [B], K_max, total, B, V).
+    """
+    B, K1, V = inp["target"].shape
+    dev = inp["target"].device
+    cu = [0]
+    for k in kb:
+        cu.append(cu[-1] + int(k))
+    total = cu[-1]
+    trow = torch.tensor([b * K1 + t for b in range(B) for t in range(kb[b] + 1)], device=dev)
+    drow = torch.tensor([b * (K1 - 1) + t for b in range(B) for t in range(kb[b])],
+                        dtype=torch.int64, device=dev)
+    target = inp["target"].reshape(B * K1, V).index_select(0, trow).contiguous()
+    draft = inp["draft"].reshape(B * (K1 - 1), V).index_select(0, drow).contiguous()
+    tokens = inp["tokens"].reshape(-1).index_select(0, drow).contiguous()
+    return dict(target=target, draft=draft, tokens=tokens,
+                cu=torch.tensor(cu, dtype=torch.int32, device=dev), kb=list(kb),
+                temperature=inp["temperature"], K_max=K1 - 1, total=total, B=B, V=V)
+
+
 def logit_bytes(B, K, V, dtype, temperature):
     """Algorithmic pass-1 bytes: target rows of every sequence, draft rows of sampled ones."""
     e = 2 if dtype == torch.bfloat16 else 4
     sampled = int((temperature != 0).sum())
     return e * V * (B * (K + 1) + sampled * K)
+
+
+def ragged_logit_bytes(kb, V, dtype, temperature):
+    """Algorithmic pass-1 bytes of a ragged batch."""
+    e = 2 if dtype == torch.bfloat16 else 4
+    T = temperature.cpu()
+    return e * V * sum(k + 1 + (k if float(T[b]) != 0.0 else 0) for b, k in enumerate(kb))
 
 
 def expected_draw_bytes(B, K, V, dtype):

@@ -26,7 +26,9 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "sv_abi_version", "sv_status_string", "sv_workspace_bytes", "spec_verify",
-        "spec_verify_greedy", "sv_fill_uniforms", "sv_profile_begin", "sv_profile_end"])
+        "spec_verify_greedy", "sv_fill_uniforms", "sv_profile_begin", "sv_profile_end",
+        "spec_verify_ragged", "spec_verify_greedy_ragged", "sv_sample",
+        "sv_fill_uniforms_ragged"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -36,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert sv.sv_abi_version() == 1
+    assert sv.sv_abi_version() == 2
     assert sv.sv_status_string(sv.SV_OK) == "ok"
     assert sv.sv_status_string(sv.SV_ERR_ARG) == "invalid argument"
     assert sv.sv_status_string(sv.SV_ERR_WORKSPACE).startswith("workspace")
@@ -140,6 +142,85 @@ def test_fill_uniforms_rejects_bad_arguments():
     assert L.sv_fill_uniforms(1, 0, 0, 4, 4, None, None) == sv.SV_ERR_ARG
     assert L.sv_fill_uniforms(1, 0, 0, 4, 4, _p(GOOD + 1), None) == sv.SV_ERR_ARG
     assert L.sv_fill_uniforms(1, 0, 0, 0, 4, None, None) == sv.SV_OK
+
+
+def call_ragged(**kw):
+    args = dict(t=GOOD, d=GOOD, dtype=sv.SV_DTYPE_BF16, cu=GOOD, total=10, K=4, x=GOOD, u=GOOD,
+                T=GOOD, B=4, V=64, tok=GOOD, n=GOOD, p=GOOD, q=GOOD, st=GOOD, ws=WS, wsb=1 << 30)
+    args.update(kw)
+    a = args
+    return sv.lib().spec_verify_ragged(
+        _p(a["t"]), _p(a["d"]), a["dtype"], _p(a["cu"]), a["total"], a["K"], _p(a["x"]),
+        _p(a["u"]), _p(a["T"]), a["B"], a["V"], _p(a["tok"]), _p(a["n"]), _p(a["p"]),
+        _p(a["q"]), _p(a["st"]), _p(a["ws"]), a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3), sv.SV_ERR_DTYPE),
+    (dict(B=-1), sv.SV_ERR_ARG),
+    (dict(K=-1), sv.SV_ERR_ARG),
+    (dict(total=-1), sv.SV_ERR_ARG),
+    (dict(V=0), sv.SV_ERR_ARG),
+    (dict(cu=0), sv.SV_ERR_ARG),
+    (dict(cu=GOOD + 2), sv.SV_ERR_ARG),
+    (dict(t=0), sv.SV_ERR_ARG),
+    (dict(d=0), sv.SV_ERR_ARG),                    # total > 0 needs draft rows
+    (dict(x=0), sv.SV_ERR_ARG),
+    (dict(u=0), sv.SV_ERR_ARG),
+    (dict(T=0), sv.SV_ERR_ARG),
+    (dict(tok=0), sv.SV_ERR_ARG),
+    (dict(n=0), sv.SV_ERR_ARG),
+    (dict(st=0), sv.SV_ERR_ARG),
+    (dict(q=GOOD + 1), sv.SV_ERR_ARG),
+    (dict(ws=0), sv.SV_ERR_WORKSPACE),
+    (dict(wsb=64), sv.SV_ERR_WORKSPACE),
+    (dict(total=2 ** 31 - 2, B=4, V=2 ** 30), sv.SV_ERR_ARG),
+])
+def test_spec_verify_ragged_rejects_bad_arguments(kw, status):
+    assert call_ragged(**kw) == status
+
+
+def test_ragged_edge_shapes_without_launch():
+    assert call_ragged(B=0, t=0, cu=0, u=0, T=0, tok=0, n=0, st=0, ws=0, wsb=0) == sv.SV_OK
+    # no drafts at all: no draft logits or tokens are needed, the rest is
+    assert call_ragged(total=0, d=0, x=0, ws=0) == sv.SV_ERR_WORKSPACE
+    # the workspace is sized by the bound K_max
+    need = sv.sv_workspace_bytes(4, 4, 64)
+    assert call_ragged(wsb=need - 1) == sv.SV_ERR_WORKSPACE
+
+
+def test_greedy_ragged_and_sample_reject_bad_arguments():
+    L = sv.lib()
+    g = lambda **kw: L.spec_verify_greedy_ragged(  # noqa: E731
+        _p(kw.get("t", GOOD)), kw.get("dtype", 0), _p(kw.get("cu", GOOD)), kw.get("total", 3),
+        kw.get("K", 2), _p(kw.get("x", GOOD)), kw.get("B", 2), kw.get("V", 64), _p(GOOD), _p(GOOD),
+        _p(GOOD), _p(kw.get("ws", WS)), kw.get("wsb", 1 << 30), None)
+    assert g(dtype=9) == sv.SV_ERR_DTYPE
+    assert g(cu=0) == sv.SV_ERR_ARG
+    assert g(x=0) == sv.SV_ERR_ARG
+    assert g(total=-2) == sv.SV_ERR_ARG
+    assert g(ws=0) == sv.SV_ERR_WORKSPACE
+    assert g(B=0, cu=0, t=0, ws=0) == sv.SV_OK
+    smp = lambda **kw: L.sv_sample(  # noqa: E731
+        _p(kw.get("z", GOOD)), kw.get("dtype", 1), _p(kw.get("u", GOOD)), _p(kw.get("T", GOOD)),
+        kw.get("B", 4), kw.get("V", 100), _p(kw.get("tok", GOOD)), _p(kw.get("st", GOOD)),
+        _p(kw.get("ws", WS)), kw.get("wsb", 1 << 30), None)
+    assert smp(dtype=7) == sv.SV_ERR_DTYPE
+    assert smp(B=-1) == sv.SV_ERR_ARG
+    assert smp(V=0) == sv.SV_ERR_ARG
+    assert smp(z=0) == sv.SV_ERR_ARG
+    assert smp(z=GOOD + 1) == sv.SV_ERR_ARG
+    assert smp(u=0) == sv.SV_ERR_ARG
+    assert smp(T=0) == sv.SV_ERR_ARG
+    assert smp(tok=0) == sv.SV_ERR_ARG
+    assert smp(st=0) == sv.SV_ERR_ARG
+    assert smp(wsb=8) == sv.SV_ERR_WORKSPACE
+    assert smp(B=0, z=0, u=0, T=0, tok=0, st=0, ws=0) == sv.SV_OK
+    assert L.sv_fill_uniforms_ragged(1, 0, 0, -1, _p(GOOD), 3, 2, _p(GOOD), None) == sv.SV_ERR_ARG
+    assert L.sv_fill_uniforms_ragged(1, 0, 0, 2, None, 3, 2, _p(GOOD), None) == sv.SV_ERR_ARG
+    assert L.sv_fill_uniforms_ragged(1, 0, 0, 2, _p(GOOD), -3, 2, _p(GOOD), None) == sv.SV_ERR_ARG
+    assert L.sv_fill_uniforms_ragged(1, 0, 0, 2, _p(GOOD), 3, 2, _p(GOOD + 1), None) == sv.SV_ERR_ARG
+    assert L.sv_fill_uniforms_ragged(1, 0, 0, 0, None, 0, 2, None, None) == sv.SV_OK
 
 
 def test_binding_refuses_host_tensors():
