@@ -8,11 +8,12 @@ V=152064 bf16 logits, Zipf(1.1)-offset target logits, T ~ U[0, 1.2] with a quart
 the sequences greedy (T = 0).  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload 4] [--no-cpu-baseline]
-                    [--path verify|ragged|sample]
+                    [--path verify|ragged|sample|tree]
 
 --path ragged: spec_verify_ragged on the same rows with K_b uniform on 1..K per sequence
 (packed layout); --path sample: sv_sample on the B draft rows of position 0 (one draw per
-row from softmax(z / T)).  Both print the same JSON contract for their own workload.
+row from softmax(z / T)); --path tree: spec_verify_tree_greedy on 64 draft trees of 64
+nodes (V=152064 bf16).  Each prints the same JSON contract for its own workload.
 """
 import argparse
 import hashlib
@@ -106,6 +107,25 @@ def cpu_baseline_sample(rows, us, Ts, budget_s=15.0):
                        f"{t_total:.1f} s of CPU time")
 
 
+def cpu_baseline_tree(trees, budget_s=15.0):
+    """The oracle's tree verification on whole trees of the timed batches."""
+    from oracle import spec_verify_oracle as O
+    hosts = [(host_logits(t["target"]), t["parents"].cpu().numpy(), t["tokens"].cpu().numpy())
+             for t in trees]
+    B, N = hosts[0][1].shape
+    done, t_total = 0, 0.0
+    while t_total < budget_s:
+        z, par, tok = hosts[(done // B) % len(hosts)]
+        b = done % B
+        t0 = time.perf_counter()
+        O.verify_tree_sequence(z[b], par[b], tok[b])
+        t_total += time.perf_counter() - t0
+        done += 1
+    return dict(value=done * N / t_total, unit="nodes/s", cores=1, kind="oracle",
+                sample=f"{done} trees of {N} nodes of the timed batches, fp64 numpy oracle, "
+                       f"one thread, {t_total:.1f} s of CPU time")
+
+
 def cpu_baseline(sets, us, budget_s=15.0):
     """The fp64 oracle as it stands, on the host: whole sequences of the timed batches,
     cycling through them until about budget_s seconds of CPU work (one thread: numpy)."""
@@ -144,7 +164,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", default="verify", choices=["verify", "ragged", "sample"])
+    ap.add_argument("--path", default="verify", choices=["verify", "ragged", "sample", "tree"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain device-to-device copy of COPY_BYTES, so that a "
                          "counter profile of this command holds a kernel of known traffic")
@@ -163,9 +183,10 @@ def main():
     dev = torch.device("cuda:0")
     cfg = args.workload
     c = W.CONFIGS[cfg]
-    log(f"bench: workload {cfg} ({W.describe(cfg)}), generating inputs")
+    log(f"bench: workload {cfg} ({W.describe(cfg)}), path {args.path}, generating inputs")
     nsets = 2
-    sets = [W.make_inputs(cfg, step=s, device=dev) for s in range(nsets)]
+    sets = ([W.make_inputs(cfg, step=s, device=dev) for s in range(nsets)] if args.path != "tree"
+            else [W.make_inputs(cfg, step=s, device=dev, B=1) for s in range(nsets)])
     B, K, V = sets[0]["B"], sets[0]["K"], sets[0]["V"]
     u = [torch.empty((B, K + 1), dtype=torch.float32, device=dev) for _ in range(nsets)]
     outs = [dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
@@ -186,7 +207,24 @@ def main():
         sv.spec_verify(x["target"], x["draft"], x["tokens"], u[k], x["temperature"],
                        out=outs[k], workspace=ws)
 
-    if args.path == "ragged":
+    if args.path == "tree":
+        trees = [W.make_tree_inputs(device=dev, V=V, dtype=c["dtype"], step=s_)
+                 for s_ in range(nsets)]
+        B, N = trees[0]["B"], trees[0]["N"]
+        outs = [dict(tokens=torch.empty((B, N), dtype=torch.int32, device=dev),
+                     nodes=torch.empty((B, N), dtype=torch.int32, device=dev),
+                     accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
+                     status=torch.empty((B,), dtype=torch.int32, device=dev))
+                for _ in range(nsets)]
+        positions = B * N
+        p1_bytes = B * N * V * (2 if c["dtype"] == torch.bfloat16 else 4)
+
+        def step(i):  # noqa: F811
+            k = i % nsets
+            t = trees[k]
+            sv.spec_verify_tree_greedy(t["target"], t["parents"], t["tokens"], out=outs[k],
+                                       workspace=ws)
+    elif args.path == "ragged":
         packs = []
         for s_, x in enumerate(sets):
             packs.append(W.pack_ragged(x, W.draft_counts(B, K, 4000 + s_)))
@@ -322,6 +360,16 @@ def main():
         result["config"]["mean_positions"] = positions
         traffic = None
         result["roofline"]["traffic"] = None
+    elif args.path == "tree":
+        result["metric"] = "verified tree nodes/sec (greedy tree verification)"
+        result["unit"] = "nodes/s"
+        result["dtype"] = "f32"
+        result["config"] = {
+            "workload": f"tree: B={B} trees of N={N} nodes (levels {list(W.TREE_LEVELS)}), "
+                        f"V={V} {'bf16' if c['dtype'] == torch.bfloat16 else 'fp32'}, "
+                        "workload-4 row recipe, node token = parent row argmax w.p. 0.75",
+            "B": B, "N": N, "V": V, "parallelism": "single GPU"}
+        result["roofline"]["traffic"] = None
     elif args.path == "sample":
         result["metric"] = "sampled tokens/sec (draft-side sampler)"
         result["unit"] = "draws/s"
@@ -332,7 +380,9 @@ def main():
         result["roofline"]["traffic"] = None
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
-        if args.path == "ragged":
+        if args.path == "tree":
+            result["cpu_baseline"] = cpu_baseline_tree(trees)
+        elif args.path == "ragged":
             result["cpu_baseline"] = cpu_baseline_ragged(packs, u)
         elif args.path == "sample":
             result["cpu_baseline"] = cpu_baseline_sample(rows, u, Ts)

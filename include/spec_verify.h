@@ -72,6 +72,8 @@ typedef enum sv_dtype {
 #define SV_SEQ_ERR_TEMPERATURE  4   /* T NaN, negative, infinite, or in (0, FLT_MIN)                */
 #define SV_SEQ_ERR_UNIFORM      8   /* (sampled sequences) u NaN or outside [0, 1)                  */
 #define SV_SEQ_NOTE_FALLBACK   16   /* not an error: a categorical draw fell back (see above)       */
+#define SV_SEQ_ERR_TREE        64   /* (tree calls) parents[b][0] != -1, or a parents[b][j] outside
+                                       [0, j) for j >= 1                                             */
 #define SV_SEQ_ERR_OFFSETS     32   /* (ragged calls) cu[b], cu[b+1] not 0 <= cu[b] <= cu[b+1] <=
                                        total_drafts with cu[b+1] - cu[b] <= K_max                   */
 
@@ -182,6 +184,59 @@ sv_status spec_verify_greedy_ragged(const void* target_logits, int dtype,
                                     int32_t* out_tokens, int32_t* out_accept_len,
                                     int32_t* out_status,
                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Largest token tree of the tree entry points (nodes per sequence, root included). */
+#define SV_TREE_MAX_NODES 1024
+
+/*
+ * Greedy verification of a draft token tree.  Node 0 of each sequence's tree is the
+ * root (the last token already emitted); node j >= 1 carries a drafted token and has a
+ * parent p(j) < j.  The target has scored all nodes in one forward pass under the tree
+ * attention mask (sv_tree_attention_mask): its row j is the next-token logits after the
+ * path root -> j.  Rule: node j is accepted when its parent is accepted and its token is
+ * the lowest-index argmax of its parent's row (the greedy rule of spec_verify_greedy
+ * along every root path); the root is accepted.  The winner is the deepest accepted node
+ * a, the lowest index among equally deep ones: the longest prefix along any accepted
+ * path.  The emitted tokens are the tokens along root -> a, then the argmax of a's row.
+ * Source: "Verificação de Atenção em Árvore" on the lesson page "Decodificação
+ * Especulativa e EAGLE" ("Kiểm tra sự chú ý của cây" on the Vietnamese page); the EAGLE
+ * section of "Accelerating Sonar through speculation" (the longest accepted candidate
+ * plus one token from the target).  The pages give no sampled rule for trees.
+ *
+ *   target_logits  device, [B][N][V] of `dtype`.
+ *   parents        device, [B][N] int32: -1 for node 0, else in [0, j).
+ *   node_tokens    device, [B][N] int32, in [0, V) for j >= 1 (node 0's is not read).
+ *   B, N, V        B >= 0, 1 <= N <= SV_TREE_MAX_NODES, V >= 1.
+ *   out_tokens     device, [B][N] int32: the d tokens along the winning path, the
+ *                  target's token after it, then -1.
+ *   out_nodes      device, [B][N] int32, or NULL: the d node indices along the path
+ *                  (root excluded), then -1 (which drafted nodes' KV entries to keep).
+ *   out_accept_len device, [B] int32: d, the depth of the winning node.
+ *   out_status     device, [B] int32: SV_SEQ_* flags (TREE, TOKEN, LOGIT); a flagged
+ *                  sequence emits -1 everywhere.
+ *   workspace      at least sv_workspace_bytes(B, N - 1, V).
+ * Bit-exact by construction (comparisons only).
+ */
+sv_status spec_verify_tree_greedy(const void* target_logits, int dtype, const int32_t* parents,
+                                  const int32_t* node_tokens, int B, int N, int V,
+                                  int32_t* out_tokens, int32_t* out_nodes,
+                                  int32_t* out_accept_len, int32_t* out_status,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The tree attention mask of the same trees: out_mask[b][i][j] = 1 when node j is node i
+ * or one of its ancestors (each token attends only to its ancestors, "Verificação de
+ * Atenção em Árvore"), else 0; out_depth[b][i] (optional) = the number of edges from the
+ * root to node i (the position offset of node i's token).  A sequence whose parents
+ * break the rule of spec_verify_tree_greedy gets SV_SEQ_ERR_TREE in out_status[b], an
+ * all-zero mask and depths -1; otherwise out_status[b] = 0.
+ *   parents   device, [B][N] int32;  out_mask device, [B][N][N] uint8;
+ *   out_depth device, [B][N] int32 or NULL;  out_status device, [B] int32.
+ * Host errors: SV_ERR_ARG for B < 0, N outside [1, SV_TREE_MAX_NODES], NULL required
+ * pointers or misaligned int32 pointers.
+ */
+sv_status sv_tree_attention_mask(const int32_t* parents, int B, int N, uint8_t* out_mask,
+                                 int32_t* out_depth, int32_t* out_status, void* stream);
 
 /*
  * Draft-side sampler: one token per row from softmax(z / T), the temperature softmax the

@@ -63,8 +63,9 @@ SEQ_ERR_TEMPERATURE = 4
 SEQ_ERR_UNIFORM = 8
 SEQ_NOTE_FALLBACK = 16
 SEQ_ERR_OFFSETS = 32
+SEQ_ERR_TREE = 64
 SEQ_ERROR_MASK = (SEQ_ERR_TOKEN | SEQ_ERR_LOGIT | SEQ_ERR_TEMPERATURE | SEQ_ERR_UNIFORM
-                  | SEQ_ERR_OFFSETS)
+                  | SEQ_ERR_OFFSETS | SEQ_ERR_TREE)
 
 FP32_MIN_NORMAL = 2.0 ** -126
 
@@ -405,3 +406,109 @@ def sample(logits, uniforms, temperature):
         status[b] = r["status"]
         draws[b] = r["draws"]
     return dict(tokens=tokens, status=status, draws=draws)
+
+
+# ----------------------------------------------------------------------------
+# Token trees (greedy)
+# ----------------------------------------------------------------------------
+
+def tree_parents_ok(parents):
+    """Node 0 is the root (parent -1); every other node's parent comes before it."""
+    return all((p == -1) if j == 0 else (0 <= p < j) for j, p in enumerate(parents))
+
+
+def verify_tree_sequence(zt, parents, tokens):
+    """Greedy verification of one draft token tree.
+
+    The target scores every node of the tree in one pass under a tree attention mask,
+    and the output is the longest prefix along any accepted root path ("Verificação de
+    Atenção em Árvore" on the lesson page "Decodificação Especulativa e EAGLE"; the EAGLE
+    section of "Accelerating Sonar through speculation").  With the greedy rule
+    ("Caso ganancioso") on every root path: the root (node 0) is accepted; node j is
+    accepted when its parent p(j) is accepted and its token equals argmax of row p(j),
+    row i being the target's logits after the path root -> i.  Reading (the pages do not
+    say which of several equally long paths wins): the deepest accepted node, the lowest
+    index among equally deep ones.  Emitted: the tokens along root -> winner, then the
+    argmax of the winner's row.
+
+    zt: [N][V] logits; parents: [N] ints; tokens: [N] ints (tokens[0] unused).
+    Returns dict: tokens [N] (-1 padded), nodes [N] (path nodes, root excluded, -1
+    padded), n (depth of the winner), status.
+    """
+    zt = np.asarray(zt)
+    N, V = zt.shape
+    parents = [int(p) for p in parents]
+    tokens = [int(t) for t in tokens]
+    status = SEQ_OK
+    if not tree_parents_ok(parents):
+        status |= SEQ_ERR_TREE
+    if any(t < 0 or t >= V for t in tokens[1:]):
+        status |= SEQ_ERR_TOKEN
+    rows = [decode_logits(zt[j]) for j in range(N)]
+    if any(row_error(r, False) for r in rows):
+        status |= SEQ_ERR_LOGIT
+    if status & SEQ_ERROR_MASK:
+        return dict(tokens=[-1] * N, nodes=[-1] * N, n=-1, status=status)
+    amax = [argmax_first(r) for r in rows]
+    accepted = [True] + [False] * (N - 1)
+    depth = [0] * N
+    for j in range(1, N):
+        p = parents[j]
+        depth[j] = depth[p] + 1
+        accepted[j] = accepted[p] and tokens[j] == amax[p]
+    win = 0
+    for j in range(N):
+        if accepted[j] and depth[j] > depth[win]:
+            win = j
+    path = []
+    cur = win
+    while cur != 0:
+        path.append(cur)
+        cur = parents[cur]
+    path.reverse()
+    d = len(path)
+    out_tokens = [tokens[j] for j in path] + [amax[win]] + [-1] * (N - d - 1)
+    out_nodes = path + [-1] * (N - d)
+    return dict(tokens=out_tokens, nodes=out_nodes, n=d, status=status)
+
+
+def verify_tree_greedy(target_logits, parents, node_tokens):
+    """Batched tree verification: target_logits [B][N][V], parents and node_tokens [B][N].
+    Returns dict of numpy arrays tokens, nodes [B][N], accept_len [B], status [B]."""
+    target_logits = np.asarray(target_logits)
+    B, N, _ = target_logits.shape
+    out = dict(tokens=np.full((B, N), -1, dtype=np.int32), nodes=np.full((B, N), -1, dtype=np.int32),
+               accept_len=np.full(B, -1, dtype=np.int32), status=np.zeros(B, dtype=np.int32))
+    for b in range(B):
+        r = verify_tree_sequence(target_logits[b], parents[b], node_tokens[b])
+        out["tokens"][b] = r["tokens"]
+        out["nodes"][b] = r["nodes"]
+        out["accept_len"][b] = r["n"]
+        out["status"][b] = r["status"]
+    return out
+
+
+def tree_attention_mask(parents):
+    """mask[i][j] = 1 when node j is node i or an ancestor of it (each token attends only
+    to its ancestors, "Verificação de Atenção em Árvore"); depth[i] = edges from the root.
+    A malformed tree gives an all-zero mask, depths -1 and ERR_TREE.  parents: [B][N]."""
+    parents = np.asarray(parents)
+    B, N = parents.shape
+    mask = np.zeros((B, N, N), dtype=np.uint8)
+    depth = np.full((B, N), -1, dtype=np.int32)
+    status = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        par = [int(p) for p in parents[b]]
+        if not tree_parents_ok(par):
+            status[b] = SEQ_ERR_TREE
+            continue
+        for i in range(N):
+            cur, d = i, 0
+            while True:
+                mask[b, i, cur] = 1
+                if cur == 0:
+                    break
+                cur = par[cur]
+                d += 1
+            depth[b, i] = d
+    return dict(mask=mask, depth=depth, status=status)

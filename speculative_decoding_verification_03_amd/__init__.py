@@ -13,11 +13,12 @@ __all__ = [
     "sv_abi_version", "sv_status_string", "sv_workspace_bytes",
     "spec_verify", "spec_verify_greedy", "sv_fill_uniforms", "Workspace",
     "spec_verify_ragged", "spec_verify_greedy_ragged", "sv_fill_uniforms_ragged", "sv_sample",
+    "spec_verify_tree_greedy", "sv_tree_attention_mask", "SV_TREE_MAX_NODES",
     "sv_profile_begin", "sv_profile_end",
     "SV_OK", "SV_ERR_ARG", "SV_ERR_DTYPE", "SV_ERR_WORKSPACE", "SV_ERR_HIP",
     "SV_DTYPE_F32", "SV_DTYPE_BF16",
     "SV_SEQ_ERR_TOKEN", "SV_SEQ_ERR_LOGIT", "SV_SEQ_ERR_TEMPERATURE", "SV_SEQ_ERR_UNIFORM",
-    "SV_SEQ_NOTE_FALLBACK", "SV_SEQ_ERR_OFFSETS",
+    "SV_SEQ_NOTE_FALLBACK", "SV_SEQ_ERR_OFFSETS", "SV_SEQ_ERR_TREE",
 ]
 
 SV_OK, SV_ERR_ARG, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_HIP = 0, 1, 2, 3, 4
@@ -25,6 +26,8 @@ SV_DTYPE_F32, SV_DTYPE_BF16 = 0, 1
 SV_SEQ_ERR_TOKEN, SV_SEQ_ERR_LOGIT, SV_SEQ_ERR_TEMPERATURE, SV_SEQ_ERR_UNIFORM = 1, 2, 4, 8
 SV_SEQ_NOTE_FALLBACK = 16
 SV_SEQ_ERR_OFFSETS = 32
+SV_SEQ_ERR_TREE = 64
+SV_TREE_MAX_NODES = 1024
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libspecverify.so")
@@ -74,6 +77,10 @@ def lib():
                                             vp, vp, vp, vp, sz, vp]
     L.sv_sample.restype = i32
     L.sv_sample.argtypes = [vp, i32, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+    L.spec_verify_tree_greedy.restype = i32
+    L.spec_verify_tree_greedy.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.sv_tree_attention_mask.restype = i32
+    L.sv_tree_attention_mask.argtypes = [vp, i32, i32, vp, vp, vp, vp]
     L.sv_fill_uniforms_ragged.restype = i32
     L.sv_fill_uniforms_ragged.argtypes = [u64, u64, u64, i32, vp, i32, i32, vp, vp]
     L.sv_profile_begin.restype = i32
@@ -318,6 +325,52 @@ def sv_sample(logits, uniforms, temperature, out=None, workspace=None, stream=No
                          _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "sv_sample")
+    return out
+
+
+def spec_verify_tree_greedy(target_logits, parents, node_tokens, out=None, with_nodes=True,
+                            workspace=None, stream=None):
+    """Greedy verification of draft token trees: target_logits [B][N][V] (row j = logits
+    after node j's path), parents [B][N] int32 (-1 for the root, else an earlier node),
+    node_tokens [B][N] int32.  Returns dict(tokens [B][N], nodes [B][N] or None,
+    accept_len [B], status [B])."""
+    torch = _torch()
+    B, N, V = target_logits.shape
+    code = _dtype_code(target_logits)
+    _check(target_logits, "target_logits")
+    _check(parents, "parents", torch.int32, (B, N))
+    _check(node_tokens, "node_tokens", torch.int32, (B, N))
+    dev = target_logits.device
+    if out is None:
+        out = dict(tokens=torch.empty((B, N), dtype=torch.int32, device=dev),
+                   nodes=torch.empty((B, N), dtype=torch.int32, device=dev) if with_nodes else None,
+                   accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
+                   status=torch.empty((B,), dtype=torch.int32, device=dev))
+    ws = _workspace(workspace, dev, B, max(N - 1, 0), V)
+    st = lib().spec_verify_tree_greedy(
+        _ptr(target_logits), code, _ptr(parents), _ptr(node_tokens), B, N, V, _ptr(out["tokens"]),
+        _ptr(out["nodes"]), _ptr(out["accept_len"]), _ptr(out["status"]), _ptr(ws), ws.numel(),
+        _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_tree_greedy")
+    return out
+
+
+def sv_tree_attention_mask(parents, out=None, with_depth=True, stream=None):
+    """Tree attention mask [B][N][N] uint8 (1: column node is the row node or an ancestor),
+    depths [B][N] and status [B] of the trees given by parents [B][N] int32."""
+    torch = _torch()
+    B, N = parents.shape
+    _check(parents, "parents", torch.int32, (B, N))
+    dev = parents.device
+    if out is None:
+        out = dict(mask=torch.empty((B, N, N), dtype=torch.uint8, device=dev),
+                   depth=torch.empty((B, N), dtype=torch.int32, device=dev) if with_depth else None,
+                   status=torch.empty((B,), dtype=torch.int32, device=dev))
+    st = lib().sv_tree_attention_mask(_ptr(parents), B, N, _ptr(out["mask"]), _ptr(out["depth"]),
+                                      _ptr(out["status"]), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "sv_tree_attention_mask")
     return out
 
 

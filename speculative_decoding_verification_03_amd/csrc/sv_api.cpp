@@ -103,8 +103,10 @@ sv::VerifyArgs make_args(const void* target, const void* draft, const int32_t* t
     return a;
 }
 
-// pass 1, then the resolve and draws, with the benchmark events around each
-sv_status launch(const sv::VerifyArgs& a, int bf16, void* stream) {
+// pass 1, then `second` (the resolve and draws, or the tree resolve), with the
+// benchmark events around each
+template <class F>
+sv_status launch_two(const sv::VerifyArgs& a, int bf16, void* stream, F&& second) {
     hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
     if (g_prof.on) {
         for (auto& e : ev) e = g_prof.next();
@@ -113,9 +115,13 @@ sv_status launch(const sv::VerifyArgs& a, int bf16, void* stream) {
     }
     if (sv::launch_pass1(a, bf16, 0, a.B, stream) != 0) return SV_ERR_HIP;
     if (g_prof.on) g_prof.record(ev[1], stream);
-    if (sv::launch_draw(a, bf16, 0, a.B, stream) != 0) return SV_ERR_HIP;
+    if (second() != 0) return SV_ERR_HIP;
     if (g_prof.on) g_prof.record(ev[2], stream);
     return SV_OK;
+}
+
+sv_status launch(const sv::VerifyArgs& a, int bf16, void* stream) {
+    return launch_two(a, bf16, stream, [&] { return sv::launch_draw(a, bf16, 0, a.B, stream); });
 }
 
 // Packed-layout sizes: (total + B) target rows of V elements must fit comfortably.
@@ -306,6 +312,66 @@ sv_status sv_fill_uniforms(uint64_t seed, uint64_t domain, uint64_t step, int B,
     if (B == 0) return SV_OK;
     if (!uniforms || !aligned(uniforms, 4)) return SV_ERR_ARG;
     if (sv::launch_uniforms(seed, domain, step, B, K, uniforms, stream) != 0) return SV_ERR_HIP;
+    return SV_OK;
+}
+
+sv_status spec_verify_tree_greedy(const void* target_logits, int dtype, const int32_t* parents,
+                                  const int32_t* node_tokens, int B, int N, int V,
+                                  int32_t* out_tokens, int32_t* out_nodes,
+                                  int32_t* out_accept_len, int32_t* out_status,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_DTYPE;
+    if (B < 0 || N < 1 || N > sv::kTreeMaxNodes || !shape_ok(B, N - 1, V)) return SV_ERR_ARG;
+    if (B == 0) return SV_OK;
+    const size_t esz = dtype == SV_DTYPE_BF16 ? 2 : 4;
+    if (!target_logits || !parents || !node_tokens || !out_tokens || !out_accept_len ||
+        !out_status)
+        return SV_ERR_ARG;
+    if (!aligned(target_logits, esz) || !aligned(parents, 4) || !aligned(node_tokens, 4) ||
+        !aligned(out_tokens, 4) || !aligned(out_accept_len, 4) || !aligned(out_status, 4) ||
+        (out_nodes && !aligned(out_nodes, 4)))
+        return SV_ERR_ARG;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < workspace_need(B, N - 1, V))
+        return SV_ERR_WORKSPACE;
+    const int R = N;
+    const Layout L = sv::make_layout(B, N - 1, V, (int)esz, R);
+    if (!grid_ok(B, R, L)) return SV_ERR_ARG;
+    // pass 1 over the N target rows of every sequence as greedy rows (no temperature)
+    const sv::VerifyArgs a = make_args(target_logits, nullptr, nullptr, nullptr, nullptr, B, N - 1,
+                                       V, R, L, workspace, nullptr, nullptr, nullptr, nullptr,
+                                       nullptr);
+    sv::TreeArgs t;
+    memset(&t, 0, sizeof(t));
+    t.parents = parents;
+    t.tokens = node_tokens;
+    t.part1 = a.part1;
+    t.B = B;
+    t.N = N;
+    t.V = V;
+    t.nchunk1 = L.nchunk1;
+    t.out_tokens = out_tokens;
+    t.out_nodes = out_nodes;
+    t.out_n = out_accept_len;
+    t.out_status = out_status;
+    return launch_two(a, dtype == SV_DTYPE_BF16, stream, [&] { return sv::launch_tree(t, stream); });
+}
+
+sv_status sv_tree_attention_mask(const int32_t* parents, int B, int N, uint8_t* out_mask,
+                                 int32_t* out_depth, int32_t* out_status, void* stream) {
+    if (B < 0 || N < 1 || N > sv::kTreeMaxNodes) return SV_ERR_ARG;
+    if (B == 0) return SV_OK;
+    if (!parents || !out_mask || !out_status || !aligned(parents, 4) || !aligned(out_status, 4) ||
+        (out_depth && !aligned(out_depth, 4)))
+        return SV_ERR_ARG;
+    sv::TreeArgs t;
+    memset(&t, 0, sizeof(t));
+    t.parents = parents;
+    t.B = B;
+    t.N = N;
+    t.out_mask = out_mask;
+    t.out_depth = out_depth;
+    t.out_status = out_status;
+    if (sv::launch_tree_mask(t, stream) != 0) return SV_ERR_HIP;
     return SV_OK;
 }
 

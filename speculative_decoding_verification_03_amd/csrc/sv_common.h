@@ -17,6 +17,10 @@ constexpr int kSeqErrTemperature = 4;
 constexpr int kSeqErrUniform = 8;
 constexpr int kSeqNoteFallback = 16;
 constexpr int kSeqErrOffsets = 32;
+constexpr int kSeqErrTree = 64;
+
+// Largest token tree (nodes per sequence, root included) of the tree entry points.
+constexpr int kTreeMaxNodes = 1024;
 
 // Draw modes handed from the resolve to the sweep and final kernels.
 constexpr int kModeNone = 0;      // greedy or failed: outputs complete after the resolve
@@ -155,6 +159,21 @@ struct VerifyArgs {
     int32_t* out_status;
 };
 
+// Tree verification: parents [B][N] (root -1, else in [0, j)), node tokens [B][N] (node
+// 0's unused); part1 holds pass 1's greedy partials of the N target rows per sequence.
+struct TreeArgs {
+    const int32_t* parents;
+    const int32_t* tokens;
+    const RowPartial* part1;  // [B][N][nchunk1]
+    int B, N, V, nchunk1;
+    int32_t* out_tokens;      // [B][N]
+    int32_t* out_nodes;       // [B][N] or null
+    int32_t* out_n;           // [B]
+    int32_t* out_status;      // [B]
+    uint8_t* out_mask;        // [B][N][N] (mask kernel)
+    int32_t* out_depth;       // [B][N] or null (mask kernel)
+};
+
 // Internal launchers (return hipError_t as int; 0 = success).  Sequences [b0, b1).
 // launch_draw runs the resolve and the draws of those sequences (greedy-only calls: the
 // resolve only) after their pass 1, on the same stream.
@@ -162,6 +181,8 @@ int launch_pass1(const VerifyArgs& a, int bf16, int b0, int b1, void* stream);
 int launch_draw(const VerifyArgs& a, int bf16, int b0, int b1, void* stream);
 int launch_uniforms(uint64_t seed, uint64_t domain, uint64_t step, int B, int K, float* u,
                     void* stream);
+int launch_tree(const TreeArgs& a, void* stream);
+int launch_tree_mask(const TreeArgs& a, void* stream);
 // Packed layout: u[cu[b] + b + t] for t <= K_b of each sequence with valid offsets.
 int launch_uniforms_packed(uint64_t seed, uint64_t domain, uint64_t step, int B, int K,
                            const int32_t* cu, int total, float* u, void* stream);

@@ -27,6 +27,12 @@ The sigma values come from the oracle-side calibration script (oracle/calibrate_
 Ragged batches (adaptive verification, a number of drafts K_b per sequence) are packed
 from a dense batch: sequence b keeps its first K_b draft rows and K_b + 1 target rows.
 The ragged workload draws K_b uniformly from {1, ..., K} on workload 4's rows.
+
+Token trees (greedy tree verification): B trees of N nodes laid out level by level
+(TREE_LEVELS nodes per level, 64 nodes, depth 8), each node's parent drawn uniformly
+from the level above; target rows follow workload 4's recipe (Zipf(1.1)-offset
+N(0, 3^2)); a node's token is the argmax of its parent's row with probability 0.75 (a
+drafter that agrees with the target), else uniform on the vocabulary.
 """
 import math
 
@@ -163,6 +169,40 @@ def pack_ragged(inp, kb):
     return dict(target=target, draft=draft, tokens=tokens,
                 cu=torch.tensor(cu, dtype=torch.int32, device=dev), kb=list(kb),
                 temperature=inp["temperature"], K_max=K1 - 1, total=total, B=B, V=V)
+
+
+TREE_LEVELS = (1, 4, 8, 12, 12, 12, 8, 4, 3)
+
+
+def make_tree_inputs(B=64, V=152064, dtype=torch.bfloat16, levels=TREE_LEVELS, step=0,
+                     device="cuda", seed=None, agree=0.75):
+    """Tree inputs: dict(target [B][N][V], parents [B][N] int32, tokens [B][N] int32)."""
+    N = sum(levels)
+    seed = 7_000_003 + 131 * step if seed is None else seed
+    g = _gen(device, seed)
+    gh = torch.Generator().manual_seed(int(seed) + 5)
+    parents = torch.empty((B, N), dtype=torch.int32)
+    for b in range(B):
+        parents[b, 0] = -1
+        start, prev = 1, (0, 1)
+        for n in levels[1:]:
+            parents[b, start:start + n] = torch.randint(prev[0], prev[1], (n,), generator=gh,
+                                                        dtype=torch.int32)
+            prev = (start, start + n)
+            start += n
+    target = torch.empty((B, N, V), dtype=dtype, device=device)
+    for b in range(B):
+        rank = torch.randperm(V, generator=g, device=device).to(torch.float32) + 1.0
+        zt = 3.0 * torch.randn((N, V), generator=g, device=device) - 1.1 * torch.log(rank)
+        target[b] = zt.to(dtype)
+    amax = torch.stack([torch.argmax(target[b].float(), dim=-1) for b in range(B)]).cpu()
+    agree_mask = torch.rand((B, N), generator=gh) < agree
+    rand_tok = torch.randint(0, V, (B, N), generator=gh)
+    par = parents.clamp_min(0).long()
+    tokens = torch.where(agree_mask, torch.gather(amax, 1, par), rand_tok).to(torch.int32)
+    tokens[:, 0] = 0
+    return dict(target=target, parents=parents.to(device), tokens=tokens.to(device), B=B, N=N,
+                V=V)
 
 
 def logit_bytes(B, K, V, dtype, temperature):

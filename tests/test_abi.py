@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
         "sv_abi_version", "sv_status_string", "sv_workspace_bytes", "spec_verify",
         "spec_verify_greedy", "sv_fill_uniforms", "sv_profile_begin", "sv_profile_end",
         "spec_verify_ragged", "spec_verify_greedy_ragged", "sv_sample",
-        "sv_fill_uniforms_ragged"])
+        "sv_fill_uniforms_ragged", "spec_verify_tree_greedy", "sv_tree_attention_mask"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -221,6 +221,38 @@ def test_greedy_ragged_and_sample_reject_bad_arguments():
     assert L.sv_fill_uniforms_ragged(1, 0, 0, 2, _p(GOOD), -3, 2, _p(GOOD), None) == sv.SV_ERR_ARG
     assert L.sv_fill_uniforms_ragged(1, 0, 0, 2, _p(GOOD), 3, 2, _p(GOOD + 1), None) == sv.SV_ERR_ARG
     assert L.sv_fill_uniforms_ragged(1, 0, 0, 0, None, 0, 2, None, None) == sv.SV_OK
+
+
+def test_tree_entry_points_reject_bad_arguments():
+    L = sv.lib()
+    t = lambda **kw: L.spec_verify_tree_greedy(  # noqa: E731
+        _p(kw.get("z", GOOD)), kw.get("dtype", 1), _p(kw.get("par", GOOD)), _p(kw.get("x", GOOD)),
+        kw.get("B", 4), kw.get("N", 16), kw.get("V", 100), _p(kw.get("tok", GOOD)),
+        _p(kw.get("nodes", GOOD)), _p(kw.get("n", GOOD)), _p(kw.get("st", GOOD)),
+        _p(kw.get("ws", WS)), kw.get("wsb", 1 << 30), None)
+    assert t(dtype=4) == sv.SV_ERR_DTYPE
+    assert t(B=-1) == sv.SV_ERR_ARG
+    assert t(N=0) == sv.SV_ERR_ARG
+    assert t(N=sv.SV_TREE_MAX_NODES + 1) == sv.SV_ERR_ARG
+    assert t(V=0) == sv.SV_ERR_ARG
+    for k in ("z", "par", "x", "tok", "n", "st"):
+        assert t(**{k: 0}) == sv.SV_ERR_ARG, k
+    assert t(par=GOOD + 2) == sv.SV_ERR_ARG
+    assert t(nodes=GOOD + 1) == sv.SV_ERR_ARG
+    assert t(ws=0) == sv.SV_ERR_WORKSPACE
+    assert t(wsb=sv.sv_workspace_bytes(4, 15, 100) - 1) == sv.SV_ERR_WORKSPACE
+    assert t(B=0, z=0, par=0, x=0, tok=0, n=0, st=0, ws=0) == sv.SV_OK
+    m = lambda **kw: L.sv_tree_attention_mask(  # noqa: E731
+        _p(kw.get("par", GOOD)), kw.get("B", 2), kw.get("N", 8), _p(kw.get("mask", GOOD)),
+        _p(kw.get("dep", GOOD)), _p(kw.get("st", GOOD)), None)
+    assert m(B=-1) == sv.SV_ERR_ARG
+    assert m(N=0) == sv.SV_ERR_ARG
+    assert m(N=2000) == sv.SV_ERR_ARG
+    assert m(par=0) == sv.SV_ERR_ARG
+    assert m(mask=0) == sv.SV_ERR_ARG
+    assert m(st=0) == sv.SV_ERR_ARG
+    assert m(dep=GOOD + 2) == sv.SV_ERR_ARG
+    assert m(B=0, par=0, mask=0, st=0) == sv.SV_OK
 
 
 def test_binding_refuses_host_tensors():

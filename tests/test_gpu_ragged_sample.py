@@ -213,3 +213,120 @@ def test_sample_parity(dev, B, V, dt):
         np.testing.assert_array_equal(r["tokens"], v["tokens"][:, 0])
     say("  ", t)
     t.assert_ok("sampler")
+
+
+# ------------------------------------------------------------------------------------
+# token trees (greedy) and the tree attention mask
+# ------------------------------------------------------------------------------------
+
+def run_tree(inp):
+    out = sv.spec_verify_tree_greedy(inp["target"], inp["parents"], inp["tokens"])
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+def oracle_tree(inp):
+    return O.verify_tree_greedy(logits_to_host(inp["target"]), inp["parents"].cpu().numpy(),
+                                inp["tokens"].cpu().numpy())
+
+
+def assert_tree_equal(g, o, what):
+    for k in ("tokens", "nodes", "accept_len", "status"):
+        np.testing.assert_array_equal(g[k], o[k], err_msg=f"{what}: {k}")
+
+
+def random_trees(dev, B, N, V, dt, seed, shape, agree=0.7, ties=False):
+    rng = np.random.default_rng(seed)
+    par = np.full((B, N), -1, dtype=np.int32)
+    for b in range(B):
+        for j in range(1, N):
+            if shape == "chain":
+                par[b, j] = j - 1
+            elif shape == "star":
+                par[b, j] = 0
+            elif shape == "binary":
+                par[b, j] = (j - 1) // 2
+            else:
+                par[b, j] = rng.integers(max(0, j - 6), j)
+    g = torch.Generator(device=dev).manual_seed(seed)
+    if ties:
+        z = torch.randint(-2, 2, (B, N, V), generator=g, device=dev).float()
+    else:
+        z = 2.0 * torch.randn((B, N, V), generator=g, device=dev)
+    z = z.to(dt).contiguous()
+    amax = torch.argmax(z.float(), dim=-1).cpu().numpy()
+    tok = np.where(rng.random((B, N)) < agree,
+                   np.take_along_axis(amax, np.maximum(par, 0).astype(np.int64), axis=1),
+                   rng.integers(0, V, (B, N)))
+    tok[:, 0] = 0
+    return dict(target=z, parents=torch.tensor(par, device=dev),
+                tokens=torch.tensor(tok.astype(np.int32), device=dev))
+
+
+TREES = [
+    # B, N, V, dtype, shape, ties
+    (8, 9, 1000, torch.float32, "chain", False),
+    (8, 31, 1003, torch.bfloat16, "binary", True),
+    (6, 64, 40000, torch.bfloat16, "random", False),
+    (4, 200, 777, torch.float32, "random", True),
+    (3, 1024, 300, torch.bfloat16, "random", True),   # the largest tree
+    (5, 1, 5000, torch.float32, "star", False),       # root only
+    (3, 17, 130001, torch.bfloat16, "star", False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(TREES)))
+def test_tree_parity(dev, case):
+    B, N, V, dt, shape, ties = TREES[case]
+    say(f"tree case {case}: B={B} N={N} V={V} {dt} {shape} ties={ties}")
+    for rep in range(2):
+        inp = random_trees(dev, B, N, V, dt, 300 + 10 * case + rep, shape, ties=ties)
+        g = run_tree(inp)
+        o = oracle_tree(inp)
+        assert_tree_equal(g, o, f"tree {case}")
+        say("   accept", g["accept_len"].tolist()[:8])
+        m = sv.sv_tree_attention_mask(inp["parents"])
+        torch.cuda.synchronize()
+        m = to_host(m)
+        om = O.tree_attention_mask(inp["parents"].cpu().numpy())
+        for k in ("mask", "depth", "status"):
+            np.testing.assert_array_equal(m[k], om[k], err_msg=f"tree mask {case}: {k}")
+
+
+def test_tree_chain_equals_linear_greedy(dev):
+    """A chain tree is the linear verify: spec_verify_greedy on the same rows."""
+    B, K, V = 16, 8, 152064
+    inp = W.make_inputs(4, step=5, device=dev, B=B)
+    par = torch.tensor([[-1] + list(range(K))] * B, dtype=torch.int32, device=dev)
+    tok = torch.cat([torch.zeros((B, 1), dtype=torch.int32, device=dev), inp["tokens"]], dim=1)
+    g = run_tree(dict(target=inp["target"], parents=par, tokens=tok.contiguous()))
+    lin = to_host(sv.spec_verify_greedy(inp["target"], inp["tokens"]))
+    np.testing.assert_array_equal(g["tokens"], lin["tokens"])
+    np.testing.assert_array_equal(g["accept_len"], lin["accept_len"])
+
+
+def test_tree_errors_flagged(dev):
+    B, N, V = 4, 6, 500
+    inp = random_trees(dev, B, N, V, torch.float32, 9, "random")
+    par = inp["parents"].clone()
+    par[1, 3] = 3            # not an earlier node
+    par[2, 0] = 0            # root with a parent
+    tok = inp["tokens"].clone()
+    tok[3, 2] = V            # token outside the vocabulary
+    tgt = inp["target"].clone()
+    tgt[0, 4, 7] = float("nan")
+    bad = dict(target=tgt, parents=par, tokens=tok)
+    assert_tree_equal(run_tree(bad), oracle_tree(bad), "tree errors")
+    m = to_host(sv.sv_tree_attention_mask(par))
+    om = O.tree_attention_mask(par.cpu().numpy())
+    for k in ("mask", "depth", "status"):
+        np.testing.assert_array_equal(m[k], om[k])
+
+
+def test_tree_workload_full_size(dev):
+    """The tree benchmark workload (64 trees of 64 nodes, V=152064 bf16) against the oracle."""
+    inp = W.make_tree_inputs(device=dev)
+    g = run_tree(inp)
+    o = oracle_tree(inp)
+    assert_tree_equal(g, o, "tree workload")
+    say("   tree workload mean accept", float(g["accept_len"].mean()))
