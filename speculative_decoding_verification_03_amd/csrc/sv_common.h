@@ -78,6 +78,11 @@ constexpr int kMinChunk1 = 4096;
 #define SV_TARGET_BLOCKS2 2560
 #endif
 constexpr int kTargetBlocks2 = SV_TARGET_BLOCKS2;
+// Threads of a sweep workgroup: each wave sweeps its own run of draw segments.
+#ifndef SV_SWEEP_THREADS
+#define SV_SWEEP_THREADS 256
+#endif
+constexpr int kSweepThreads = SV_SWEEP_THREADS;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

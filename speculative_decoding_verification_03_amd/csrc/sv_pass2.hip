@@ -59,6 +59,18 @@ constexpr double kFlushLog2 = 70.0;
 constexpr double kMaxRefGapLog2 = 900.0;
 // Row statistics of the resolve kept in LDS; rows past this are merged again on demand.
 constexpr int kRowsLds = 64;
+// Pass-1 partials of one sequence the resolve stages in LDS (16 KB); more stay in memory.
+constexpr int kPartsLds = 1024;
+// Threads of a resolve workgroup (one workgroup per sequence).
+#ifndef SV_RESOLVE_THREADS
+#define SV_RESOLVE_THREADS 1024
+#endif
+constexpr int kResolveThreads = SV_RESOLVE_THREADS;
+// Threads of a final workgroup (one workgroup per sequence; a multiple of kSeg / 8).
+#ifndef SV_FINAL_THREADS
+#define SV_FINAL_THREADS 512
+#endif
+constexpr int kFinalThreads = SV_FINAL_THREADS;
 
 // bf16 weight table in LDS: two halves of kTabHalf slots (positive, then negative values).
 // Slot q of a half holds the weight of the bf16 value whose 15-bit magnitude field is
@@ -123,15 +135,31 @@ struct RowStat {
 // ln x for finite x > 0 in fp64 (the resolve's few logarithms).
 __device__ __forceinline__ double ln(double x) { return log(x); }
 
+// Where the resolve finds its inputs: the sequence's pass-1 partials (staged in LDS when
+// they fit, else in the workspace), and its first kRowsLds draft tokens and kRowsLds + 1
+// uniforms (LDS; later ones are read from memory).
+struct ResolveIn {
+    const RowPartial* parts;  // [R][nchunk1] of the sequence
+    const int32_t* xs;        // LDS tokens
+    const float* us;          // LDS uniforms
+    const int32_t* x;         // tokens in memory
+    const float* u;           // uniforms in memory (null for greedy-only calls)
+    __device__ __forceinline__ int token(int t) const { return t < kRowsLds ? xs[t] : x[t]; }
+    __device__ __forceinline__ float uniform(int t) const { return t <= kRowsLds ? us[t] : u[t]; }
+};
+
 // Row i (0..K_b target rows, K_b+1..2K_b draft rows) of sequence b from its pass-1 chunk
-// partials.  Greedy: max and lowest index (chunks in order, strict comparison keeps the
-// earlier chunk on ties).  Sampled: max m and S from partials in the 2^((z - m_c) * c2) form.
-__device__ __forceinline__ RowStat merge_row(const VerifyArgs& a, int b, const SeqRows& s, int i,
-                                             bool sampled, float c2, const double* tab) {
+// partials, by one thread.  Greedy: max and lowest index (chunks in order, strict
+// comparison keeps the earlier chunk on ties).  Sampled: max m and S = the chunks' sums
+// rebased from their own maxima to m, 2^((m_c - m) c2) in fp64, added in chunk order;
+// `terms` (or null) holds those rebased sums, computed beforehand one per thread.
+__device__ __forceinline__ RowStat merge_row(const VerifyArgs& a, const SeqRows& s, const ResolveIn& in,
+                                             int i, bool sampled, float c2, const double* tab,
+                                             const double* terms) {
     const bool is_target = i <= s.K;
     const int t = is_target ? i : i - s.K - 1;
     const int j = is_target ? t : a.K + 1 + t;  // workspace slot (dense layout, K the bound)
-    const RowPartial* p = a.part1 + ((int64_t)b * a.R + j) * a.nchunk1;
+    const RowPartial* p = in.parts + (int64_t)j * a.nchunk1;
     RowStat r{-INFINITY, 0x7fffffff, 0.0, -INFINITY};
     if (!sampled) {
         bool bad = false;
@@ -150,7 +178,7 @@ __device__ __forceinline__ RowStat merge_row(const VerifyArgs& a, int b, const S
     // the chunk holding this row's draft token recorded the logit there
     int cx = -1;
     if (t < s.K) {
-        const int x = a.tokens[s.d0 + t];
+        const int x = in.token(t);
         if (x >= 0 && x < a.V) cx = x / a.ch1;
     }
     r.zx = -INFINITY;
@@ -159,22 +187,43 @@ __device__ __forceinline__ RowStat merge_row(const VerifyArgs& a, int b, const S
 #pragma unroll 4
     for (int c = 0; c < a.nchunk1; ++c) {
         const RowPartial q = p[c];
-        if (q.s != 0.0) r.S += q.s * exp2_256(((double)q.m - (double)r.m) * ((double)c2 * 256.0), tab);
+        if (q.s != 0.0)
+            r.S += terms ? terms[(int64_t)i * a.nchunk1 + c]
+                         : q.s * exp2_256(((double)q.m - (double)r.m) * ((double)c2 * 256.0), tab);
         if (c == cx) r.zx = __int_as_float(q.idx);
     }
     return r;
 }
 
+// The rebased chunk sum of sampled row i, chunk c (see merge_row).
+__device__ __forceinline__ double chunk_term(const VerifyArgs& a, const SeqRows& s, const ResolveIn& in,
+                                             int i, int c, float c2, const double* tab) {
+    const bool is_target = i <= s.K;
+    const int t = is_target ? i : i - s.K - 1;
+    const int j = is_target ? t : a.K + 1 + t;
+    const RowPartial* p = in.parts + (int64_t)j * a.nchunk1;
+    float m = -INFINITY;
+    for (int cc = 0; cc < a.nchunk1; ++cc) m = nmax(m, p[cc].m);
+    const RowPartial q = p[c];
+    return q.s != 0.0 ? q.s * exp2_256(((double)q.m - (double)m) * ((double)c2 * 256.0), tab) : 0.0;
+}
+
 // The resolve of sequence b by the whole workgroup of NT threads.  write: also write the
 // outputs (all but the drawn token of a sampled sequence, and its status).  Returns the
-// same SeqDesc in every thread.  Contains __syncthreads().
-template <typename E, int NT = kThreads>
-__device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool write, const double* tab) {
+// same SeqDesc in every thread, without the sign bracket of a residual draw (tau_lo,
+// tau_hi; see desc_bracket).  Contains __syncthreads().
+template <typename E, int NT>
+__device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool write, const double* tab,
+                                               double& St, double& Sd) {
     constexpr int NW = NT / 64;
     __shared__ RowStat rows[kRowsLds];
+    __shared__ RowPartial parts[kPartsLds];
+    __shared__ double terms[kPartsLds];
+    __shared__ int32_t xs[kRowsLds];
+    __shared__ float us[kRowsLds + 1];
     __shared__ int shi[NW];
-    __shared__ SeqDesc sd;
     const int tid = threadIdx.x;
+    St = Sd = 0.0;
     const SeqRows s = seq_rows(a, b);
     if (s.K < 0) {
         // packed offsets that do not describe a sequence: nothing of it can be located
@@ -188,36 +237,68 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
     }
     const int K = s.K, V = a.V;
     const float T = a.temperature ? a.temperature[b] : 0.0f;
+    // every load of the resolve goes out at once: the partials of all the sequence's
+    // workspace rows (used or not), its tokens and uniforms (greedy sequences of a
+    // sampled call read their uniforms too, unused)
+    ResolveIn in;
+    in.x = a.tokens + s.d0;
+    in.u = a.uniforms ? a.uniforms + s.t0 : nullptr;
+    in.xs = xs;
+    in.us = us;
+    const int nparts = a.R * a.nchunk1;
+    const RowPartial* src = a.part1 + (int64_t)b * nparts;
+    const bool staged = nparts <= kPartsLds;
+    in.parts = staged ? parts : src;
+    if (staged) {
+        // two 16-byte loads in flight per thread (indices clamped, stores guarded)
+        const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+        u32x4* d4 = reinterpret_cast<u32x4*>(parts);
+        for (int i0 = 0; i0 < nparts; i0 += 2 * NT) {
+            const int i1 = i0 + tid, i2 = i0 + NT + tid;
+            const u32x4 q1 = s4[min(i1, nparts - 1)];
+            const u32x4 q2 = s4[min(i2, nparts - 1)];
+            if (i1 < nparts) d4[i1] = q1;
+            if (i2 < nparts) d4[i2] = q2;
+        }
+    }
+    if (tid < K && tid < kRowsLds) xs[tid] = in.x[tid];
+    if (in.u && tid <= K && tid <= kRowsLds) us[tid] = in.u[tid];
+    __syncthreads();
     const bool sampled = !(T == 0.0f);
-    const int32_t* x = a.tokens + s.d0;
-    const float* u = sampled ? a.uniforms + s.t0 : nullptr;
     const float c2 = sampled ? (float)(kLog2eD / (double)T) : 0.0f;
 
-    // tokens and uniforms (the logits at the tokens come with the pass-1 partials)
-    int xt = 0;
-    float ut = 0.5f;
     int err = 0;
-    if (tid < K) xt = x[tid];
-    if (sampled && tid <= K) ut = u[tid];
     for (int t = tid; t < K; t += NT) {
-        const int v = x[t];
+        const int v = in.token(t);
         if (v < 0 || v >= V) err |= kSeqErrToken;
     }
     if (sampled)
         for (int t = tid; t <= K; t += NT) {
-            const float v = u[t];
+            const float v = in.uniform(t);
             if (!(v >= 0.0f && v < 1.0f)) err |= kSeqErrUniform;
         }
     if (tid == 0 && temperature_bad(T)) err |= kSeqErrTemperature;
-    // row statistics (draft rows only for sampled sequences)
+    // row statistics (draft rows only for sampled sequences): with the partials in LDS
+    // the rebasing exponentials of all (row, chunk) pairs first, one per thread, then one
+    // thread per row
     const int nrows = sampled ? 2 * K + 1 : K + 1;
+    const bool by_pair = staged && sampled && nrows <= kRowsLds;
+    if (by_pair) {
+        for (int q = tid; q < nrows * a.nchunk1; q += NT) {
+            const int i = q / a.nchunk1;
+            terms[q] = chunk_term(a, s, in, i, q - i * a.nchunk1, c2, tab);
+        }
+        __syncthreads();
+    }
     for (int i = tid; i < nrows; i += NT) {
-        const RowStat r = merge_row(a, b, s, i, sampled, c2, tab);
+        const RowStat r = merge_row(a, s, in, i, sampled, c2, tab, by_pair ? terms : nullptr);
         if (row_bad(r.m, sampled)) err |= kSeqErrLogit;
         if (i < kRowsLds) rows[i] = r;
     }
     err = block_or<NW>(err, shi);  // also orders the rows[] writes before the reads below
-    auto row = [&](int i) -> RowStat { return i < kRowsLds ? rows[i] : merge_row(a, b, s, i, sampled, c2, tab); };
+    auto row = [&](int i) -> RowStat {
+        return i < kRowsLds ? rows[i] : merge_row(a, s, in, i, sampled, c2, tab, nullptr);
+    };
 
     int32_t* tok = a.out_tokens + s.t0;
     float* op = a.out_p ? a.out_p + s.d0 : nullptr;
@@ -239,26 +320,48 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
         return d;
     }
 
-    // the first position that fails
+    // the first position that fails.  With every row in LDS the tests and the reported
+    // p, q go to separate threads; otherwise one thread per position (rows past kRowsLds
+    // are merged again by the thread that needs them)
     const double c256 = sampled ? 256.0 * kLog2eD / (double)T : 0.0;
+    const bool all_lds = nrows <= kRowsLds;
     int first = K;
-    for (int t = tid; t < K; t += NT) {
-        if (t >= NT) {  // K > NT: the early loads above covered t < NT only
-            xt = x[t];
-            if (sampled) ut = u[t];
-        }
-        if (!sampled) {
-            if (row(t).idx != xt) first = min(first, t);
+    if (!sampled) {
+        for (int t = tid; t < K; t += NT) {
             if (write && op) op[t] = __builtin_nanf("");
             if (write && oq) oq[t] = __builtin_nanf("");
-        } else {
-            const RowStat rt = row(t), rd = row(K + 1 + t);
+        }
+        for (int t = tid; t < K; t += NT)
+            if (row(t).idx != in.token(t)) first = min(first, t);
+    } else if (all_lds) {
+        for (int q = tid; q < 3 * K; q += NT) {
+            const int kind = q / K, t = q - kind * K;
+            const RowStat rt = rows[t], rd = rows[K + 1 + t];
             // p = 2^((zx - mt) c2) / St and q = 2^((dx - md) c2) / Sd
+            const double ex = (double)rt.zx - (double)rt.m, dxm = (double)rd.zx - (double)rd.m;
+            if (kind == 1) {
+                if (write && op) op[t] = (float)(exp2_256(ex * c256, tab) / rt.S);
+            } else if (kind == 2) {
+                if (write && oq) oq[t] = (float)(exp2_256(dxm * c256, tab) / rd.S);
+            } else {
+                // r < p/q, i.e. r St < Sd 2^((ex - dxm) c2); q = 0 with p > 0 accepts,
+                // p = 0 rejects (2^y saturates to inf above and to 0 below the fp64 range)
+                const float ut = in.uniform(t);
+                bool accept;
+                if (rt.zx == -INFINITY) accept = false;
+                else if (rd.zx == -INFINITY) accept = true;
+                else if (ut == 0.0f) accept = true;
+                else accept = (double)ut * rt.S < rd.S * exp2_256((ex - dxm) * c256, tab);
+                if (!accept) first = min(first, t);
+            }
+        }
+    } else {
+        for (int t = tid; t < K; t += NT) {
+            const RowStat rt = row(t), rd = row(K + 1 + t);
             const double ex = (double)rt.zx - (double)rt.m, dxm = (double)rd.zx - (double)rd.m;
             if (write && op) op[t] = (float)(exp2_256(ex * c256, tab) / rt.S);
             if (write && oq) oq[t] = (float)(exp2_256(dxm * c256, tab) / rd.S);
-            // r < p/q, i.e. r St < Sd 2^((ex - dxm) c2); q = 0 with p > 0 accepts, p = 0
-            // rejects (2^y saturates to inf above and to 0 below the fp64 range)
+            const float ut = in.uniform(t);
             bool accept;
             if (rt.zx == -INFINITY) accept = false;
             else if (rd.zx == -INFINITY) accept = true;
@@ -270,43 +373,47 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
     const int n = block_min<NW>(first, shi);
     if (write)
         for (int t = tid; t <= K; t += NT)
-            if (t != n) tok[t] = t < n ? x[t] : -1;
-    if (tid == 0) {
-        SeqDesc d{};
-        d.n = n;
-        d.T = T;
-        d.trow = s.t0 + n;
-        d.drow = s.d0 + n;
-        if (write && a.out_n) a.out_n[b] = n;
-        if (!sampled) {
-            if (write) {
-                tok[n] = row(n).idx;
-                a.out_status[b] = 0;
-            }
-            d.mode = kModeNone;
-        } else {
-            const RowStat rt = row(n);
-            d.mt = rt.m;
-            d.md = rt.m;
-            d.tau_lo = d.tau_hi = 0.0;
-            if (n < K) {
-                const RowStat rd = row(K + 1 + n);
-                d.md = rd.m;
-                d.mode = kModeResidual;
-                const double base = (double)T * ln(rt.S / rd.S) + ((double)rt.m - (double)rd.m);
-                d.tau_hi = base + (double)T * kLnDeltaHi;
-                d.tau_lo = base + (double)T * kLnDeltaLo;
-            } else {
-                d.mode = kModeBonus;
-            }
-            d.u = u[K];
+            if (t != n) tok[t] = t < n ? in.token(t) : -1;
+    // every thread reads the same rows: the descriptor in every thread
+    const RowStat rt = row(n);
+    SeqDesc d{};
+    d.n = n;
+    d.T = T;
+    d.trow = s.t0 + n;
+    d.drow = s.d0 + n;
+    if (write && tid == 0 && a.out_n) a.out_n[b] = n;
+    if (!sampled) {
+        if (write && tid == 0) {
+            tok[n] = rt.idx;
+            a.out_status[b] = 0;
         }
-        sd = d;
+        d.mode = kModeNone;
+        return d;
     }
-    __syncthreads();
-    const SeqDesc d = sd;
-    __syncthreads();
+    d.mt = rt.m;
+    d.md = rt.m;
+    St = rt.S;
+    if (n < K) {
+        const RowStat rd = row(K + 1 + n);
+        d.md = rd.m;
+        Sd = rd.S;
+        d.mode = kModeResidual;
+    } else {
+        d.mode = kModeBonus;
+    }
+    d.u = in.uniform(K);
     return d;
+}
+
+// The sign bracket of a residual draw: [tau_lo, tau_hi] on zt_i - zd_i around the
+// threshold T ln(St/Sd) + mt - md, St and Sd the pass-1 normalisers of the two rows.
+__device__ __forceinline__ void desc_bracket(SeqDesc& d, double St, double Sd) {
+    d.tau_lo = d.tau_hi = 0.0;
+    if (d.mode != kModeResidual) return;
+    const double T = (double)d.T;
+    const double base = T * ln(St / Sd) + ((double)d.mt - (double)d.md);
+    d.tau_hi = base + T * kLnDeltaHi;
+    d.tau_lo = base + T * kLnDeltaLo;
 }
 
 // ------------------------------------------------------------------------------------
@@ -318,6 +425,27 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
 __device__ __forceinline__ uint32_t tab_slot(uint32_t x) {
     const uint32_t t = min(max(x & 0x7fffu, kTabLo), kTabHi);
     return (t - kTabLo) + ((x >> 4) & 0x800u);
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Byte offsets into the table of the two bf16 values packed in x (o0: low half, o1: high
+// half): 8 tab_slot(...) of each, both halves at once with packed 16-bit integer
+// arithmetic (saturating subtract, minimum, shift).
+__device__ __forceinline__ void tab_offsets(uint32_t x, uint32_t& o0, uint32_t& o1) {
+    const u16x2 m = __builtin_bit_cast(u16x2, x & 0x7fff7fffu);
+    const u16x2 lo = {(unsigned short)kTabLo, (unsigned short)kTabLo};
+    const u16x2 top = {(unsigned short)(kTabN + 1), (unsigned short)(kTabN + 1)};
+    u16x2 c = __builtin_elementwise_sub_sat(m, lo);  // magnitude - kTabLo, or 0 below
+    c = __builtin_elementwise_min(c, top);           // kTabN + 1 above
+    c = c << (unsigned short)3;
+    const uint32_t off = __builtin_bit_cast(uint32_t, c) | ((x >> 1) & 0x40004000u);  // + sign half
+    o0 = off & 0xffffu;
+    o1 = off >> 16;
+}
+
+__device__ __forceinline__ double tab_at(const double* wt, uint32_t off) {
+    return *reinterpret_cast<const double*>(reinterpret_cast<const char*>(wt) + off);
 }
 
 // Whether the bf16 value in the low 16 bits of h has a table slot, and that slot.
@@ -408,6 +536,7 @@ __device__ __forceinline__ DrawRows<E> draw_rows(const VerifyArgs& a, int b, con
     return r;
 }
 
+static_assert(sizeof(RowPartial) == sizeof(u32x4), "partials move as 16-byte vectors");
 static_assert(kTabLen == kWtabLen, "workspace slot of the weight table");
 
 // The bf16 weight table of a sequence (kTabLen doubles) for reference r.refA (= r.refB),
@@ -428,14 +557,31 @@ __device__ __forceinline__ void weight_table_write(const DrawRows<E>& r, double*
     }
 }
 
-// Copy a sequence's weight table from the workspace into LDS (16-byte pieces; the caller's
-// next __syncthreads() publishes it).
-__device__ __forceinline__ void weight_table_load(const double* src, double* wt) {
-    const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
-    u32x4* d4 = reinterpret_cast<u32x4*>(wt);
+// A sequence's weight table on its way from the workspace into LDS, in 16-byte pieces:
+// load() puts every load in flight at once, store() writes LDS later (the caller's next
+// __syncthreads() publishes it), so other loads can go out in between.
+template <int NT>
+struct TableCopy {
+    static constexpr int kPieces = kTabLen / 2;
+    static constexpr int kN = (kPieces + NT - 1) / NT;
+    u32x4 v[kN];
+    __device__ __forceinline__ void load(const double* src) {
+        const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
 #pragma unroll
-    for (int k = threadIdx.x; k < kTabLen / 2; k += kThreads) d4[k] = s4[k];
-}
+        for (int k = 0; k < kN; ++k) {
+            const int i = (int)threadIdx.x + k * NT;
+            v[k] = s4[kPieces % NT == 0 ? i : min(i, kPieces - 1)];
+        }
+    }
+    __device__ __forceinline__ void store(double* wt) const {
+        u32x4* d4 = reinterpret_cast<u32x4*>(wt);
+#pragma unroll
+        for (int k = 0; k < kN; ++k) {
+            const int i = (int)threadIdx.x + k * NT;
+            if (kPieces % NT == 0 || i < kPieces) d4[i] = v[k];
+        }
+    }
+};
 
 // Logits at positions i .. i+VEC-1: one 16-byte vector when aligned and inside [.., hi),
 // else element by element with positions at or past hi reading -inf (weight 0).
@@ -591,8 +737,11 @@ __device__ __forceinline__ void fast_word_res(const double* wt, uint32_t xt, uin
     const float D0 = zt0 - zd0, D1 = zt1 - zd1;
     const bool p0 = D0 > th, p1 = D1 > th;
     const bool u0 = !p0 && D0 >= tl, u1 = !p1 && D1 >= tl;
-    const double a0 = wt[tab_slot(xt)], a1 = wt[tab_slot(xt >> 16)];
-    const double b0 = wt[tab_slot(xd)], b1 = wt[tab_slot(xd >> 16)];
+    uint32_t ot0, ot1, od0, od1;
+    tab_offsets(xt, ot0, ot1);
+    tab_offsets(xd, od0, od1);
+    const double a0 = tab_at(wt, ot0), a1 = tab_at(wt, ot1);
+    const double b0 = tab_at(wt, od0), b1 = tab_at(wt, od1);
     if (__any(u0 || u1)) {
         if (s.key != s.key) {  // the first undecided difference becomes the key
             const uint64_t m = __ballot(u0 || u1);
@@ -621,8 +770,10 @@ __device__ __forceinline__ void fast_word_res(const double* wt, uint32_t xt, uin
 }
 
 __device__ __forceinline__ void fast_word_bonus(const double* wt, uint32_t xt, SweepAcc& s) {
-    s.sp += wt[tab_slot(xt)];
-    s.sp += wt[tab_slot(xt >> 16)];
+    uint32_t o0, o1;
+    tab_offsets(xt, o0, o1);
+    s.sp += tab_at(wt, o0);
+    s.sp += tab_at(wt, o1);
     asm volatile("" ::"v"(s.sp));
 }
 
@@ -1002,7 +1153,7 @@ __device__ __forceinline__ void block_sum2_or(double& x, double& y, int& o, doub
 // bkt[k * kBuckets ...]), loaded once; one reduction, one scan, one segment search.
 template <typename E, int NT, int PER>
 __device__ __forceinline__ void final_seq_small(const VerifyArgs& a, DrawRows<E> r, const SeqDesc& d, int b,
-                                                const DrawPartial* part, const Bucket* bkt, int nsub, int L) {
+                                                DrawPartial dp, Bucket bk0, const Bucket* bkt, int nsub, int L) {
     constexpr int NW = NT / 64;
     __shared__ double shd[2 * NW];
     __shared__ int shi[NW];
@@ -1011,8 +1162,8 @@ __device__ __forceinline__ void final_seq_small(const VerifyArgs& a, DrawRows<E>
     const double u = (double)d.u;
     int status = 0;
 
-    DrawPartial dp{};
-    if (tid < nsub) dp = part[tid];
+    // dp, bk0: this thread's segment partial and its first bucket (thread tid < nsub)
+    if (tid >= nsub) dp = DrawPartial{};
     double sp = dp.sp, sq = dp.sq;
     int over = dp.nbkt > kBuckets;
     block_sum2_or<NW>(sp, sq, over, shd, shi);
@@ -1047,7 +1198,8 @@ __device__ __forceinline__ void final_seq_small(const VerifyArgs& a, DrawRows<E>
                 v = dp.A * r.inv_sp - dp.B * r.inv_sq;
                 const Bucket* bk = bkt + tid * kBuckets;
                 for (int q = 0; q < dp.nbkt; ++q) {
-                    const double t = bk[q].a * r.inv_sp - bk[q].b * r.inv_sq;
+                    const Bucket bq = q == 0 ? bk0 : bk[q];
+                    const double t = bq.a * r.inv_sp - bq.b * r.inv_sq;
                     if (t > 0.0) v += t;
                 }
                 v = v > 0.0 ? v : 0.0;
@@ -1087,10 +1239,11 @@ __device__ __forceinline__ void final_seq_small(const VerifyArgs& a, DrawRows<E>
 }
 
 // The draw of sequence b from the partials of all its segments, by one workgroup.
-template <typename E>
+template <typename E, int NT>
 __device__ __forceinline__ void final_seq(const VerifyArgs& a, DrawRows<E> r, const SeqDesc& d, int b) {
-    __shared__ double shd[kWaves];
-    __shared__ int shi[kWaves];
+    constexpr int NW = NT / 64;
+    __shared__ double shd[NW];
+    __shared__ int shi[NW];
     __shared__ double sh_base;
     const int tid = threadIdx.x;
     const int nsub = a.nseg;
@@ -1102,15 +1255,15 @@ __device__ __forceinline__ void final_seq(const VerifyArgs& a, DrawRows<E> r, co
     // threshold T ln(S_p/S_q) + refA - refB lies well inside the bracket
     double sp = 0.0, sq = 0.0;
     int over = 0;
-    for (int k = tid; k < nsub; k += kThreads) {
+    for (int k = tid; k < nsub; k += NT) {
         const DrawPartial dp = a.part2[e0 + k];
         sp += dp.sp;
         sq += dp.sq;
         over |= dp.nbkt > kBuckets;
     }
-    sp = block_sum(sp, shd);
-    sq = block_sum(sq, shd);
-    over = block_or(over, shi);
+    sp = block_sum<NW>(sp, shd);
+    sq = block_sum<NW>(sq, shd);
+    over = block_or<NW>(over, shi);
     bool exact_ok = sp > 0.0;
     if (r.residual) {
         exact_ok = exact_ok && sq > 0.0 && !over;
@@ -1129,7 +1282,7 @@ __device__ __forceinline__ void final_seq(const VerifyArgs& a, DrawRows<E> r, co
     int y;
     if (!exact_ok) {
         // too many undecided positions, or the estimate was off: one exact sweep
-        y = block_search(r, 0, a.V, 0.0, 0.0, true, u);
+        y = block_search<E, NT>(r, 0, a.V, 0.0, 0.0, true, u);
     } else {
         // mass of sub-chunk k in the units of the draw: its certain part and, per bucket of
         // undecided positions (one residual sign each), the bucket's residual if positive
@@ -1145,11 +1298,11 @@ __device__ __forceinline__ void final_seq(const VerifyArgs& a, DrawRows<E> r, co
             return w > 0.0 ? w : 0.0;
         };
         double carry = 0.0;
-        for (int t0 = 0; t0 < nsub; t0 += kThreads) {
+        for (int t0 = 0; t0 < nsub; t0 += NT) {
             const int k = t0 + tid;
             const double v = k < nsub ? mass(k) : 0.0;
             double tot;
-            block_exclusive_scan(v, tot, shd);
+            block_exclusive_scan<NW>(v, tot, shd);
             carry += tot;
         }
         const double total = carry;
@@ -1159,14 +1312,14 @@ __device__ __forceinline__ void final_seq(const VerifyArgs& a, DrawRows<E> r, co
             const double target = u * total;
             carry = 0.0;
             int hit = 0x7fffffff;
-            for (int t0 = 0; t0 < nsub; t0 += kThreads) {
+            for (int t0 = 0; t0 < nsub; t0 += NT) {
                 const int k = t0 + tid;
                 const double v = k < nsub ? mass(k) : 0.0;
                 double tot;
-                const double ex = block_exclusive_scan(v, tot, shd);
+                const double ex = block_exclusive_scan<NW>(v, tot, shd);
                 const double incl = carry + ex + v;
                 // a sub-chunk without mass never holds the first crossing (guards rounding)
-                const int f = block_min((k < nsub && v > 0.0 && incl > target) ? k : 0x7fffffff, shi);
+                const int f = block_min<NW>((k < nsub && v > 0.0 && incl > target) ? k : 0x7fffffff, shi);
                 if (f != 0x7fffffff) {
                     if (k == f) sh_base = carry + ex;
                     __syncthreads();
@@ -1179,11 +1332,11 @@ __device__ __forceinline__ void final_seq(const VerifyArgs& a, DrawRows<E> r, co
             if (hit == 0x7fffffff) {
                 // rounding put u*W past every prefix: the last sub-chunk with mass, last index
                 int last = -1;
-                for (int t0 = 0; t0 < nsub; t0 += kThreads) {
+                for (int t0 = 0; t0 < nsub; t0 += NT) {
                     const int k = t0 + tid;
                     if (k < nsub && mass(k) > 0.0) last = max(last, k);
                 }
-                hit = block_max(last, shi);
+                hit = block_max<NW>(last, shi);
                 tgt = INFINITY;
                 status |= kSeqNoteFallback;
             } else {
@@ -1191,14 +1344,14 @@ __device__ __forceinline__ void final_seq(const VerifyArgs& a, DrawRows<E> r, co
             }
             int lo, hi;
             seg_range(a.V, kSeg, hit, lo, hi);
-            y = block_search(r, lo, hi, base, tgt, false, u);
+            y = block_search<E, NT>(r, lo, hi, base, tgt, false, u);
         }
     }
     if (y < 0) {
         // residual without fp64 mass (exact arithmetic rules it out): draw from p_n
         status |= kSeqNoteFallback;
         r.residual = 0;
-        y = block_search(r, 0, a.V, 0.0, 0.0, true, u);
+        y = block_search<E, NT>(r, 0, a.V, 0.0, 0.0, true, u);
     }
     if (tid == 0) {
         a.out_tokens[d.trow] = y;
@@ -1222,16 +1375,21 @@ static_assert(sizeof(SeqDesc) <= kSeqDescBytes && kSeqDescBytes % alignof(SeqDes
 // token and status), the sequence's SeqDesc and, for bf16 draws with one reference, the
 // sequence's weight table.
 template <typename E>
-__global__ __launch_bounds__(kThreads) void resolve_kernel(VerifyArgs a, int b0) {
+__global__ __launch_bounds__(kResolveThreads) void resolve_kernel(VerifyArgs a, int b0) {
     __shared__ double tab[kExpTable];
     const int b = b0 + (int)blockIdx.x;
     exp2_table_init(tab);
-    const SeqDesc d = resolve_seq<E>(a, b, true, tab);
-    if (threadIdx.x == 0) reinterpret_cast<SeqDesc*>(a.desc)[b] = d;
+    double St, Sd;
+    SeqDesc d = resolve_seq<E, kResolveThreads>(a, b, true, tab, St, Sd);
+    // thread 0 finishes the descriptor while the others start on the weight table
+    if (threadIdx.x == 0) {
+        desc_bracket(d, St, Sd);
+        reinterpret_cast<SeqDesc*>(a.desc)[b] = d;
+    }
     if constexpr (sizeof(E) == 2) {
         if (d.mode == kModeNone) return;
-        const DrawRows<E> r = draw_rows<E>(a, b, d, tab, nullptr);
-        if (r.one_ref) weight_table_write(r, a.wtab + (int64_t)b * kWtabLen);
+        const DrawRows<E> r = draw_rows<E>(a, b, d, tab, nullptr);  // the bracket is not used
+        if (r.one_ref) weight_table_write<E, kResolveThreads>(r, a.wtab + (int64_t)b * kWtabLen);
     }
 }
 
@@ -1239,8 +1397,9 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(VerifyArgs a, int b0)
 // [c spc, (c + 1) spc) of the draw row(s), each wave a contiguous run of them, into
 // per-segment partials.
 template <typename E>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SV_DRAW_WAVES)))
+__global__ __launch_bounds__(kSweepThreads) __attribute__((amdgpu_waves_per_eu(SV_DRAW_WAVES)))
 void sweep_kernel(VerifyArgs a, int b0) {
+    constexpr int NW = kSweepThreads / 64;
     __shared__ double tab[kExpTable];
     __shared__ double wt[DrawLds<E>::kWt];
     const int b = b0 + (int)(blockIdx.x / (unsigned)a.nchunk2);
@@ -1253,7 +1412,7 @@ void sweep_kernel(VerifyArgs a, int b0) {
     acc.lane = threadIdx.x & 63;
     acc.reset();
     const int c0 = c * a.spc, c1 = min(a.nseg, c0 + a.spc);
-    const int per = (c1 - c0 + kWaves - 1) / kWaves;
+    const int per = (c1 - c0 + NW - 1) / NW;
     const int s0 = min(c1, c0 + w * per), s1 = min(c1, s0 + per);
     DrawPartial* part = a.part2 + (int64_t)b * a.nseg;
     Bucket* bkt = a.bkt + (int64_t)b * a.nseg * kBuckets;
@@ -1268,7 +1427,9 @@ void sweep_kernel(VerifyArgs a, int b0) {
                 if (r.residual) first_span<true>(r, lo, acc.lane, f);
                 else first_span<false>(r, lo, acc.lane, f);
             }
-            weight_table_load(a.wtab + (int64_t)b * kWtabLen, wt);
+            TableCopy<kSweepThreads> tc;
+            tc.load(a.wtab + (int64_t)b * kWtabLen);
+            tc.store(wt);
             exp2_table_init(tab);  // its barrier also publishes wt
             if (s0 < s1) {
                 if (r.residual) sweep_wave_tab<true>(r, lo, hi, kSeg, part, bkt, acc, f, have_first);
@@ -1284,32 +1445,44 @@ void sweep_kernel(VerifyArgs a, int b0) {
 }
 
 // grid = sequences: the draw of each sampled sequence from the partials of all its segments.
-// Weights come from the fp64 exponential, which gives exactly the sweep's table values
-// (the table holds the same function of the same operands).
+// Weights as in the sweep: the sequence's table in LDS for bf16 values it covers, the fp64
+// exponential otherwise.
 template <typename E>
-__global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a, int b0) {
+__global__ __launch_bounds__(kFinalThreads) void final_kernel(VerifyArgs a, int b0) {
     __shared__ double tab[kExpTable];
+    __shared__ double wt[DrawLds<E>::kWt];
     const int b = b0 + (int)blockIdx.x;
+    // bf16: the sequence's weight table comes in with the descriptor (whether it holds a
+    // table is known once the descriptor is: unused otherwise)
+    TableCopy<kFinalThreads> tc;
+    if constexpr (sizeof(E) == 2) tc.load(a.wtab + (int64_t)b * kWtabLen);
     const SeqDesc d = reinterpret_cast<const SeqDesc*>(a.desc)[b];
+    // the segment partials and first buckets load together with the descriptor
+    const bool small = a.nseg <= kFinalThreads;
+    const DrawPartial* part = a.part2 + (int64_t)b * a.nseg;
+    const Bucket* bkt = a.bkt + (int64_t)b * a.nseg * kBuckets;
+    const int k = min((int)threadIdx.x, a.nseg - 1);
+    const DrawPartial dp = part[k];
+    const Bucket bk0 = bkt[k * kBuckets];
     if (d.mode == kModeNone) return;  // whole workgroup
-    exp2_table_init(tab);
-    const DrawRows<E> r = draw_rows<E>(a, b, d, tab, nullptr);
-    if (a.nseg <= kThreads)
-        final_seq_small<E, kThreads, kSeg / kThreads>(a, r, d, b, a.part2 + (int64_t)b * a.nseg,
-                                                      a.bkt + (int64_t)b * a.nseg * kBuckets, a.nseg, kSeg);
+    if constexpr (sizeof(E) == 2) tc.store(wt);
+    exp2_table_init(tab);  // its barrier also publishes wt
+    const DrawRows<E> r = draw_rows<E>(a, b, d, tab, sizeof(E) == 2 ? wt : nullptr);
+    if (small)
+        final_seq_small<E, kFinalThreads, kSeg / kFinalThreads>(a, r, d, b, dp, bk0, bkt, a.nseg, kSeg);
     else
-        final_seq<E>(a, r, d, b);
+        final_seq<E, kFinalThreads>(a, r, d, b);
 }
 
 }  // namespace
 
 template <typename E>
 void launch_all(const VerifyArgs& a, int b0, int b1, hipStream_t s) {
-    hipLaunchKernelGGL(resolve_kernel<E>, dim3((unsigned)(b1 - b0)), dim3(kThreads), 0, s, a, b0);
+    hipLaunchKernelGGL(resolve_kernel<E>, dim3((unsigned)(b1 - b0)), dim3(kResolveThreads), 0, s, a, b0);
     if (!a.temperature) return;  // greedy only: the resolve is everything
     const unsigned blocks = (unsigned)((int64_t)(b1 - b0) * a.nchunk2);
-    hipLaunchKernelGGL(sweep_kernel<E>, dim3(blocks), dim3(kThreads), 0, s, a, b0);
-    hipLaunchKernelGGL(final_kernel<E>, dim3((unsigned)(b1 - b0)), dim3(kThreads), 0, s, a, b0);
+    hipLaunchKernelGGL(sweep_kernel<E>, dim3(blocks), dim3(kSweepThreads), 0, s, a, b0);
+    hipLaunchKernelGGL(final_kernel<E>, dim3((unsigned)(b1 - b0)), dim3(kFinalThreads), 0, s, a, b0);
 }
 
 int launch_draw(const VerifyArgs& a, int bf16, int b0, int b1, void* stream) {
