@@ -91,9 +91,14 @@ constexpr int kTabLen = 2 * kTabHalf;
 // 16-byte vectors per row whose loads are in flight together per lane; a span is what one
 // wave covers with them.
 #ifndef SV_SWEEP_G
-#define SV_SWEEP_G 2
+#define SV_SWEEP_G 1
 #endif
 constexpr int kG = SV_SWEEP_G;
+// Words of the fast path between scheduling fences (their table reads may overlap).
+#ifndef SV_SWEEP_WPF
+#define SV_SWEEP_WPF 4
+#endif
+constexpr int kWordsPerFence = SV_SWEEP_WPF;
 constexpr int kSpan16 = 64 * kG * 8;
 static_assert(kSeg % kSpan16 == 0 && kSeg / kSpan16 <= 32, "draw segments are whole spans of bf16 vectors");
 
@@ -883,7 +888,7 @@ __device__ __forceinline__ void sweep_wave_tab(const DrawRows<uint16_t>& r, int 
                 for (int q = 0; q < 4; ++q) {
                     if (Residual) fast_word_res(r.wt, xt4[q], xd4[q], th, tl, acc, odd);
                     else fast_word_bonus(r.wt, xt4[q], acc);
-                    __builtin_amdgcn_sched_barrier(0);
+                    if ((q + 1) % kWordsPerFence == 0) __builtin_amdgcn_sched_barrier(0);
                 }
             }
             if (__any(odd || acc.sp != acc.sp || acc.sq != acc.sq)) {  // rare
