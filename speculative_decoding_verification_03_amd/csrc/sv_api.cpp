@@ -245,7 +245,22 @@ sv_status sv_sample(const void* logits, int dtype, const float* uniforms,
     const sv::VerifyArgs a = make_args(logits, nullptr, nullptr, uniforms, temperature, B, 0, V,
                                        1, L, workspace, out_tokens, nullptr, nullptr, nullptr,
                                        out_status);
-    return launch(a, dtype == SV_DTYPE_BF16, stream);
+    const int bf16 = dtype == SV_DTYPE_BF16;
+    if ((int64_t)V > (int64_t)sv::kSampleMaxSeg * sv::kSeg) return launch(a, bf16, stream);
+    // rows of at most kSampleMaxSeg segments: one workgroup per row does everything
+    // (timed as the first phase)
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    if (g_prof.on) {
+        for (auto& e : ev) e = g_prof.next();
+        g_prof.calls++;
+        g_prof.record(ev[0], stream);
+    }
+    if (sv::launch_sample(a, bf16, stream) != 0) return SV_ERR_HIP;
+    if (g_prof.on) {
+        g_prof.record(ev[1], stream);
+        g_prof.record(ev[2], stream);
+    }
+    return SV_OK;
 }
 
 sv_status spec_verify_greedy(const void* target_logits, int dtype,

@@ -83,6 +83,9 @@ constexpr int kTargetBlocks2 = SV_TARGET_BLOCKS2;
 #define SV_SWEEP_THREADS 256
 #endif
 constexpr int kSweepThreads = SV_SWEEP_THREADS;
+// The one-workgroup-per-row sampler: threads, and the longest row it takes (segments).
+constexpr int kSampleThreads = 1024;
+constexpr int kSampleMaxSeg = kSampleThreads;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -187,6 +190,8 @@ int launch_draw(const VerifyArgs& a, int bf16, int b0, int b1, void* stream);
 int launch_uniforms(uint64_t seed, uint64_t domain, uint64_t step, int B, int K, float* u,
                     void* stream);
 int launch_tree(const TreeArgs& a, void* stream);
+// sv_sample with at most kSampleMaxSeg segments per row: one workgroup per row.
+int launch_sample(const VerifyArgs& a, int bf16, void* stream);
 int launch_tree_mask(const TreeArgs& a, void* stream);
 // Packed layout: u[cu[b] + b + t] for t <= K_b of each sequence with valid offsets.
 int launch_uniforms_packed(uint64_t seed, uint64_t domain, uint64_t step, int B, int K,

@@ -246,6 +246,21 @@ __device__ __forceinline__ float block_nmax(float v, float* sh) {
     return t;
 }
 
+// Maximum of floats (fmaxf: a NaN operand is ignored).
+template <int NW = kWaves>
+__device__ __forceinline__ float block_max_f(float v, float* sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    if (lane == 0) sh[w] = v;
+    __syncthreads();
+    float t = sh[0];
+#pragma unroll
+    for (int k = 1; k < NW; ++k) t = fmaxf(t, sh[k]);
+    __syncthreads();
+    return t;
+}
+
 template <int NW = kWaves>
 __device__ __forceinline__ int block_min(int v, int* sh) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;

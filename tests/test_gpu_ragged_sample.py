@@ -193,7 +193,9 @@ def sample_as_verify(r):
 
 
 @pytest.mark.parametrize("B,V,dt", [(64, 152064, torch.bfloat16), (37, 1000, torch.float32),
-                                    (20, 131073, torch.float32), (3, 1, torch.bfloat16)])
+                                    (20, 131073, torch.float32), (3, 1, torch.bfloat16),
+                                    (7, 4096 * 1024, torch.bfloat16),    # longest one-workgroup row
+                                    (2, 4096 * 1024 + 5, torch.bfloat16)])  # the multi-kernel path
 def test_sample_parity(dev, B, V, dt):
     say(f"sampler B={B} V={V} {dt}")
     t = Tally()
