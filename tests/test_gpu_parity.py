@@ -181,6 +181,9 @@ EDGE = [
     (2, 6, 40000, torch.bfloat16, [1.0, 0.8]),           # several chunks per row
     (1, 12, 70001, torch.bfloat16, [0.6]),               # long K, several chunks, ragged
     (6, 3, 130000, torch.float32, [1.0, 0.0, 0.05, 1.2, 0.0, 0.5]),
+    (3, 40, 3000, torch.bfloat16, [1.0, 0.0, 0.3]),      # 2K+1 rows past the resolve's LDS rows
+    (2, 100, 500, torch.float32, [0.8, 0.0]),            # tokens and uniforms past them too
+    (1, 8, 4194307, torch.bfloat16, [0.9]),              # partials too many to stage in LDS
 ]
 
 
