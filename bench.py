@@ -377,7 +377,10 @@ def main():
                                        f"{'bf16' if c['dtype'] == torch.bfloat16 else 'fp32'} "
                                        "draft logits (workload-4 recipe), T~U[0,1.2], 25% greedy")
         result["config"]["K"] = 0
+        result["config"]["arithmetic"] = "fp64 weights from an LDS table of the row's bf16 values"
         result["roofline"]["traffic"] = None
+        result["roofline"]["kernel"] = ("sample_kernel (one workgroup per row; algorithmic bytes: "
+                                        "each row read once)")
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         if args.path == "tree":
