@@ -2,10 +2,11 @@
 """Benchmark of the batched speculative-sampling verify step on one MI355X.
 
 One step = the whole hot path over one batch resident in HBM: the counter-based
-uniforms (sv_fill_uniforms) and spec_verify (pass 1 row streaming; pass 2 resolve and
-categorical draws).  Default workload: B=256 sequences, K=8 drafted tokens,
-V=152064 bf16 logits, Zipf(1.1)-offset target logits, T ~ U[0, 1.2] with a quarter of
-the sequences greedy (T = 0).  Prints one JSON line.
+uniforms and the verify (pass 1 row streaming; pass 2 resolve and categorical draws), by
+spec_verify_philox (the uniforms come from the first workgroups of pass 1; with
+--separate-uniforms: sv_fill_uniforms, then spec_verify).  Default workload: B=256
+sequences, K=8 drafted tokens, V=152064 bf16 logits, Zipf(1.1)-offset target logits,
+T ~ U[0, 1.2] with a quarter of the sequences greedy (T = 0).  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload 4] [--no-cpu-baseline]
                     [--path verify|ragged|sample|tree]
@@ -165,6 +166,9 @@ def main():
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="verify", choices=["verify", "ragged", "sample", "tree"])
+    ap.add_argument("--separate-uniforms", action="store_true",
+                    help="verify path: sv_fill_uniforms, then spec_verify (default: "
+                         "spec_verify_philox, which generates them in the same launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain device-to-device copy of COPY_BYTES, so that a "
                          "counter profile of this command holds a kernel of known traffic")
@@ -200,12 +204,19 @@ def main():
     positions = B * (K + 1)
     p1_bytes = W.logit_bytes(B, K, V, c["dtype"], temps)
 
+    for k in range(nsets):
+        outs[k]["uniforms"] = u[k]
+
     def step(i):
         k = i % nsets
         x = sets[k]
-        sv.sv_fill_uniforms(seed, 0, i, B, K, out=u[k])
-        sv.spec_verify(x["target"], x["draft"], x["tokens"], u[k], x["temperature"],
-                       out=outs[k], workspace=ws)
+        if args.separate_uniforms:
+            sv.sv_fill_uniforms(seed, 0, i, B, K, out=u[k])
+            sv.spec_verify(x["target"], x["draft"], x["tokens"], u[k], x["temperature"],
+                           out=outs[k], workspace=ws)
+        else:
+            sv.spec_verify_philox(x["target"], x["draft"], x["tokens"], x["temperature"], seed, 0,
+                                  i, out=outs[k], workspace=ws)
 
     if args.path == "tree":
         trees = [W.make_tree_inputs(device=dev, V=V, dtype=c["dtype"], step=s_)

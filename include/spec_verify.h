@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 2
+#define SV_ABI_VERSION 3
 
 /* Host-side return codes. */
 typedef enum sv_status {
@@ -124,6 +124,22 @@ sv_status spec_verify(const void* target_logits, const void* draft_logits, int d
                       int32_t* out_tokens, int32_t* out_accept_len,
                       float* out_p, float* out_q, int32_t* out_status,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify with uniforms from the counter generator: the same as
+ *   sv_fill_uniforms(seed, domain, step, B, K, uniforms_out, stream);
+ *   spec_verify(..., uniforms_out, ...);
+ * with one launch fewer (the first workgroups of the logit-streaming kernel write the
+ * uniforms).  uniforms_out: device, [B][K+1] fp32, written by the call, owned by the
+ * caller.  Every other argument as for spec_verify.  Outputs are bit-identical to the
+ * two calls above.
+ */
+sv_status spec_verify_philox(const void* target_logits, const void* draft_logits, int dtype,
+                             const int32_t* draft_tokens, const float* temperature,
+                             int B, int K, int V, uint64_t seed, uint64_t domain, uint64_t step,
+                             float* uniforms_out, int32_t* out_tokens, int32_t* out_accept_len,
+                             float* out_p, float* out_q, int32_t* out_status,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Greedy verify (temperature 0 for every sequence): accept x_t while the lowest-index

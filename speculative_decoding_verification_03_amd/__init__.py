@@ -11,7 +11,7 @@ import os
 __all__ = [
     "LibraryMissing", "SpecVerifyError", "lib", "lib_path",
     "sv_abi_version", "sv_status_string", "sv_workspace_bytes",
-    "spec_verify", "spec_verify_greedy", "sv_fill_uniforms", "Workspace",
+    "spec_verify", "spec_verify_greedy", "sv_fill_uniforms", "Workspace", "spec_verify_philox",
     "spec_verify_ragged", "spec_verify_greedy_ragged", "sv_fill_uniforms_ragged", "sv_sample",
     "spec_verify_tree_greedy", "sv_tree_attention_mask", "SV_TREE_MAX_NODES",
     "sv_profile_begin", "sv_profile_end",
@@ -65,6 +65,9 @@ def lib():
     L.spec_verify.restype = i32
     L.spec_verify.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32,
                               vp, vp, vp, vp, vp, vp, sz, vp]
+    L.spec_verify_philox.restype = i32
+    L.spec_verify_philox.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, u64, u64, u64, vp,
+                                     vp, vp, vp, vp, vp, vp, sz, vp]
     L.spec_verify_greedy.restype = i32
     L.spec_verify_greedy.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.sv_fill_uniforms.restype = i32
@@ -211,6 +214,41 @@ def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature
         _ptr(ws), ws.numel(), _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify")
+    return out
+
+
+def spec_verify_philox(target_logits, draft_logits, draft_tokens, temperature, seed, domain, step,
+                       out=None, with_probs=True, workspace=None, stream=None):
+    """spec_verify with uniforms from the counter generator (seed, domain, step), written to
+    out["uniforms"] [B][K+1] by the call itself.  Same outputs as sv_fill_uniforms followed
+    by spec_verify."""
+    torch = _torch()
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    code = _dtype_code(target_logits)
+    _check(target_logits, "target_logits")
+    _check(draft_logits, "draft_logits", target_logits.dtype, (B, K, V))
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K))
+    _check(temperature, "temperature", torch.float32, (B,))
+    dev = target_logits.device
+    if out is None:
+        out = dict(
+            tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+            accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
+            p=torch.empty((B, K), dtype=torch.float32, device=dev) if with_probs else None,
+            q=torch.empty((B, K), dtype=torch.float32, device=dev) if with_probs else None,
+            status=torch.empty((B,), dtype=torch.int32, device=dev),
+            uniforms=torch.empty((B, K + 1), dtype=torch.float32, device=dev),
+        )
+    _check(out["uniforms"], "uniforms", torch.float32, (B, K + 1))
+    ws = _workspace(workspace, dev, B, K, V)
+    st = lib().spec_verify_philox(
+        _ptr(target_logits), _ptr(draft_logits), code, _ptr(draft_tokens), _ptr(temperature),
+        B, K, V, int(seed), int(domain), int(step), _ptr(out["uniforms"]), _ptr(out["tokens"]),
+        _ptr(out["accept_len"]), _ptr(out["p"]), _ptr(out["q"]), _ptr(out["status"]),
+        _ptr(ws), ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_philox")
     return out
 
 

@@ -100,6 +100,8 @@ sv::VerifyArgs make_args(const void* target, const void* draft, const int32_t* t
     a.out_p = out_p;
     a.out_q = out_q;
     a.out_status = out_status;
+    a.u_gen = nullptr;
+    a.seed = a.domain = a.step = 0;
     return a;
 }
 
@@ -189,6 +191,44 @@ sv_status spec_verify(const void* target_logits, const void* draft_logits, int d
                                        temperature, B, K, V, R, L, workspace, out_tokens,
                                        out_accept_len, out_p, out_q, out_status);
     return launch(a, dtype == SV_DTYPE_BF16, stream);
+}
+
+sv_status spec_verify_philox(const void* target_logits, const void* draft_logits, int dtype,
+                             const int32_t* draft_tokens, const float* temperature,
+                             int B, int K, int V, uint64_t seed, uint64_t domain, uint64_t step,
+                             float* uniforms_out, int32_t* out_tokens, int32_t* out_accept_len,
+                             float* out_p, float* out_q, int32_t* out_status,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_DTYPE;
+    if (!shape_ok(B, K, V)) return SV_ERR_ARG;
+    if (B == 0) return SV_OK;
+    if (!uniforms_out || !aligned(uniforms_out, 4)) return SV_ERR_ARG;
+    // the uniforms are written by the first workgroups of pass 1
+    sv_status st = SV_OK;
+    const size_t esz = dtype == SV_DTYPE_BF16 ? 2 : 4;
+    if (!target_logits || !temperature || !out_tokens || !out_accept_len || !out_status)
+        return SV_ERR_ARG;
+    if (K > 0 && (!draft_logits || !draft_tokens)) return SV_ERR_ARG;
+    if (!aligned(target_logits, esz) || (draft_logits && !aligned(draft_logits, esz)))
+        return SV_ERR_ARG;
+    if (!aligned(temperature, 4) || !aligned(out_tokens, 4) || !aligned(out_accept_len, 4) ||
+        !aligned(out_status, 4) || (draft_tokens && !aligned(draft_tokens, 4)) ||
+        (out_p && !aligned(out_p, 4)) || (out_q && !aligned(out_q, 4)))
+        return SV_ERR_ARG;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < workspace_need(B, K, V))
+        return SV_ERR_WORKSPACE;
+    const int R = 2 * K + 1;
+    const Layout L = sv::make_layout(B, K, V, (int)esz, R);
+    if (!grid_ok(B, R, L)) return SV_ERR_ARG;
+    sv::VerifyArgs a = make_args(target_logits, draft_logits, draft_tokens, uniforms_out,
+                                 temperature, B, K, V, R, L, workspace, out_tokens,
+                                 out_accept_len, out_p, out_q, out_status);
+    a.u_gen = uniforms_out;
+    a.seed = seed;
+    a.domain = domain;
+    a.step = step;
+    st = launch(a, dtype == SV_DTYPE_BF16, stream);
+    return st;
 }
 
 sv_status spec_verify_ragged(const void* target_logits, const void* draft_logits, int dtype,

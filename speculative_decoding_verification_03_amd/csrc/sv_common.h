@@ -160,6 +160,10 @@ struct VerifyArgs {
     DrawPartial* part2;        // [B][nseg]
     Bucket* bkt;               // [B][nseg][kBuckets]
     double* wtab;              // bf16: [B][kWtabLen] weight table of each sequence's draw
+    // when u_gen is set, pass 1 also writes uniforms[B][K+1] (dense layout) from the
+    // counter generator with these parameters; the resolve reads them after it
+    float* u_gen;
+    uint64_t seed, domain, step;
     int32_t* out_tokens;
     int32_t* out_n;            // may be null (plain sampling)
     float* out_p;

@@ -133,6 +133,36 @@ __device__ __forceinline__ double exp2_arg(double z, double ref, double c) {
 }
 
 // ---------------------------------------------------------------------------------
+// counter-based uniforms: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC'11): 10 rounds of two 64x64->128-bit multiplies and a
+// permutation, with a Weyl-sequence key schedule.  Contract:
+//   key = (seed, domain), counter = (t, b, step, 0), u = (word0 >> 40) * 2^-24.
+// ---------------------------------------------------------------------------------
+
+__device__ __forceinline__ float philox_uniform(uint64_t seed, uint64_t domain, uint64_t t,
+                                                uint64_t b, uint64_t step) {
+    constexpr uint64_t kM0 = 0xD2E7470EE14C6C93ull;
+    constexpr uint64_t kM1 = 0xCA5A826395121157ull;
+    constexpr uint64_t kW0 = 0x9E3779B97F4A7C15ull;
+    constexpr uint64_t kW1 = 0xBB67AE8584CAA73Bull;
+    uint64_t c0 = t, c1 = b, c2 = step, c3 = 0;
+    uint64_t k0 = seed, k1 = domain;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t lo0 = kM0 * c0, hi0 = __umul64hi(kM0, c0);
+        const uint64_t lo1 = kM1 * c2, hi1 = __umul64hi(kM1, c2);
+        const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+        k0 += kW0;
+        k1 += kW1;
+    }
+    return (float)(uint32_t)(c0 >> 40) * 0x1p-24f;
+}
+
+// ---------------------------------------------------------------------------------
 // where a sequence's rows live (dense or packed layout, see VerifyArgs)
 // ---------------------------------------------------------------------------------
 

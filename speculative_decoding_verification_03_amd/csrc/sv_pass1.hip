@@ -186,6 +186,13 @@ __device__ void tile_argmax(const E* row, int lo, int hi, RowPartial* out) {
 template <typename E>
 __global__ __launch_bounds__(kThreads) void pass1_kernel(VerifyArgs a, int b0) {
     const int64_t blk = blockIdx.x;
+    if (a.u_gen) {
+        // the uniforms of the call, one per thread of the first workgroups
+        const int64_t i = blk * kThreads + threadIdx.x;
+        if (i < (int64_t)a.B * (a.K + 1))
+            a.u_gen[i] = philox_uniform(a.seed, a.domain, (uint64_t)(i % (a.K + 1)),
+                                        (uint64_t)(i / (a.K + 1)), a.step);
+    }
     const int r = (int)(blk / a.nchunk1);
     const int c = (int)(blk - (int64_t)r * a.nchunk1);
     const int b = b0 + r / a.R;

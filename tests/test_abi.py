@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
         "sv_abi_version", "sv_status_string", "sv_workspace_bytes", "spec_verify",
         "spec_verify_greedy", "sv_fill_uniforms", "sv_profile_begin", "sv_profile_end",
         "spec_verify_ragged", "spec_verify_greedy_ragged", "sv_sample",
-        "sv_fill_uniforms_ragged", "spec_verify_tree_greedy", "sv_tree_attention_mask"])
+        "sv_fill_uniforms_ragged", "spec_verify_tree_greedy", "sv_tree_attention_mask",
+        "spec_verify_philox"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert sv.sv_abi_version() == 2
+    assert sv.sv_abi_version() == 3
     assert sv.sv_status_string(sv.SV_OK) == "ok"
     assert sv.sv_status_string(sv.SV_ERR_ARG) == "invalid argument"
     assert sv.sv_status_string(sv.SV_ERR_WORKSPACE).startswith("workspace")
@@ -253,6 +254,23 @@ def test_tree_entry_points_reject_bad_arguments():
     assert m(st=0) == sv.SV_ERR_ARG
     assert m(dep=GOOD + 2) == sv.SV_ERR_ARG
     assert m(B=0, par=0, mask=0, st=0) == sv.SV_OK
+
+
+def test_spec_verify_philox_rejects_bad_arguments():
+    L = sv.lib()
+    f = lambda **kw: L.spec_verify_philox(  # noqa: E731
+        _p(kw.get("t", GOOD)), _p(kw.get("d", GOOD)), kw.get("dtype", 1), _p(kw.get("x", GOOD)),
+        _p(kw.get("T", GOOD)), kw.get("B", 4), kw.get("K", 3), kw.get("V", 64), 1, 0, 0,
+        _p(kw.get("u", GOOD)), _p(kw.get("tok", GOOD)), _p(kw.get("n", GOOD)), _p(GOOD), _p(GOOD),
+        _p(kw.get("st", GOOD)), _p(kw.get("ws", WS)), kw.get("wsb", 1 << 30), None)
+    assert f(dtype=9) == sv.SV_ERR_DTYPE
+    assert f(B=-1) == sv.SV_ERR_ARG
+    for k in ("t", "d", "x", "T", "u", "tok", "n", "st"):
+        assert f(**{k: 0}) == sv.SV_ERR_ARG, k
+    assert f(u=GOOD + 2) == sv.SV_ERR_ARG
+    assert f(ws=0) == sv.SV_ERR_WORKSPACE
+    assert f(K=0, d=0, x=0, ws=0) == sv.SV_ERR_WORKSPACE
+    assert f(B=0, t=0, d=0, x=0, T=0, u=0, tok=0, n=0, st=0, ws=0) == sv.SV_OK
 
 
 def test_binding_refuses_host_tensors():

@@ -340,3 +340,22 @@ def test_deterministic_and_workspace_reuse(dev):
                 assert np.array_equal(x[k], y[k], equal_nan=True), k
     t = compare(a, oracle_sampled(inp, u), range(16), inp["temperature"].cpu())
     t.assert_ok("reuse")
+
+
+@pytest.mark.parametrize("cfg,B", [(4, None), (1, 700), (2, None)])
+def test_philox_entry_point_equals_two_calls(dev, cfg, B):
+    """spec_verify_philox = sv_fill_uniforms + spec_verify, bit for bit (uniforms too)."""
+    inp = W.make_inputs(cfg, step=9, device=dev, B=B)
+    Bn, K = inp["B"], inp["K"]
+    say(f"philox entry point: workload {cfg} B={Bn}")
+    u = sv.sv_fill_uniforms(31337, 2, 9, Bn, K)
+    a = to_host(sv.spec_verify(inp["target"], inp["draft"], inp["tokens"], u, inp["temperature"]))
+    f = sv.spec_verify_philox(inp["target"], inp["draft"], inp["tokens"], inp["temperature"],
+                              31337, 2, 9)
+    torch.cuda.synchronize()
+    f = to_host(f)
+    np.testing.assert_array_equal(f["uniforms"], u.cpu().numpy())
+    for k in ("tokens", "accept_len", "status"):
+        np.testing.assert_array_equal(f[k], a[k])
+    for k in ("p", "q"):
+        np.testing.assert_array_equal(f[k].view(np.uint32), a[k].view(np.uint32))
