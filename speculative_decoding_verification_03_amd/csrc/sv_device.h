@@ -346,6 +346,18 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, float* shv, int* 
     __syncthreads();
 }
 
+// Inclusive prefix sum over the wave's lanes in lane order (Hillis-Steele: a fixed
+// combination order, so the result is reproducible).
+__device__ __forceinline__ double wave_inclusive_scan(double v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(v, o, 64);
+        if (lane >= o) v += y;
+    }
+    return v;
+}
+
 // Exclusive prefix sum of one fp64 value per thread, in thread order; also returns
 // the workgroup total.  Fixed combination order (Hillis-Steele inside each wave, then
 // wave totals left to right), so results are reproducible.

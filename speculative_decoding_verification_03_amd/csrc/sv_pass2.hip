@@ -1,11 +1,13 @@
 // Pass 2 of the verify step: the resolve and the one categorical draw of each sequence,
 // in three kernels: resolve_kernel (one workgroup per sequence), sweep_kernel over
-// (sequence, chunk) workgroups, then final_kernel (one workgroup per sequence).
+// (sequence, chunk) workgroups, then final_kernel (one workgroup per sequence); and the
+// draft-side sampler, sample_kernel (one workgroup per row).
 //
 // Resolve: validation, then the left-to-right test r_t < p_t(x_t)/q_t(x_t) of "A Regra
-// de Exatidão" (lesson page "Decodificação Especulativa e EAGLE"), evaluated in fp64 log
-// space from the pass-1 row statistics, or for T = 0 the greedy comparison
-// argmax(p_t) == x_t ("Caso ganancioso").  n = the first failing position (K if none).
+// de Exatidão" (lesson page "Decodificação Especulativa e EAGLE"), evaluated in fp64 from
+// the pass-1 row statistics, or for T = 0 the greedy comparison argmax(p_t) == x_t ("Caso
+// ganancioso").  n = the first failing position (K if none).  It also writes the draw's
+// descriptor and, for bf16 logits, the sequence's weight table to the workspace.
 //
 // The draw.  After a rejection at n the token comes from (p_n - q_n)+, the positive part
 // of the pointwise difference over the whole vocabulary ("A Regra de Exatidão"; the
@@ -18,22 +20,25 @@
 // Weights.  a_i = 2^((zt_i - refA) c2), b_i = 2^((zd_i - refB) c2), c2 = log2(e)/T, so that
 // p_i = a_i / S_p and q_i = b_i / S_q.  Both rows share one reference (the larger row
 // maximum) unless that would push the smaller row toward fp64 underflow.  For bf16 logits
-// each workgroup tabulates the weight of every bf16 value with |z| in [2^-10, 32) in LDS
-// (3840 doubles) and looks weights up; other values, and fp32 logits, take the fp64
-// exponential of sv_device.h.  A weight below 2^-70 of its row maximum counts as 0: over
-// any vocabulary that moves the normalisers by less than V 2^-70 relative.
+// the resolve tabulates the weight of every bf16 value with |z| in [2^-10, 32) (3840
+// doubles); the sweep and final kernels copy the table into LDS and look weights up.
+// Other values, and fp32 logits, take the fp64 exponential of sv_device.h.  A weight so
+// computed below 2^-70 of its row maximum counts as 0: over any vocabulary that moves the
+// normalisers by less than V 2^-70 relative.
 //
-// Sweep (each workgroup one chunk of the row, each wave one contiguous sub-chunk): S_p,
-// S_q, and the sums A, B of a_i, b_i over the positions whose residual is positive for
-// every normaliser ratio within 1 +- kDelta of the pass-1 estimate.  The sign test is on the
-// logit difference: p_i > q_i exactly when zt_i - zd_i > tau = T ln(S_p/S_q) + refA - refB.
-// Positions whose difference falls inside the bracket go to buckets of equal difference
-// (equal difference, equal a/b ratio, one residual sign), each with its sums of a and b.
+// Sweep (each workgroup one chunk of the row, each wave a run of kSeg-position segments):
+// per segment S_p, S_q, and the sums A, B of a_i, b_i over the positions whose residual is
+// positive for every normaliser ratio within 1 +- kDelta of the pass-1 estimate.  The sign
+// test is on the logit difference: p_i > q_i exactly when zt_i - zd_i > tau =
+// T ln(S_p/S_q) + refA - refB.  Positions whose difference falls inside the bracket go to
+// buckets of equal difference (equal difference, equal a/b ratio, one residual sign), each
+// with its sums of a and b.
 //
-// Final (one workgroup per sequence, after every sweep): exact fp64 normalisers, the check that the estimate bracketed them (else
-// one exact sweep by this workgroup), each sub-chunk's residual mass A/S_p - B/S_q plus the
-// positive bucket masses, a scan of the masses for u * W, and a scan inside the sub-chunk
-// that holds it: token = min{ i : C_i > u * W }, C the prefix sums in index order.
+// Final (one workgroup per sequence, after every sweep): exact fp64 normalisers, the check
+// that the estimate bracketed them (else one exact sweep by this workgroup), each
+// segment's residual mass A/S_p - B/S_q plus the positive bucket masses, a scan of the
+// masses for u * W, and a scan inside the segment that holds it:
+// token = min{ i : C_i > u * W }, C the prefix sums in index order.
 #include <float.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -1167,11 +1172,22 @@ __device__ __forceinline__ void final_seq_small(const VerifyArgs& a, DrawRows<E>
     const double u = (double)d.u;
     int status = 0;
 
-    // dp, bk0: this thread's segment partial and its first bucket (thread tid < nsub)
-    if (tid >= nsub) dp = DrawPartial{};
+    // dp, bk0: the partial and first bucket of segment k of this thread.  Up to 64
+    // segments every wave holds all of them (k = lane) and reduces and scans them itself,
+    // with no barrier; otherwise thread k holds segment k and the workgroup combines.
+    const int lane = tid & 63;
+    const bool per_wave = nsub <= 64;
+    const int k = per_wave ? lane : tid;
+    if (k >= nsub) dp = DrawPartial{};
     double sp = dp.sp, sq = dp.sq;
     int over = dp.nbkt > kBuckets;
-    block_sum2_or<NW>(sp, sq, over, shd, shi);
+    if (per_wave) {
+        sp = wave_sum(sp);
+        sq = wave_sum(sq);
+        over = wave_or(over);
+    } else {
+        block_sum2_or<NW>(sp, sq, over, shd, shi);
+    }
     // the classification by the pass-1 estimate stands if the exact threshold
     // T ln(S_p/S_q) + refA - refB lies well inside the bracket
     bool exact_ok = sp > 0.0;
@@ -1196,12 +1212,12 @@ __device__ __forceinline__ void final_seq_small(const VerifyArgs& a, DrawRows<E>
         // this segment's mass in the units of the draw: its certain part and, per bucket
         // of undecided positions (one residual sign each), the bucket's residual if positive
         double v = 0.0;
-        if (tid < nsub) {
+        if (k < nsub) {
             if (!r.residual) {
                 v = dp.sp;
             } else {
                 v = dp.A * r.inv_sp - dp.B * r.inv_sq;
-                const Bucket* bk = bkt + tid * kBuckets;
+                const Bucket* bk = bkt + k * kBuckets;
                 for (int q = 0; q < dp.nbkt; ++q) {
                     const Bucket bq = q == 0 ? bk0 : bk[q];
                     const double t = bq.a * r.inv_sp - bq.b * r.inv_sq;
@@ -1210,22 +1226,44 @@ __device__ __forceinline__ void final_seq_small(const VerifyArgs& a, DrawRows<E>
                 v = v > 0.0 ? v : 0.0;
             }
         }
-        double total;
-        const double ex = block_exclusive_scan<NW>(v, total, shd);
+        double total, ex;
+        if (per_wave) {
+            const double incl = wave_inclusive_scan(v);
+            total = __shfl(incl, 63, 64);
+            ex = __shfl_up(incl, 1, 64);
+            if (lane == 0) ex = 0.0;
+        } else {
+            ex = block_exclusive_scan<NW>(v, total, shd);
+        }
         if (total > 0.0) {
             const double target = u * total;
             // a segment without mass never holds the first crossing (guards rounding)
-            int hit = block_min<NW>((tid < nsub && v > 0.0 && ex + v > target) ? tid : 0x7fffffff, shi);
-            double tgt = target;
-            if (hit == 0x7fffffff) {
-                // rounding put u*W past every prefix: the last segment with mass, last index
-                hit = block_max<NW>((tid < nsub && v > 0.0) ? tid : -1, shi);
-                tgt = INFINITY;
-                status |= kSeqNoteFallback;
+            const bool crosses = k < nsub && v > 0.0 && ex + v > target;
+            const bool mass = k < nsub && v > 0.0;
+            int hit;
+            double tgt = target, base;
+            if (per_wave) {
+                const uint64_t mc = __ballot(crosses), mm = __ballot(mass);
+                if (mc) {
+                    hit = __ffsll((unsigned long long)mc) - 1;
+                } else {
+                    // rounding put u*W past every prefix: the last segment with mass, last index
+                    hit = 63 - __clzll((long long)mm);
+                    tgt = INFINITY;
+                    status |= kSeqNoteFallback;
+                }
+                base = __shfl(ex, hit, 64);
+            } else {
+                hit = block_min<NW>(crosses ? k : 0x7fffffff, shi);
+                if (hit == 0x7fffffff) {
+                    hit = block_max<NW>(mass ? k : -1, shi);
+                    tgt = INFINITY;
+                    status |= kSeqNoteFallback;
+                }
+                if (tid == hit) sh_base = ex;
+                __syncthreads();
+                base = sh_base;
             }
-            if (tid == hit) sh_base = ex;
-            __syncthreads();
-            const double base = sh_base;
             int lo, hi;
             seg_range(a.V, L, hit, lo, hi);
             y = segment_search<E, NT, PER>(r, lo, hi, base, tgt);
@@ -1466,7 +1504,8 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(VerifyArgs a, int 
     const bool small = a.nseg <= kFinalThreads;
     const DrawPartial* part = a.part2 + (int64_t)b * a.nseg;
     const Bucket* bkt = a.bkt + (int64_t)b * a.nseg * kBuckets;
-    const int k = min((int)threadIdx.x, a.nseg - 1);
+    // the segment of this thread in final_seq_small: its lane up to 64 segments
+    const int k = min(a.nseg <= 64 ? (int)(threadIdx.x & 63) : (int)threadIdx.x, a.nseg - 1);
     const DrawPartial dp = part[k];
     const Bucket bk0 = bkt[k * kBuckets];
     if (d.mode == kModeNone) return;  // whole workgroup
