@@ -145,11 +145,9 @@ struct RowStat {
 // ln x for finite x > 0 in fp64 (the resolve's few logarithms).
 __device__ __forceinline__ double ln(double x) { return log(x); }
 
-// Where the resolve finds its inputs: the sequence's pass-1 partials (staged in LDS when
-// they fit, else in the workspace), and its first kRowsLds draft tokens and kRowsLds + 1
-// uniforms (LDS; later ones are read from memory).
+// Where the resolve finds a sequence's draft tokens and uniforms: the first kRowsLds
+// tokens and kRowsLds + 1 uniforms in LDS, later ones in memory.
 struct ResolveIn {
-    const RowPartial* parts;  // [R][nchunk1] of the sequence
     const int32_t* xs;        // LDS tokens
     const float* us;          // LDS uniforms
     const int32_t* x;         // tokens in memory
@@ -163,13 +161,15 @@ struct ResolveIn {
 // comparison keeps the earlier chunk on ties).  Sampled: max m and S = the chunks' sums
 // rebased from their own maxima to m, 2^((m_c - m) c2) in fp64, added in chunk order;
 // `terms` (or null) holds those rebased sums, computed beforehand one per thread.
+// `parts`: the sequence's partials (in LDS or in memory; the caller passes the array
+// itself, so that the compiler sees which).
 __device__ __forceinline__ RowStat merge_row(const VerifyArgs& a, const SeqRows& s, const ResolveIn& in,
-                                             int i, bool sampled, float c2, const double* tab,
-                                             const double* terms) {
+                                             const RowPartial* parts, int i, bool sampled, float c2,
+                                             const double* tab, const double* terms) {
     const bool is_target = i <= s.K;
     const int t = is_target ? i : i - s.K - 1;
     const int j = is_target ? t : a.K + 1 + t;  // workspace slot (dense layout, K the bound)
-    const RowPartial* p = in.parts + (int64_t)j * a.nchunk1;
+    const RowPartial* p = parts + (int64_t)j * a.nchunk1;
     RowStat r{-INFINITY, 0x7fffffff, 0.0, -INFINITY};
     if (!sampled) {
         bool bad = false;
@@ -206,12 +206,12 @@ __device__ __forceinline__ RowStat merge_row(const VerifyArgs& a, const SeqRows&
 }
 
 // The rebased chunk sum of sampled row i, chunk c (see merge_row).
-__device__ __forceinline__ double chunk_term(const VerifyArgs& a, const SeqRows& s, const ResolveIn& in,
+__device__ __forceinline__ double chunk_term(const VerifyArgs& a, const SeqRows& s, const RowPartial* parts,
                                              int i, int c, float c2, const double* tab) {
     const bool is_target = i <= s.K;
     const int t = is_target ? i : i - s.K - 1;
     const int j = is_target ? t : a.K + 1 + t;
-    const RowPartial* p = in.parts + (int64_t)j * a.nchunk1;
+    const RowPartial* p = parts + (int64_t)j * a.nchunk1;
     float m = -INFINITY;
     for (int cc = 0; cc < a.nchunk1; ++cc) m = nmax(m, p[cc].m);
     const RowPartial q = p[c];
@@ -258,7 +258,6 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
     const int nparts = a.R * a.nchunk1;
     const RowPartial* src = a.part1 + (int64_t)b * nparts;
     const bool staged = nparts <= kPartsLds;
-    in.parts = staged ? parts : src;
     if (staged) {
         // two 16-byte loads in flight per thread (indices clamped, stores guarded)
         const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
@@ -296,18 +295,21 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
     if (by_pair) {
         for (int q = tid; q < nrows * a.nchunk1; q += NT) {
             const int i = q / a.nchunk1;
-            terms[q] = chunk_term(a, s, in, i, q - i * a.nchunk1, c2, tab);
+            terms[q] = chunk_term(a, s, parts, i, q - i * a.nchunk1, c2, tab);
         }
         __syncthreads();
     }
     for (int i = tid; i < nrows; i += NT) {
-        const RowStat r = merge_row(a, s, in, i, sampled, c2, tab, by_pair ? terms : nullptr);
+        const RowStat r = staged ? merge_row(a, s, in, parts, i, sampled, c2, tab, by_pair ? terms : nullptr)
+                                 : merge_row(a, s, in, src, i, sampled, c2, tab, nullptr);
         if (row_bad(r.m, sampled)) err |= kSeqErrLogit;
         if (i < kRowsLds) rows[i] = r;
     }
     err = block_or<NW>(err, shi);  // also orders the rows[] writes before the reads below
     auto row = [&](int i) -> RowStat {
-        return i < kRowsLds ? rows[i] : merge_row(a, s, in, i, sampled, c2, tab, nullptr);
+        if (i < kRowsLds) return rows[i];
+        return staged ? merge_row(a, s, in, parts, i, sampled, c2, tab, nullptr)
+                      : merge_row(a, s, in, src, i, sampled, c2, tab, nullptr);
     };
 
     int32_t* tok = a.out_tokens + s.t0;
