@@ -105,12 +105,17 @@ inline void chunking1(int64_t rows, int V, int esize, int& nchunk1, int& ch1) {
 inline int segments(int V) { return (int)ceil_div(V, (int64_t)kSeg); }
 
 // Draw chunks (workgroups) per sequence for a launch over `seqs` sequences: about
-// kTargetBlocks2 workgroups in all; each chunk holds spc whole segments.
+// kTargetBlocks2 workgroups in all; each chunk holds spc whole segments, at least one per
+// wave of a workgroup when the row has that many (each workgroup copies the weight table
+// once, so a chunk should keep all its waves busy).
 inline void chunking2(int64_t seqs, int V, int& nchunk2, int& spc) {
     const int64_t nseg = segments(V);
     const int64_t want = seqs > 0 ? ceil_div(kTargetBlocks2, seqs) : 1;
     const int64_t n = want < 1 ? 1 : (want > nseg ? nseg : want);
-    spc = (int)ceil_div(nseg, n);
+    int64_t per = ceil_div(nseg, n);
+    const int64_t waves = kSweepThreads / 64;
+    if (per < waves) per = nseg < waves ? nseg : waves;
+    spc = (int)per;
     nchunk2 = (int)ceil_div(nseg, spc);
 }
 

@@ -737,6 +737,50 @@ __device__ __forceinline__ void exact_word_tab(const DrawRows<uint16_t>& r, uint
     accumulate<uint16_t, 2>(r, av, bv, zt, zd, dx_ok, live, s);
 }
 
+// One word of each row of a span that is taken again: words whose four values all lie in
+// the table take the fast path's arithmetic with every undecided position bucketed by its
+// exact difference (the differences of such values are exact in fp32); other words take
+// the exact path.
+template <bool Residual>
+__device__ __forceinline__ void redo_word_tab(const DrawRows<uint16_t>& r, uint32_t xt, uint32_t xd,
+                                              SweepAcc& s) {
+    uint32_t ot0, ot1, od0 = 0, od1 = 0;
+    tab_offsets(xt, ot0, ot1);
+    if (Residual) tab_offsets(xd, od0, od1);
+    const double a0 = tab_at(r.wt, ot0), a1 = tab_at(r.wt, ot1);
+    const double b0 = Residual ? tab_at(r.wt, od0) : 0.0, b1 = Residual ? tab_at(r.wt, od1) : 0.0;
+    // a sentinel (value outside the table) reads NaN
+    const bool out = (a0 != a0) | (a1 != a1) | (b0 != b0) | (b1 != b1);
+    if (__any(out)) {
+        exact_word_tab<Residual>(r, xt, xd, s);
+        return;
+    }
+    if (!Residual) {
+        s.sp += a0;
+        s.sp += a1;
+        return;
+    }
+    const float D0 = __uint_as_float(xt << 16) - __uint_as_float(xd << 16);
+    const float D1 = __uint_as_float(xt & 0xffff0000u) - __uint_as_float(xd & 0xffff0000u);
+    const bool p0 = D0 > r.tau_hi_f, p1 = D1 > r.tau_hi_f;
+    // positions with no weight on either side need no sign (as on the exact path)
+    const bool u0 = !p0 && D0 >= r.tau_lo_f && (a0 != 0.0 || b0 != 0.0);
+    const bool u1 = !p1 && D1 >= r.tau_lo_f && (a1 != 0.0 || b1 != 0.0);
+    s.sp += a0;
+    s.sq += b0;
+    s.sp += a1;
+    s.sq += b1;
+    const double s0 = p0 ? 1.0 : 0.0, s1 = p1 ? 1.0 : 0.0;
+    s.A = __builtin_fma(a0, s0, s.A);
+    s.B = __builtin_fma(b0, s0, s.B);
+    s.A = __builtin_fma(a1, s1, s.A);
+    s.B = __builtin_fma(b1, s1, s.B);
+    if (__any(u0 || u1)) {
+        bucket_add(s, u0, (double)D0, a0, b0);
+        bucket_add(s, u1, (double)D1, a1, b1);
+    }
+}
+
 // Fast path for one word of each row: table weights without range checks (a value outside
 // the table reads NaN), signs from the fp32 difference.  Undecided positions (difference
 // inside the bracket) are summed into s.kA, s.kB when their difference equals the wave's
@@ -916,10 +960,10 @@ __device__ __forceinline__ void sweep_wave_tab(const DrawRows<uint16_t>& r, int 
                 const int i = g0 + j * kSpan16 + (g * 64 + lane) * 8;
                 const u32x4 vt = *reinterpret_cast<const u32x4*>(r.t + i);
                 const u32x4 vd = Residual ? *reinterpret_cast<const u32x4*>(r.d + i) : u32x4{0u, 0u, 0u, 0u};
-                exact_word_tab<Residual>(r, vt.x, vd.x, acc);
-                exact_word_tab<Residual>(r, vt.y, vd.y, acc);
-                exact_word_tab<Residual>(r, vt.z, vd.z, acc);
-                exact_word_tab<Residual>(r, vt.w, vd.w, acc);
+                redo_word_tab<Residual>(r, vt.x, vd.x, acc);
+                redo_word_tab<Residual>(r, vt.y, vd.y, acc);
+                redo_word_tab<Residual>(r, vt.z, vd.z, acc);
+                redo_word_tab<Residual>(r, vt.w, vd.w, acc);
             }
         }
         // a segment ends here (or the row does, exactly at a span)
