@@ -166,6 +166,9 @@ def main():
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="verify", choices=["verify", "ragged", "sample", "tree"])
+    ap.add_argument("--early-exit", action="store_true",
+                    help="verify path: sv_fill_uniforms, then spec_verify_early_exit (rows read "
+                         "only up to each sequence's first rejection; p, q past it not reported)")
     ap.add_argument("--separate-uniforms", action="store_true",
                     help="verify path: sv_fill_uniforms, then spec_verify (default: "
                          "spec_verify_philox, which generates them in the same launches)")
@@ -210,7 +213,11 @@ def main():
     def step(i):
         k = i % nsets
         x = sets[k]
-        if args.separate_uniforms:
+        if args.early_exit:
+            sv.sv_fill_uniforms(seed, 0, i, B, K, out=u[k])
+            sv.spec_verify_early_exit(x["target"], x["draft"], x["tokens"], u[k], x["temperature"],
+                                      out=outs[k], workspace=ws)
+        elif args.separate_uniforms:
             sv.sv_fill_uniforms(seed, 0, i, B, K, out=u[k])
             sv.spec_verify(x["target"], x["draft"], x["tokens"], u[k], x["temperature"],
                            out=outs[k], workspace=ws)
@@ -361,6 +368,12 @@ def main():
             "algorithmic_bytes_per_launch": p1_bytes,
         },
     }
+    if args.path == "verify" and args.early_exit:
+        result["metric"] += " (early exit)"
+        result["config"]["workload"] += "; rows read only up to each sequence's first rejection"
+        result["roofline"]["kernel"] = ("pass1_kernel, both rounds (algorithmic bytes: every row "
+                                        "of the full read, so frac here is an effective rate)")
+        result["roofline"]["traffic"] = None
     if args.path == "ragged":
         kbs = [k for P in packs for k in P["kb"]]
         result["metric"] = "verified positions/sec at ragged K_b (adaptive verification)"

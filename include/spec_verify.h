@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 3
+#define SV_ABI_VERSION 4
 
 /* Host-side return codes. */
 typedef enum sv_status {
@@ -124,6 +124,24 @@ sv_status spec_verify(const void* target_logits, const void* draft_logits, int d
                       int32_t* out_tokens, int32_t* out_accept_len,
                       float* out_p, float* out_q, int32_t* out_status,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify reading each sequence's rows only up to its first rejection: the tests run
+ * left to right and stop there ("A Regra de Exatidão": the first rejection ends the step),
+ * so the rows of later positions are never needed for the emitted tokens.  Positions are
+ * read in two rounds (the first third, then the rest for the sequences that accepted all
+ * of the first); a sequence whose test fails in the first round reads nothing more.  The
+ * emitted tokens, accept lengths and draws are bit-identical to spec_verify's.
+ * Differences: out_p / out_q are NaN for positions whose rows were not read (past the
+ * round in which the sequence stopped), and a NaN or +inf logit in a row that was not
+ * read is not reported.  Arguments as for spec_verify.
+ */
+sv_status spec_verify_early_exit(const void* target_logits, const void* draft_logits, int dtype,
+                                 const int32_t* draft_tokens, const float* uniforms,
+                                 const float* temperature, int B, int K, int V,
+                                 int32_t* out_tokens, int32_t* out_accept_len,
+                                 float* out_p, float* out_q, int32_t* out_status,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * spec_verify with uniforms from the counter generator: the same as

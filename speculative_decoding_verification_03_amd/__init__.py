@@ -12,6 +12,7 @@ __all__ = [
     "LibraryMissing", "SpecVerifyError", "lib", "lib_path",
     "sv_abi_version", "sv_status_string", "sv_workspace_bytes",
     "spec_verify", "spec_verify_greedy", "sv_fill_uniforms", "Workspace", "spec_verify_philox",
+    "spec_verify_early_exit",
     "spec_verify_ragged", "spec_verify_greedy_ragged", "sv_fill_uniforms_ragged", "sv_sample",
     "spec_verify_tree_greedy", "sv_tree_attention_mask", "SV_TREE_MAX_NODES",
     "sv_profile_begin", "sv_profile_end",
@@ -65,6 +66,9 @@ def lib():
     L.spec_verify.restype = i32
     L.spec_verify.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32,
                               vp, vp, vp, vp, vp, vp, sz, vp]
+    L.spec_verify_early_exit.restype = i32
+    L.spec_verify_early_exit.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32,
+                                         vp, vp, vp, vp, vp, vp, sz, vp]
     L.spec_verify_philox.restype = i32
     L.spec_verify_philox.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, u64, u64, u64, vp,
                                      vp, vp, vp, vp, vp, vp, sz, vp]
@@ -180,7 +184,7 @@ def _workspace(ws, device, B, K, V):
 
 
 def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature,
-                out=None, with_probs=True, workspace=None, stream=None):
+                out=None, with_probs=True, workspace=None, stream=None, _entry="spec_verify"):
     """Sampled verify (greedy rule where temperature == 0).
 
     target_logits [B][K+1][V], draft_logits [B][K][V] (bf16 or fp32, same dtype),
@@ -207,14 +211,23 @@ def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature
             status=torch.empty((B,), dtype=torch.int32, device=dev),
         )
     ws = _workspace(workspace, dev, B, K, V)
-    st = lib().spec_verify(
+    st = getattr(lib(), _entry)(
         _ptr(target_logits), _ptr(draft_logits), code, _ptr(draft_tokens), _ptr(uniforms),
         _ptr(temperature), B, K, V, _ptr(out["tokens"]), _ptr(out["accept_len"]),
         _ptr(out["p"]), _ptr(out["q"]), _ptr(out["status"]),
         _ptr(ws), ws.numel(), _stream(stream))
     if st != SV_OK:
-        raise SpecVerifyError(st, "spec_verify")
+        raise SpecVerifyError(st, _entry)
     return out
+
+
+def spec_verify_early_exit(target_logits, draft_logits, draft_tokens, uniforms, temperature,
+                           out=None, with_probs=True, workspace=None, stream=None):
+    """spec_verify reading rows only up to each sequence's first rejection (see
+    include/spec_verify.h): same tokens and accept lengths; p, q NaN where not read."""
+    return spec_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, out=out,
+                       with_probs=with_probs, workspace=workspace, stream=stream,
+                       _entry="spec_verify_early_exit")
 
 
 def spec_verify_philox(target_logits, draft_logits, draft_tokens, temperature, seed, domain, step,

@@ -193,6 +193,60 @@ sv_status spec_verify(const void* target_logits, const void* draft_logits, int d
     return launch(a, dtype == SV_DTYPE_BF16, stream);
 }
 
+sv_status spec_verify_early_exit(const void* target_logits, const void* draft_logits, int dtype,
+                                 const int32_t* draft_tokens, const float* uniforms,
+                                 const float* temperature, int B, int K, int V,
+                                 int32_t* out_tokens, int32_t* out_accept_len,
+                                 float* out_p, float* out_q, int32_t* out_status,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_DTYPE;
+    if (!shape_ok(B, K, V)) return SV_ERR_ARG;
+    if (B == 0) return SV_OK;
+    const size_t esz = dtype == SV_DTYPE_BF16 ? 2 : 4;
+    if (!target_logits || !uniforms || !temperature || !out_tokens || !out_accept_len ||
+        !out_status)
+        return SV_ERR_ARG;
+    if (K > 0 && (!draft_logits || !draft_tokens)) return SV_ERR_ARG;
+    if (!aligned(target_logits, esz) || (draft_logits && !aligned(draft_logits, esz)))
+        return SV_ERR_ARG;
+    if (!aligned(uniforms, 4) || !aligned(temperature, 4) || !aligned(out_tokens, 4) ||
+        !aligned(out_accept_len, 4) || !aligned(out_status, 4) ||
+        (draft_tokens && !aligned(draft_tokens, 4)) || (out_p && !aligned(out_p, 4)) ||
+        (out_q && !aligned(out_q, 4)))
+        return SV_ERR_ARG;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < workspace_need(B, K, V))
+        return SV_ERR_WORKSPACE;
+    const int R = 2 * K + 1;
+    const Layout L = sv::make_layout(B, K, V, (int)esz, R);
+    if (!grid_ok(B, R, L)) return SV_ERR_ARG;
+    sv::VerifyArgs a = make_args(target_logits, draft_logits, draft_tokens, uniforms,
+                                 temperature, B, K, V, R, L, workspace, out_tokens,
+                                 out_accept_len, out_p, out_q, out_status);
+    a.limit = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + L.off_limit);
+    const int bf16 = dtype == SV_DTYPE_BF16;
+    // two rounds: the first third of the positions, then the rest for the sequences that
+    // accepted all of them
+    const int r1 = (K + 3) / 3;
+    const int bounds[3] = {0, r1, K + 1};
+    const int rounds = r1 >= K + 1 ? 1 : 2;
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    if (g_prof.on) {
+        for (auto& e : ev) e = g_prof.next();
+        g_prof.calls++;
+        g_prof.record(ev[0], stream);
+    }
+    for (int r = 0; r < rounds; ++r) {
+        a.t0 = bounds[r];
+        a.t1 = r + 1 == rounds ? K + 1 : bounds[r + 1];
+        if (sv::launch_pass1(a, bf16, 0, B, stream) != 0) return SV_ERR_HIP;
+        if (sv::launch_prefix(a, bf16, stream) != 0) return SV_ERR_HIP;
+    }
+    if (g_prof.on) g_prof.record(ev[1], stream);
+    if (sv::launch_draw(a, bf16, 0, B, stream) != 0) return SV_ERR_HIP;
+    if (g_prof.on) g_prof.record(ev[2], stream);
+    return SV_OK;
+}
+
 sv_status spec_verify_philox(const void* target_logits, const void* draft_logits, int dtype,
                              const int32_t* draft_tokens, const float* temperature,
                              int B, int K, int V, uint64_t seed, uint64_t domain, uint64_t step,

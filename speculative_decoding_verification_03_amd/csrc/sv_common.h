@@ -63,8 +63,13 @@ constexpr int kSeqDescBytes = 64;  // workspace slot of the resolve's per-sequen
 struct Layout {
     int nchunk1, ch1;  // pass-1 chunks per row and elements per chunk (multiple of 64)
     int nseg;          // draw segments per sequence: ceil(V / kSeg)
-    size_t off_desc, off_part1, off_part2, off_bkt, off_wtab, total;
+    size_t off_desc, off_part1, off_part2, off_bkt, off_wtab, off_limit, total;
 };
+
+// Early exit: positions are read in rounds [t0, t1); limit[b] holds how many positions
+// of sequence b have been read (target and draft rows), with kStopBit set once one of
+// its tests has failed (nothing more of it is read).
+constexpr int32_t kStopBit = 0x40000000;
 
 // Pass-1 chunks of about kChunkBytes1 (long streams per workgroup), more when the batch
 // is too small to fill the chip, never shorter than kMinChunk1 elements.
@@ -138,6 +143,8 @@ inline Layout make_layout(int B, int K, int V, int esize, int rows_per_seq) {
     off = align256(off + sizeof(Bucket) * kBuckets * (size_t)B * L.nseg);
     L.off_wtab = off;
     if (esize == 2) off = align256(off + sizeof(double) * kWtabLen * (size_t)B);
+    L.off_limit = off;
+    off = align256(off + sizeof(int32_t) * (size_t)B);
     L.total = off;
     return L;
 }
@@ -169,6 +176,10 @@ struct VerifyArgs {
     // counter generator with these parameters; the resolve reads them after it
     float* u_gen;
     uint64_t seed, domain, step;
+    // early exit (null: every row is read): pass 1 and the prefix test take the positions
+    // [t0, t1) of the sequences still going; the resolve uses the rows read
+    int32_t* limit;
+    int t0, t1;
     int32_t* out_tokens;
     int32_t* out_n;            // may be null (plain sampling)
     float* out_p;
@@ -199,6 +210,8 @@ int launch_draw(const VerifyArgs& a, int bf16, int b0, int b1, void* stream);
 int launch_uniforms(uint64_t seed, uint64_t domain, uint64_t step, int B, int K, float* u,
                     void* stream);
 int launch_tree(const TreeArgs& a, void* stream);
+// Early exit: the tests of positions [a.t0, a.t1) of the sequences still going.
+int launch_prefix(const VerifyArgs& a, int bf16, void* stream);
 // sv_sample with at most kSampleMaxSeg segments per row: one workgroup per row.
 int launch_sample(const VerifyArgs& a, int bf16, void* stream);
 int launch_tree_mask(const TreeArgs& a, void* stream);

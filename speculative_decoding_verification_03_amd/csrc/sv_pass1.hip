@@ -204,6 +204,11 @@ __global__ __launch_bounds__(kThreads) void pass1_kernel(VerifyArgs a, int b0) {
     const bool is_target = j <= a.K;
     const int t = is_target ? j : j - a.K - 1;
     if (t > s.K || (!is_target && t == s.K)) return;  // past this sequence's drafts, or bad offsets
+    if (a.limit) {
+        // early exit: this round's positions of the sequences still going
+        if (t < a.t0 || t >= a.t1) return;
+        if (a.t0 > 0 && a.limit[b] != a.t0) return;
+    }
     const E* row = is_target ? static_cast<const E*>(a.target) + (s.t0 + t) * a.V
                              : static_cast<const E*>(a.draft) + (s.d0 + t) * a.V;
     const int lo = c * a.ch1;

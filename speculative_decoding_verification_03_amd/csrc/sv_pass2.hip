@@ -218,6 +218,18 @@ __device__ __forceinline__ double chunk_term(const VerifyArgs& a, const SeqRows&
     return q.s != 0.0 ? q.s * exp2_256(((double)q.m - (double)m) * ((double)c2 * 256.0), tab) : 0.0;
 }
 
+// The test of position t: r < p/q, i.e. r St < Sd 2^((ex - dxm) c2) with ex = zx - mt and
+// dxm = dx - md; q = 0 with p > 0 accepts, p = 0 rejects (2^y saturates to inf above and
+// to 0 below the fp64 range).
+__device__ __forceinline__ bool accept_test(const RowStat& rt, const RowStat& rd, float ut, double c256,
+                                            const double* tab) {
+    const double ex = (double)rt.zx - (double)rt.m, dxm = (double)rd.zx - (double)rd.m;
+    if (rt.zx == -INFINITY) return false;
+    if (rd.zx == -INFINITY) return true;
+    if (ut == 0.0f) return true;
+    return (double)ut * rt.S < rd.S * exp2_256((ex - dxm) * c256, tab);
+}
+
 // The resolve of sequence b by the whole workgroup of NT threads.  write: also write the
 // outputs (all but the drawn token of a sampled sequence, and its status).  Returns the
 // same SeqDesc in every thread, without the sign bracket of a residual draw (tau_lo,
@@ -291,15 +303,22 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
     // the rebasing exponentials of all (row, chunk) pairs first, one per thread, then one
     // thread per row
     const int nrows = sampled ? 2 * K + 1 : K + 1;
+    // early exit: only the rows of the first L positions were read
+    const int L = a.limit ? (a.limit[b] & ~kStopBit) : K + 1;
+    auto row_read = [&](int i) { return (i <= K ? i : i - K - 1) < L; };
     const bool by_pair = staged && sampled && nrows <= kRowsLds;
     if (by_pair) {
         for (int q = tid; q < nrows * a.nchunk1; q += NT) {
             const int i = q / a.nchunk1;
-            terms[q] = chunk_term(a, s, parts, i, q - i * a.nchunk1, c2, tab);
+            if (row_read(i)) terms[q] = chunk_term(a, s, parts, i, q - i * a.nchunk1, c2, tab);
         }
         __syncthreads();
     }
     for (int i = tid; i < nrows; i += NT) {
+        if (!row_read(i)) {
+            if (i < kRowsLds) rows[i] = RowStat{0.0f, -1, 1.0, -INFINITY};
+            continue;
+        }
         const RowStat r = staged ? merge_row(a, s, in, parts, i, sampled, c2, tab, by_pair ? terms : nullptr)
                                  : merge_row(a, s, in, src, i, sampled, c2, tab, nullptr);
         if (row_bad(r.m, sampled)) err |= kSeqErrLogit;
@@ -337,13 +356,14 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
     // are merged again by the thread that needs them)
     const double c256 = sampled ? 256.0 * kLog2eD / (double)T : 0.0;
     const bool all_lds = nrows <= kRowsLds;
+    const int Kt = min(K, L);  // positions whose rows were read (early exit: up to the stop)
     int first = K;
     if (!sampled) {
         for (int t = tid; t < K; t += NT) {
             if (write && op) op[t] = __builtin_nanf("");
             if (write && oq) oq[t] = __builtin_nanf("");
         }
-        for (int t = tid; t < K; t += NT)
+        for (int t = tid; t < Kt; t += NT)
             if (row(t).idx != in.token(t)) first = min(first, t);
     } else if (all_lds) {
         for (int q = tid; q < 3 * K; q += NT) {
@@ -352,34 +372,25 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
             // p = 2^((zx - mt) c2) / St and q = 2^((dx - md) c2) / Sd
             const double ex = (double)rt.zx - (double)rt.m, dxm = (double)rd.zx - (double)rd.m;
             if (kind == 1) {
-                if (write && op) op[t] = (float)(exp2_256(ex * c256, tab) / rt.S);
+                if (write && op) op[t] = t < Kt ? (float)(exp2_256(ex * c256, tab) / rt.S) : __builtin_nanf("");
             } else if (kind == 2) {
-                if (write && oq) oq[t] = (float)(exp2_256(dxm * c256, tab) / rd.S);
-            } else {
-                // r < p/q, i.e. r St < Sd 2^((ex - dxm) c2); q = 0 with p > 0 accepts,
-                // p = 0 rejects (2^y saturates to inf above and to 0 below the fp64 range)
-                const float ut = in.uniform(t);
-                bool accept;
-                if (rt.zx == -INFINITY) accept = false;
-                else if (rd.zx == -INFINITY) accept = true;
-                else if (ut == 0.0f) accept = true;
-                else accept = (double)ut * rt.S < rd.S * exp2_256((ex - dxm) * c256, tab);
-                if (!accept) first = min(first, t);
+                if (write && oq) oq[t] = t < Kt ? (float)(exp2_256(dxm * c256, tab) / rd.S) : __builtin_nanf("");
+            } else if (t < Kt) {
+                if (!accept_test(rt, rd, in.uniform(t), c256, tab)) first = min(first, t);
             }
         }
     } else {
         for (int t = tid; t < K; t += NT) {
+            if (t >= Kt) {
+                if (write && op) op[t] = __builtin_nanf("");
+                if (write && oq) oq[t] = __builtin_nanf("");
+                continue;
+            }
             const RowStat rt = row(t), rd = row(K + 1 + t);
             const double ex = (double)rt.zx - (double)rt.m, dxm = (double)rd.zx - (double)rd.m;
             if (write && op) op[t] = (float)(exp2_256(ex * c256, tab) / rt.S);
             if (write && oq) oq[t] = (float)(exp2_256(dxm * c256, tab) / rd.S);
-            const float ut = in.uniform(t);
-            bool accept;
-            if (rt.zx == -INFINITY) accept = false;
-            else if (rd.zx == -INFINITY) accept = true;
-            else if (ut == 0.0f) accept = true;
-            else accept = (double)ut * rt.S < rd.S * exp2_256((ex - dxm) * c256, tab);
-            if (!accept) first = min(first, t);
+            if (!accept_test(rt, rd, in.uniform(t), c256, tab)) first = min(first, t);
         }
     }
     const int n = block_min<NW>(first, shi);
@@ -1565,6 +1576,53 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(VerifyArgs a, int 
 }
 
 // ------------------------------------------------------------------------------------
+// early exit: the tests of one round of positions
+// ------------------------------------------------------------------------------------
+
+// grid = sequences.  For a sequence still going (limit == t0; every sequence in the first
+// round), the tests of positions [t0, min(t1, K)) from the rows pass 1 has just read, with
+// the resolve's arithmetic (merge_row, accept_test: the resolve, which tests these
+// positions again, reaches the same decisions).  limit becomes (n + 1) | kStopBit at the
+// first failing position n, else min(t1, K + 1).  Invalid data only ends the sequence;
+// the resolve reports it.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void prefix_kernel(VerifyArgs a) {
+    __shared__ double tab[kExpTable];
+    __shared__ int shi[kWaves];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    if (a.t0 > 0 && a.limit[b] != a.t0) return;  // whole workgroup: stopped earlier
+    exp2_table_init(tab);
+    const SeqRows s = seq_rows(a, b);
+    const int K = s.K;
+    const float T = a.temperature ? a.temperature[b] : 0.0f;
+    const bool sampled = !(T == 0.0f);
+    const float c2 = sampled ? (float)(kLog2eD / (double)T) : 0.0f;
+    const double c256 = sampled ? 256.0 * kLog2eD / (double)T : 0.0;
+    ResolveIn in;
+    in.x = a.tokens + s.d0;
+    in.u = a.uniforms ? a.uniforms + s.t0 : nullptr;
+    in.xs = in.x;  // tokens and uniforms straight from memory
+    in.us = in.u;
+    const RowPartial* parts = a.part1 + (int64_t)b * a.R * a.nchunk1;
+    const int te = min(a.t1, K);
+    int first = 0x7fffffff;
+    for (int t = a.t0 + tid; t < te; t += kThreads) {
+        const RowStat rt = merge_row(a, s, in, parts, t, sampled, c2, tab, nullptr);
+        bool ok;
+        if (!sampled) {
+            ok = rt.idx == in.x[t];
+        } else {
+            const RowStat rd = merge_row(a, s, in, parts, K + 1 + t, true, c2, tab, nullptr);
+            const float ut = in.u[t];
+            ok = (ut >= 0.0f && ut < 1.0f) && accept_test(rt, rd, ut, c256, tab);
+        }
+        if (!ok) first = min(first, t);
+    }
+    first = block_min(first, shi);
+    if (tid == 0) a.limit[b] = first != 0x7fffffff ? (first + 1) | kStopBit : min(a.t1, K + 1);
+}
+
+// ------------------------------------------------------------------------------------
 // the draft-side sampler: one draw per row from softmax(z / T), the whole row in one
 // workgroup
 // ------------------------------------------------------------------------------------
@@ -1772,6 +1830,15 @@ void launch_all(const VerifyArgs& a, int b0, int b1, hipStream_t s) {
     const unsigned blocks = (unsigned)((int64_t)(b1 - b0) * a.nchunk2);
     hipLaunchKernelGGL(sweep_kernel<E>, dim3(blocks), dim3(kSweepThreads), 0, s, a, b0);
     hipLaunchKernelGGL(final_kernel<E>, dim3((unsigned)(b1 - b0)), dim3(kFinalThreads), 0, s, a, b0);
+}
+
+int launch_prefix(const VerifyArgs& a, int bf16, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (bf16)
+        hipLaunchKernelGGL(prefix_kernel<uint16_t>, dim3((unsigned)a.B), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(prefix_kernel<float>, dim3((unsigned)a.B), dim3(kThreads), 0, s, a);
+    return (int)hipGetLastError();
 }
 
 int launch_sample(const VerifyArgs& a, int bf16, void* stream) {

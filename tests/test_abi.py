@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
         "spec_verify_greedy", "sv_fill_uniforms", "sv_profile_begin", "sv_profile_end",
         "spec_verify_ragged", "spec_verify_greedy_ragged", "sv_sample",
         "sv_fill_uniforms_ragged", "spec_verify_tree_greedy", "sv_tree_attention_mask",
-        "spec_verify_philox"])
+        "spec_verify_philox", "spec_verify_early_exit"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert sv.sv_abi_version() == 3
+    assert sv.sv_abi_version() == 4
     assert sv.sv_status_string(sv.SV_OK) == "ok"
     assert sv.sv_status_string(sv.SV_ERR_ARG) == "invalid argument"
     assert sv.sv_status_string(sv.SV_ERR_WORKSPACE).startswith("workspace")
@@ -116,6 +116,14 @@ def call_greedy(**kw):
 ])
 def test_spec_verify_rejects_bad_arguments(kw, status):
     assert call_verify(**kw) == status
+    # the early-exit entry point takes the same arguments and validates them alike
+    a = dict(t=GOOD, d=GOOD, dtype=sv.SV_DTYPE_BF16, x=GOOD, u=GOOD, T=GOOD, B=4, K=3, V=64,
+             tok=GOOD, n=GOOD, p=GOOD, q=GOOD, st=GOOD, ws=WS, wsb=1 << 30)
+    a.update(kw)
+    assert sv.lib().spec_verify_early_exit(
+        _p(a["t"]), _p(a["d"]), a["dtype"], _p(a["x"]), _p(a["u"]), _p(a["T"]), a["B"], a["K"],
+        a["V"], _p(a["tok"]), _p(a["n"]), _p(a["p"]), _p(a["q"]), _p(a["st"]), _p(a["ws"]),
+        a["wsb"], None) == status
 
 
 def test_spec_verify_edge_shapes_without_launch():

@@ -359,3 +359,43 @@ def test_philox_entry_point_equals_two_calls(dev, cfg, B):
         np.testing.assert_array_equal(f[k], a[k])
     for k in ("p", "q"):
         np.testing.assert_array_equal(f[k].view(np.uint32), a[k].view(np.uint32))
+
+
+def _assert_early_exit_matches(full, ee, K, what):
+    for k in ("tokens", "accept_len", "status"):
+        np.testing.assert_array_equal(ee[k], full[k], err_msg=f"{what}: {k}")
+    for k in ("p", "q"):
+        f, e = full[k], ee[k]
+        read = ~np.isnan(e)
+        np.testing.assert_array_equal(e[read].view(np.uint32), f[read].view(np.uint32),
+                                      err_msg=f"{what}: {k}")
+        # unread positions come after the sequence's first rejection
+        for b in range(f.shape[0]):
+            n = int(full["accept_len"][b])
+            miss = np.nonzero(~read[b])[0]
+            if len(miss) and not np.isnan(f[b]).all():
+                assert miss.min() > n, (what, b, n, miss.min())
+
+
+@pytest.mark.parametrize("cfg,B", [(4, None), (3, None), (2, None), (1, 700)])
+def test_early_exit_equals_full_read(dev, cfg, B):
+    """spec_verify_early_exit: the same tokens, accept lengths and statuses as spec_verify
+    bit for bit; p and q equal wherever the rows were read."""
+    inp = W.make_inputs(cfg, step=4, device=dev, B=B)
+    say(f"early exit: workload {cfg} B={inp['B']}")
+    u = sv.sv_fill_uniforms(1000 + cfg, 0, 4, inp["B"], inp["K"])
+    full = to_host(sv.spec_verify(inp["target"], inp["draft"], inp["tokens"], u, inp["temperature"]))
+    ee = to_host(sv.spec_verify_early_exit(inp["target"], inp["draft"], inp["tokens"], u,
+                                           inp["temperature"]))
+    _assert_early_exit_matches(full, ee, inp["K"], f"workload {cfg}")
+
+
+@pytest.mark.parametrize("case", range(len(EDGE)))
+def test_early_exit_edge_shapes(dev, case):
+    B, K, V, dt, temps = EDGE[case]
+    inp = random_case(dev, B, K, V, dt, temps, seed=700 + case, sigma=0.3)
+    u = gpu_uniforms(5 + case, 1, B, K)
+    full = to_host(sv.spec_verify(inp["target"], inp["draft"], inp["tokens"], u, inp["temperature"]))
+    ee = to_host(sv.spec_verify_early_exit(inp["target"], inp["draft"], inp["tokens"], u,
+                                           inp["temperature"]))
+    _assert_early_exit_matches(full, ee, K, f"edge {case}")
