@@ -8,7 +8,7 @@ spec_verify_philox (the uniforms come from the first workgroups of pass 1; with
 sequences, K=8 drafted tokens, V=152064 bf16 logits, Zipf(1.1)-offset target logits,
 T ~ U[0, 1.2] with a quarter of the sequences greedy (T = 0).  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload 4] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 40] [--workload 4] [--no-cpu-baseline]
                     [--path verify|ragged|sample|tree]
 
 --path ragged: spec_verify_ragged on the same rows with K_b uniform on 1..K per sequence
@@ -161,8 +161,8 @@ def cpu_baseline(sets, us, budget_s=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="verify", choices=["verify", "ragged", "sample", "tree"])
