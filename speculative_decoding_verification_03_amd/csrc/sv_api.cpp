@@ -64,7 +64,7 @@ size_t workspace_need(int B, int K, int V) {
 
 bool grid_ok(int B, int R, const Layout& L) {
     const __int128 blocks1 = (__int128)B * R * L.nchunk1;
-    const __int128 blocks2 = (__int128)B * L.nseg;
+    const __int128 blocks2 = ((__int128)B + 7) * L.nseg;  // the sweep pads B to whole rounds of 8 XCDs
     return blocks1 <= 0x7fffffff && blocks2 <= 0x7fffffff;
 }
 

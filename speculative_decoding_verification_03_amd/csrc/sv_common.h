@@ -167,6 +167,7 @@ struct VerifyArgs {
     int nchunk2, spc;          // draw chunking of this launch: chunks per sequence, segments
                                // per chunk
     int nseg;                  // draw segments per sequence
+    int nseq2;                 // sequences of this draw launch (set by the launcher)
     void* desc;                // [B] the resolve's result per sequence (kSeqDescBytes each)
     RowPartial* part1;         // [B][R][nchunk1]
     DrawPartial* part2;        // [B][nseg]

@@ -100,6 +100,8 @@ constexpr int kTabLen = 2 * kTabHalf;
 #endif
 constexpr int kG = SV_SWEEP_G;
 // Words of the fast path between scheduling fences (their table reads may overlap).
+constexpr unsigned kXcds = 8;  // XCDs of an MI355X
+
 #ifndef SV_SWEEP_WPF
 #define SV_SWEEP_WPF 4
 #endif
@@ -1493,7 +1495,8 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(VerifyArgs a, 
     }
 }
 
-// grid = sequences x nchunk2.  Sampled sequences: workgroup c sweeps segments
+// grid = (sequences rounded up to a multiple of kXcds) x nchunk2.  Sampled sequences:
+// workgroup c of a sequence sweeps segments
 // [c spc, (c + 1) spc) of the draw row(s), each wave a contiguous run of them, into
 // per-segment partials.
 template <typename E>
@@ -1502,8 +1505,15 @@ void sweep_kernel(VerifyArgs a, int b0) {
     constexpr int NW = kSweepThreads / 64;
     __shared__ double tab[kExpTable];
     __shared__ double wt[DrawLds<E>::kWt];
-    const int b = b0 + (int)(blockIdx.x / (unsigned)a.nchunk2);
-    const int c = (int)(blockIdx.x % (unsigned)a.nchunk2);
+    // workgroups are handed to the XCDs in turn (workgroup id mod kXcds): every chunk of
+    // sequence b0 + bl runs on XCD bl mod kXcds, like its resolve and final workgroups, so
+    // its weight table is fetched into one L2 (the grid is padded to whole rounds of kXcds
+    // sequences)
+    const unsigned x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+    const int bl = (int)(x + kXcds * (j / (unsigned)a.nchunk2));
+    if (bl >= a.nseq2) return;
+    const int b = b0 + bl;
+    const int c = (int)(j % (unsigned)a.nchunk2);
     const SeqDesc d = reinterpret_cast<const SeqDesc*>(a.desc)[b];
     if (d.mode == kModeNone) return;  // whole workgroup
     DrawRows<E> r = draw_rows<E>(a, b, d, tab, wt);
@@ -1827,8 +1837,11 @@ template <typename E>
 void launch_all(const VerifyArgs& a, int b0, int b1, hipStream_t s) {
     hipLaunchKernelGGL(resolve_kernel<E>, dim3((unsigned)(b1 - b0)), dim3(kResolveThreads), 0, s, a, b0);
     if (!a.temperature) return;  // greedy only: the resolve is everything
-    const unsigned blocks = (unsigned)((int64_t)(b1 - b0) * a.nchunk2);
-    hipLaunchKernelGGL(sweep_kernel<E>, dim3(blocks), dim3(kSweepThreads), 0, s, a, b0);
+    VerifyArgs a2 = a;
+    a2.nseq2 = b1 - b0;
+    const int64_t padded = ((int64_t)(b1 - b0) + kXcds - 1) / kXcds * kXcds;
+    const unsigned blocks = (unsigned)(padded * a.nchunk2);
+    hipLaunchKernelGGL(sweep_kernel<E>, dim3(blocks), dim3(kSweepThreads), 0, s, a2, b0);
     hipLaunchKernelGGL(final_kernel<E>, dim3((unsigned)(b1 - b0)), dim3(kFinalThreads), 0, s, a, b0);
 }
 
