@@ -95,6 +95,8 @@ sv::VerifyArgs make_args(const void* target, const void* draft, const int32_t* t
     a.part2 = reinterpret_cast<sv::DrawPartial*>(ws + L.off_part2);
     a.bkt = reinterpret_cast<sv::Bucket*>(ws + L.off_bkt);
     a.wtab = reinterpret_cast<double*>(ws + L.off_wtab);
+    a.deal = temperature ? reinterpret_cast<int32_t*>(ws + L.off_deal) : nullptr;
+    a.deal_desc = temperature ? ws + L.off_deal_desc : nullptr;
     a.out_tokens = out_tokens;
     a.out_n = out_n;
     a.out_p = out_p;

@@ -63,7 +63,7 @@ constexpr int kSeqDescBytes = 64;  // workspace slot of the resolve's per-sequen
 struct Layout {
     int nchunk1, ch1;  // pass-1 chunks per row and elements per chunk (multiple of 64)
     int nseg;          // draw segments per sequence: ceil(V / kSeg)
-    size_t off_desc, off_part1, off_part2, off_bkt, off_wtab, off_limit, total;
+    size_t off_desc, off_part1, off_part2, off_bkt, off_wtab, off_limit, off_deal, off_deal_desc, total;
 };
 
 // Early exit: positions are read in rounds [t0, t1); limit[b] holds how many positions
@@ -145,6 +145,10 @@ inline Layout make_layout(int B, int K, int V, int esize, int rows_per_seq) {
     if (esize == 2) off = align256(off + sizeof(double) * kWtabLen * (size_t)B);
     L.off_limit = off;
     off = align256(off + sizeof(int32_t) * (size_t)B);
+    L.off_deal = off;
+    off = align256(off + 2 * sizeof(int32_t));
+    L.off_deal_desc = off;
+    off = align256(off + kSeqDescBytes * (size_t)B);
     L.total = off;
     return L;
 }
@@ -168,6 +172,13 @@ struct VerifyArgs {
                                // per chunk
     int nseg;                  // draw segments per sequence
     int nseq2;                 // sequences of this draw launch (set by the launcher)
+    // The draw deal of this call (null when no draw follows): deal_desc[nseq2] descriptors
+    // (kSeqDescBytes each) and deal[2] counts.  Pass 1 resets it (counts 0, every entry's
+    // mode kModeNone); each resolve workgroup with a draw copies its descriptor into it,
+    // residual draws from the front, bonus draws from the back, deal[0] and deal[1]
+    // counting them.
+    int32_t* deal;
+    void* deal_desc;
     void* desc;                // [B] the resolve's result per sequence (kSeqDescBytes each)
     RowPartial* part1;         // [B][R][nchunk1]
     DrawPartial* part2;        // [B][nseg]

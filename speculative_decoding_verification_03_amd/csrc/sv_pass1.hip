@@ -186,6 +186,13 @@ __device__ void tile_argmax(const E* row, int lo, int hi, RowPartial* out) {
 template <typename E>
 __global__ __launch_bounds__(kThreads) void pass1_kernel(VerifyArgs a, int b0) {
     const int64_t blk = blockIdx.x;
+    if (a.deal) {
+        // the draw deal starts empty: no entries (a descriptor's mode is its first field)
+        // and zero counts; the grid has at least B workgroups
+        const int64_t i = blk * kThreads + threadIdx.x;
+        if (i < a.B) reinterpret_cast<int32_t*>(static_cast<char*>(a.deal_desc) + i * kSeqDescBytes)[0] = kModeNone;
+        else if (i < (int64_t)a.B + 2) a.deal[i - a.B] = 0;
+    }
     if (a.u_gen) {
         // the uniforms of the call, one per thread of the first workgroups
         const int64_t i = blk * kThreads + threadIdx.x;

@@ -42,6 +42,7 @@
 #include <float.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stddef.h>
 
 #include "sv_common.h"
 #include "sv_device.h"
@@ -117,6 +118,7 @@ struct SeqDesc {
     float T;       // temperature
     float u;       // uniform of the final draw
     float mt, md;  // maxima of target row n and draft row n
+    int b;         // the sequence
     // residual draws: the bracket [tau_lo, tau_hi] on zt_i - zd_i around the sign threshold
     // T ln(St/Sd) + mt - md, St and Sd the pass-1 normalisers sum exp((z - m) / T) of the
     // two rows
@@ -1472,6 +1474,7 @@ struct DrawLds {
 
 static_assert(sizeof(SeqDesc) <= kSeqDescBytes && kSeqDescBytes % alignof(SeqDesc) == 0,
               "workspace slot of the descriptor");
+static_assert(offsetof(SeqDesc, mode) == 0, "pass 1 clears deal entries through their first field");
 
 // grid = sequences: the resolve.  Writes the outputs (all but a sampled sequence's drawn
 // token and status), the sequence's SeqDesc and, for bf16 draws with one reference, the
@@ -1483,16 +1486,24 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(VerifyArgs a, 
     exp2_table_init(tab);
     double St, Sd;
     SeqDesc d = resolve_seq<E, kResolveThreads>(a, b, true, tab, St, Sd);
-    // thread 0 finishes the descriptor while the others start on the weight table
+    d.b = b;
+    // thread 0 takes the draw's slot in the deal (residual draws, two rows, from the front;
+    // bonus draws, one row, from the back; the atomic's round trip overlaps the weight
+    // table) and finishes the descriptor while the others start on the table
+    int slot = -1;
     if (threadIdx.x == 0) {
+        if (a.deal && (d.mode == kModeResidual || d.mode == kModeBonus))
+            slot = d.mode == kModeResidual ? atomicAdd(&a.deal[0], 1) : a.nseq2 - 1 - atomicAdd(&a.deal[1], 1);
         desc_bracket(d, St, Sd);
         reinterpret_cast<SeqDesc*>(a.desc)[b] = d;
     }
     if constexpr (sizeof(E) == 2) {
-        if (d.mode == kModeNone) return;
-        const DrawRows<E> r = draw_rows<E>(a, b, d, tab, nullptr);  // the bracket is not used
-        if (r.one_ref) weight_table_write<E, kResolveThreads>(r, a.wtab + (int64_t)b * kWtabLen);
+        if (d.mode != kModeNone) {
+            const DrawRows<E> r = draw_rows<E>(a, b, d, tab, nullptr);  // the bracket is not used
+            if (r.one_ref) weight_table_write<E, kResolveThreads>(r, a.wtab + (int64_t)b * kWtabLen);
+        }
     }
+    if (slot >= 0) reinterpret_cast<SeqDesc*>(a.deal_desc)[slot] = d;
 }
 
 // grid = (sequences rounded up to a multiple of kXcds) x nchunk2.  Sampled sequences:
@@ -1506,16 +1517,20 @@ void sweep_kernel(VerifyArgs a, int b0) {
     __shared__ double tab[kExpTable];
     __shared__ double wt[DrawLds<E>::kWt];
     // workgroups are handed to the XCDs in turn (workgroup id mod kXcds): every chunk of
-    // sequence b0 + bl runs on XCD bl mod kXcds, like its resolve and final workgroups, so
-    // its weight table is fetched into one L2 (the grid is padded to whole rounds of kXcds
-    // sequences)
+    // entry k runs on XCD k mod kXcds, so a sequence's weight table is fetched into one
+    // L2.  Entry k is the deal's (the draws dealt over the XCDs in turn, two-row residual
+    // draws first, which balances the XCDs' work when the sweep takes several rounds of
+    // workgroups; the entries between the two kinds of draws are empty), or else
+    // sequence b0 + k, on the XCD of its resolve and final workgroups.  The grid is padded
+    // to whole rounds of kXcds entries.
     const unsigned x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
-    const int bl = (int)(x + kXcds * (j / (unsigned)a.nchunk2));
-    if (bl >= a.nseq2) return;
-    const int b = b0 + bl;
+    const int k = (int)(x + kXcds * (j / (unsigned)a.nchunk2));
+    if (k >= a.nseq2) return;
+    const SeqDesc d = a.deal ? reinterpret_cast<const SeqDesc*>(a.deal_desc)[k]
+                             : reinterpret_cast<const SeqDesc*>(a.desc)[b0 + k];
+    if (d.mode == kModeNone || d.b < b0 || d.b >= b0 + a.nseq2) return;  // whole workgroup
+    const int b = d.b;
     const int c = (int)(j % (unsigned)a.nchunk2);
-    const SeqDesc d = reinterpret_cast<const SeqDesc*>(a.desc)[b];
-    if (d.mode == kModeNone) return;  // whole workgroup
     DrawRows<E> r = draw_rows<E>(a, b, d, tab, wt);
     const int w = threadIdx.x >> 6;
     SweepAcc acc;
@@ -1833,16 +1848,35 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(VerifyArgs a) {
 
 }  // namespace
 
+// Waves the sweep keeps resident on the current device (kDrawWaves per SIMD, 4 SIMDs per
+// compute unit), cached per device.
+int sweep_resident_waves() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1 << 30;
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return 1 << 30;
+        cache[dev] = cus * 4 * SV_DRAW_WAVES;
+    }
+    return cache[dev];
+}
+
 template <typename E>
 void launch_all(const VerifyArgs& a, int b0, int b1, hipStream_t s) {
-    hipLaunchKernelGGL(resolve_kernel<E>, dim3((unsigned)(b1 - b0)), dim3(kResolveThreads), 0, s, a, b0);
-    if (!a.temperature) return;  // greedy only: the resolve is everything
     VerifyArgs a2 = a;
     a2.nseq2 = b1 - b0;
+    // deal the draws over the XCDs only when the sweep takes more than one round of
+    // resident waves: in a single round every workgroup runs at once and nothing is gained
+    const int64_t sweep_waves = (int64_t)(b1 - b0) * a.nchunk2 * (kSweepThreads / 64);
+    if (!a.temperature || sweep_waves <= sweep_resident_waves()) a2.deal = nullptr;
+    hipLaunchKernelGGL(resolve_kernel<E>, dim3((unsigned)(b1 - b0)), dim3(kResolveThreads), 0, s, a2, b0);
+    if (!a.temperature) return;  // greedy only: the resolve is everything
     const int64_t padded = ((int64_t)(b1 - b0) + kXcds - 1) / kXcds * kXcds;
     const unsigned blocks = (unsigned)(padded * a.nchunk2);
     hipLaunchKernelGGL(sweep_kernel<E>, dim3(blocks), dim3(kSweepThreads), 0, s, a2, b0);
-    hipLaunchKernelGGL(final_kernel<E>, dim3((unsigned)(b1 - b0)), dim3(kFinalThreads), 0, s, a, b0);
+    hipLaunchKernelGGL(final_kernel<E>, dim3((unsigned)(b1 - b0)), dim3(kFinalThreads), 0, s, a2, b0);
 }
 
 int launch_prefix(const VerifyArgs& a, int bf16, void* stream) {
