@@ -303,6 +303,40 @@ def test_data_errors_flagged_like_oracle(dev):
     g.assert_ok("data errors greedy")
 
 
+def test_draw_deal_many_rounds(dev):
+    """Enough draws that the sweep takes several rounds of resident waves (512 sequences x
+    3 chunks x 4 waves against 16 waves on each of 256 compute units), so the draws are
+    dealt over the XCDs: greedy sequences, drafts that nearly copy the target (mostly
+    bonus draws), noisy drafts (residual draws) and sequences with bad data, mixed.  The
+    deal's order depends on which resolve takes a slot first; results may not."""
+    B, K, V = 512, 3, 40000
+    say(f"draw deal: B={B} K={K} V={V} bf16")
+    g = torch.Generator(device=dev).manual_seed(77)
+    rng = np.random.default_rng(77)
+    temps = [0.0 if b % 4 == 1 else float(rng.uniform(0.3, 1.5)) for b in range(B)]
+    sig = torch.tensor([0.02 if b % 3 == 0 else 1.0 for b in range(B)], device=dev).view(B, 1, 1)
+    zt = 2.0 * torch.randn((B, K + 1, V), generator=g, device=dev)
+    zd = zt[:, :K] + sig * torch.randn((B, K, V), generator=g, device=dev)
+    T = torch.tensor(temps, dtype=torch.float32)
+    inp = dict(target=zt.to(torch.bfloat16).contiguous(), draft=zd.to(torch.bfloat16).contiguous(),
+               temperature=T.to(dev))
+    inp["tokens"] = W._draft_tokens(inp["draft"], T, g)
+    inp["target"][6, 2, 123] = float("nan")   # bad data in sampled sequences
+    inp["tokens"][10, 1] = V
+    u = gpu_uniforms(77, 0, B, K)
+    a = run_sampled(inp, u)
+    b = run_sampled(inp, u)
+    for k in a:
+        if a[k] is not None:
+            assert np.array_equal(a[k], b[k], equal_nan=True), k
+    n = a["accept_len"]
+    sampled = np.array(temps) != 0.0
+    say(f"   bonus draws {int(((n == K) & sampled).sum())}, residual draws {int(((n < K) & (n >= 0) & sampled).sum())}")
+    t = compare(a, oracle_sampled(inp, u), range(B), T)
+    say("  ", t)
+    t.assert_ok("draw deal")
+
+
 def test_small_temperature_equals_greedy(dev):
     say("T -> 0 against greedy")
     B, K, V = 32, 5, 20000
