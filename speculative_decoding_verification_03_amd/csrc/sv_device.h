@@ -72,10 +72,10 @@ struct Logit<uint16_t> {
 
 constexpr int kExpTable = 256;
 
-// Fill the table (kExpTable doubles of LDS) once per workgroup; contains __syncthreads().
+// Fill the table (kExpTable doubles of LDS) once per workgroup, without a barrier:
 // 2^x for x = j/256 in [0, 1) from the Taylor series of exp(x ln2) to degree 17 (truncation
 // below 2e-19), evaluated by Horner: a few registers, unlike a library exp2.
-__device__ __forceinline__ void exp2_table_init(double* t) {
+__device__ __forceinline__ void exp2_table_fill(double* t) {
     constexpr double c[18] = {1.0,
                               0.6931471805599453,
                               0.2402265069591007,
@@ -101,6 +101,11 @@ __device__ __forceinline__ void exp2_table_init(double* t) {
         for (int n = 16; n >= 0; --n) p = __builtin_fma(p, x, c[n]);
         t[j] = p;
     }
+}
+
+// The same, then __syncthreads().
+__device__ __forceinline__ void exp2_table_init(double* t) {
+    exp2_table_fill(t);
     __syncthreads();
 }
 

@@ -222,6 +222,73 @@ __device__ __forceinline__ double chunk_term(const VerifyArgs& a, const SeqRows&
     return q.s != 0.0 ? q.s * exp2_256(((double)q.m - (double)m) * ((double)c2 * 256.0), tab) : 0.0;
 }
 
+// Every row of the sequence from its partials in LDS, by lane groups: G lanes per row (G the
+// power of two at or above nchunk1), chunk c of row i on thread i G + c, which the caller
+// guarantees covers them (G <= 64, so that a group lies inside one wave; nrows <= kRowsLds;
+// nrows G <= blockDim.x).  Group maxima by
+// shuffles; the rebased sums added in chunk order with the very operations of merge_row,
+// so the result has merge_row's bits.  Rows past the first L positions (early exit) get
+// the placeholder of rows not read.  Returns this thread's error bits.
+__device__ __forceinline__ int merge_rows_grouped(const VerifyArgs& a, const SeqRows& s, const ResolveIn& in,
+                                                  const RowPartial* parts, int nrows, bool sampled, float c2,
+                                                  const double* tab, int L, RowStat* rows) {
+    const int nc = a.nchunk1;
+    int lg = 0;
+    while ((1 << lg) < nc) ++lg;
+    const int tid = threadIdx.x, i = tid >> lg, c = tid & ((1 << lg) - 1);
+    const int base = (tid & 63) - c;  // lane of the group's chunk 0
+    if (i >= nrows) return 0;  // whole groups
+    const bool is_target = i <= s.K;
+    const int t = is_target ? i : i - s.K - 1;
+    if (t >= L) {
+        if (c == 0) rows[i] = RowStat{0.0f, -1, 1.0, -INFINITY};
+        return 0;
+    }
+    const int j = is_target ? t : a.K + 1 + t;  // workspace slot (dense layout, K the bound)
+    const bool live = c < nc;
+    RowPartial q;
+    q.m = -INFINITY;
+    q.idx = 0;
+    q.s = 0.0;
+    if (live) q = parts[(int64_t)j * nc + c];
+    RowStat r{-INFINITY, 0x7fffffff, 0.0, -INFINITY};
+    if (!sampled) {
+        // the strict maximum over chunks in order: the first chunk reaching the maximum of
+        // the chunk maxima that are not NaN; any NaN marks the row
+        const bool nan = live && q.m != q.m;
+        float m = nan ? -INFINITY : q.m;
+        for (int o = 1; o < (1 << lg); o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        int first = (live && !nan && q.m == m && m > -INFINITY) ? c : 0x7fff;
+        int bad = nan;
+        for (int o = 1; o < (1 << lg); o <<= 1) {
+            first = min(first, __shfl_xor(first, o, 64));
+            bad |= __shfl_xor(bad, o, 64);
+        }
+        const int idx = __shfl(q.idx, base + (first == 0x7fff ? 0 : first), 64);
+        r.m = bad ? __builtin_nanf("") : m;
+        r.idx = first == 0x7fff ? 0x7fffffff : idx;
+    } else {
+        float m = q.m;
+        for (int o = 1; o < (1 << lg); o <<= 1) m = nmax(m, __shfl_xor(m, o, 64));
+        r.m = m;
+        const double term = (live && q.s != 0.0)
+                                ? q.s * exp2_256(((double)q.m - (double)m) * ((double)c2 * 256.0), tab)
+                                : 0.0;
+        for (int cc = 0; cc < nc; ++cc) r.S += __shfl(term, base + cc, 64);
+        // the chunk holding this row's draft token recorded the logit there
+        int cx = -1;
+        if (t < s.K) {
+            const int x = in.token(t);
+            if (x >= 0 && x < a.V) cx = x / a.ch1;
+        }
+        const int zbits = __shfl(q.idx, base + (cx < 0 ? 0 : cx), 64);
+        r.zx = cx < 0 ? -INFINITY : __int_as_float(zbits);
+    }
+    if (c != 0) return 0;
+    if (i < kRowsLds) rows[i] = r;
+    return row_bad(r.m, sampled) ? kSeqErrLogit : 0;
+}
+
 // The test of position t: r < p/q, i.e. r St < Sd 2^((ex - dxm) c2) with ex = zx - mt and
 // dxm = dx - md; q = 0 with p > 0 accepts, p = 0 rejects (2^y saturates to inf above and
 // to 0 below the fp64 range).
@@ -239,7 +306,7 @@ __device__ __forceinline__ bool accept_test(const RowStat& rt, const RowStat& rd
 // same SeqDesc in every thread, without the sign bracket of a residual draw (tau_lo,
 // tau_hi; see desc_bracket).  Contains __syncthreads().
 template <typename E, int NT>
-__device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool write, const double* tab,
+__device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool write, double* tab,
                                                double& St, double& Sd) {
     constexpr int NW = NT / 64;
     __shared__ RowStat rows[kRowsLds];
@@ -274,10 +341,11 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
     const int nparts = a.R * a.nchunk1;
     const RowPartial* src = a.part1 + (int64_t)b * nparts;
     const bool staged = nparts <= kPartsLds;
-    if (staged) {
+    const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+    u32x4* d4 = reinterpret_cast<u32x4*>(parts);
+    constexpr bool one_load = NT >= kPartsLds;  // one 16-byte load per thread stages them all
+    if (staged && !one_load) {
         // two 16-byte loads in flight per thread (indices clamped, stores guarded)
-        const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
-        u32x4* d4 = reinterpret_cast<u32x4*>(parts);
         for (int i0 = 0; i0 < nparts; i0 += 2 * NT) {
             const int i1 = i0 + tid, i2 = i0 + NT + tid;
             const u32x4 q1 = s4[min(i1, nparts - 1)];
@@ -286,9 +354,19 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
             if (i2 < nparts) d4[i2] = q2;
         }
     }
-    if (tid < K && tid < kRowsLds) xs[tid] = in.x[tid];
-    if (in.u && tid <= K && tid <= kRowsLds) us[tid] = in.u[tid];
-    __syncthreads();
+    const bool mine = staged && one_load && tid < nparts;
+    const bool has_x = tid < K && tid < kRowsLds, has_u = in.u && tid <= K && tid <= kRowsLds;
+    u32x4 qp{0u, 0u, 0u, 0u};
+    int xv = 0;
+    float uv = 0.0f;
+    if (mine) qp = s4[tid];
+    if (has_x) xv = in.x[tid];
+    if (has_u) uv = in.u[tid];
+    exp2_table_fill(tab);  // while the loads are in flight
+    if (mine) d4[tid] = qp;
+    if (has_x) xs[tid] = xv;
+    if (has_u) us[tid] = uv;
+    __syncthreads();  // publishes the staging and the exponential table
     const bool sampled = !(T == 0.0f);
     const float c2 = sampled ? (float)(kLog2eD / (double)T) : 0.0f;
 
@@ -310,7 +388,13 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
     // early exit: only the rows of the first L positions were read
     const int L = a.limit ? (a.limit[b] & ~kStopBit) : K + 1;
     auto row_read = [&](int i) { return (i <= K ? i : i - K - 1) < L; };
-    const bool by_pair = staged && sampled && nrows <= kRowsLds;
+    int lg = 0;
+    while ((1 << lg) < a.nchunk1) ++lg;
+    // lane groups stay inside one wave (16 lanes at most: the chunk-order sum takes one
+    // shuffle per chunk)
+    const bool grouped = staged && lg <= 4 && nrows <= kRowsLds && (nrows << lg) <= NT;
+    const bool by_pair = !grouped && staged && sampled && nrows <= kRowsLds;
+    if (grouped) err |= merge_rows_grouped(a, s, in, parts, nrows, sampled, c2, tab, L, rows);
     if (by_pair) {
         for (int q = tid; q < nrows * a.nchunk1; q += NT) {
             const int i = q / a.nchunk1;
@@ -318,7 +402,7 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
         }
         __syncthreads();
     }
-    for (int i = tid; i < nrows; i += NT) {
+    for (int i = grouped ? nrows : tid; i < nrows; i += NT) {
         if (!row_read(i)) {
             if (i < kRowsLds) rows[i] = RowStat{0.0f, -1, 1.0, -INFINITY};
             continue;
@@ -571,6 +655,7 @@ static_assert(kTabLen == kWtabLen, "workspace slot of the weight table");
 // DrawRows evaluates without the table.
 template <typename E, int NT = kThreads>
 __device__ __forceinline__ void weight_table_write(const DrawRows<E>& r, double* dst) {
+#pragma unroll 4
     for (int k = threadIdx.x; k < kTabLen; k += NT) {
         const uint32_t q = (uint32_t)k & (kTabHalf - 1);
         double v = 0.0;
@@ -1483,9 +1568,8 @@ template <typename E>
 __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(VerifyArgs a, int b0) {
     __shared__ double tab[kExpTable];
     const int b = b0 + (int)blockIdx.x;
-    exp2_table_init(tab);
     double St, Sd;
-    SeqDesc d = resolve_seq<E, kResolveThreads>(a, b, true, tab, St, Sd);
+    SeqDesc d = resolve_seq<E, kResolveThreads>(a, b, true, tab, St, Sd);  // fills tab
     d.b = b;
     // thread 0 takes the draw's slot in the deal (residual draws, two rows, from the front;
     // bonus draws, one row, from the back; the atomic's round trip overlaps the weight
