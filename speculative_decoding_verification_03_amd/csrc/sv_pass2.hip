@@ -65,6 +65,7 @@ constexpr double kFlushLog2 = 70.0;
 constexpr double kMaxRefGapLog2 = 900.0;
 // Row statistics of the resolve kept in LDS; rows past this are merged again on demand.
 constexpr int kRowsLds = 64;
+static_assert(kRowsLds <= 64, "with every row in LDS (2K + 1 <= kRowsLds) one wave holds the K tests");
 // Pass-1 partials of one sequence the resolve stages in LDS (16 KB); more stay in memory.
 constexpr int kPartsLds = 1024;
 // Threads of a resolve workgroup (one workgroup per sequence).
@@ -453,6 +454,21 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
         }
         for (int t = tid; t < Kt; t += NT)
             if (row(t).idx != in.token(t)) first = min(first, t);
+    } else if (all_lds && NT >= 192) {
+        // the tests on wave 0, p on wave 1, q on wave 2 (K < kRowsLds <= 64 here): no wave
+        // runs more than one kind
+        const int kind = tid >> 6, t = tid & 63;
+        if (kind < 3 && t < K) {
+            const RowStat rt = rows[t], rd = rows[K + 1 + t];
+            const double ex = (double)rt.zx - (double)rt.m, dxm = (double)rd.zx - (double)rd.m;
+            if (kind == 1) {
+                if (write && op) op[t] = t < Kt ? (float)(exp2_256(ex * c256, tab) / rt.S) : __builtin_nanf("");
+            } else if (kind == 2) {
+                if (write && oq) oq[t] = t < Kt ? (float)(exp2_256(dxm * c256, tab) / rd.S) : __builtin_nanf("");
+            } else if (t < Kt) {
+                if (!accept_test(rt, rd, in.uniform(t), c256, tab)) first = t;
+            }
+        }
     } else if (all_lds) {
         for (int q = tid; q < 3 * K; q += NT) {
             const int kind = q / K, t = q - kind * K;
