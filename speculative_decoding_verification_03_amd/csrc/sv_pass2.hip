@@ -1753,9 +1753,11 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(VerifyArgs a) {
 // ------------------------------------------------------------------------------------
 
 // One wave's fp64 sum of the bonus weights over positions [lo, hi) of r.t: the table fast
-// path over a whole segment of 16-byte vectors when it applies (a value outside the table,
-// NaN and infinities included, reads NaN and sends the segment through the exact path),
-// the exact path otherwise.  bad: the exact path met a NaN or +inf logit (wave-uniform).
+// path over a whole segment of 16-byte vectors when it applies, the exact path otherwise.
+// On the fast path a value outside the table reads NaN: its lane's vector is read again
+// (from cache) and its values outside the table take the fp64 exponential (the callers
+// have ruled out NaN and +inf logits).  bad: the exact path met a NaN or +inf logit
+// (wave-uniform).
 template <typename E>
 __device__ __forceinline__ double wave_row_sum(const DrawRows<E>& r, int lo, int hi, bool& bad) {
     constexpr int VEC = Logit<E>::kVec;
@@ -1768,18 +1770,35 @@ __device__ __forceinline__ double wave_row_sum(const DrawRows<E>& r, int lo, int
             u32x4 v[kU];  // every load of the segment in flight at once
 #pragma unroll
             for (int k = 0; k < kU; ++k) v[k] = load16(r.t + lo + (k * 64 + lane) * VEC);
+            uint32_t again = 0;  // this lane's vectors with a value outside the table
 #pragma unroll
             for (int k = 0; k < kU; ++k) {
                 const uint32_t x4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+                double sk = 0.0;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     uint32_t o0, o1;
                     tab_offsets(x4[q], o0, o1);
-                    s += tab_at(r.wt, o0);
-                    s += tab_at(r.wt, o1);
+                    sk += tab_at(r.wt, o0);
+                    sk += tab_at(r.wt, o1);
                 }
+                if (sk != sk) again |= 1u << k;
+                else s += sk;
             }
-            exact = __any(s != s);
+            while (again) {  // rare
+                const int k = __ffs(again) - 1;
+                again &= again - 1;
+                const u32x4 w = load16(r.t + lo + (k * 64 + lane) * VEC);
+                const uint32_t x4[4] = {w.x, w.y, w.z, w.w};
+                double sk = 0.0;
+#pragma unroll 1
+                for (int q = 0; q < 8; ++q) {
+                    const uint32_t h = (x4[q >> 1] >> (16 * (q & 1))) & 0xffffu;
+                    sk += r.a_of(__uint_as_float(h << 16));
+                }
+                s += sk;
+            }
+            exact = false;
         }
     }
     bool b = false;
