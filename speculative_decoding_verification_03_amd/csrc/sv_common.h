@@ -57,7 +57,7 @@ struct alignas(16) Bucket {
 };
 
 constexpr int kSeg = 4096;         // positions per draw segment (one partial each)
-constexpr int kWtabLen = 4096;     // doubles per sequence of the bf16 weight table
+constexpr int kWtabLen = 4356;     // doubles per sequence of the bf16 weight table
 constexpr int kSeqDescBytes = 64;  // workspace slot of the resolve's per-sequence result
 
 struct Layout {

@@ -20,7 +20,7 @@
 // Weights.  a_i = 2^((zt_i - refA) c2), b_i = 2^((zd_i - refB) c2), c2 = log2(e)/T, so that
 // p_i = a_i / S_p and q_i = b_i / S_q.  Both rows share one reference (the larger row
 // maximum) unless that would push the smaller row toward fp64 underflow.  For bf16 logits
-// the resolve tabulates the weight of every bf16 value with |z| in [2^-10, 32) (3840
+// the resolve tabulates the weight of every bf16 value with |z| in [2^-12, 32) (4352
 // doubles); the sweep and final kernels copy the table into LDS and look weights up.
 // Other values, and fp32 logits, take the fp64 exponential of sv_device.h.  A weight so
 // computed below 2^-70 of its row maximum counts as 0: over any vocabulary that moves the
@@ -79,16 +79,16 @@ constexpr int kResolveThreads = SV_RESOLVE_THREADS;
 #endif
 constexpr int kFinalThreads = SV_FINAL_THREADS;
 
-// bf16 weight table in LDS: two halves of kTabHalf slots (positive, then negative values).
-// Slot q of a half holds the weight of the bf16 value whose 15-bit magnitude field is
-// kTabLo + q, for q in [1, kTabN]: biased exponents 117..131, |z| in [2^-10, 32).  Slots 0
-// and kTabN + 1 hold NaN: a magnitude outside the range is clamped onto them, so a sum
-// that met one turns NaN and its span is redone exactly.
-constexpr uint32_t kTabLo = 117 * 128 - 1;
-constexpr int kTabN = 15 * 128;
+// bf16 weight table in LDS, the signs interleaved: slot 2q + s holds the weight of the bf16
+// value with sign s whose 15-bit magnitude field is kTabLo + q, for q in [1, kTabN]: biased
+// exponents 115..131, |z| in [2^-12, 32), the widest range in which the difference of two
+// of its values is exact in fp32 (16 binary orders apart at most, 8 significant bits
+// each).  Slots of q = 0 and q = kTabN + 1 hold NaN: a magnitude outside the range is
+// clamped onto them, so a sum that met one turns NaN and its span is redone exactly.
+constexpr uint32_t kTabLo = 115 * 128 - 1;
+constexpr int kTabN = 17 * 128;
 constexpr uint32_t kTabHi = kTabLo + kTabN + 1;
-constexpr int kTabHalf = 2048;
-constexpr int kTabLen = 2 * kTabHalf;
+constexpr int kTabLen = 2 * (kTabN + 2);
 
 // Waves per SIMD the sweep kernel's register allocation must allow (4 workgroups per CU).
 #ifndef SV_DRAW_WAVES
@@ -551,22 +551,23 @@ __device__ __forceinline__ void desc_bracket(SeqDesc& d, double St, double Sd) {
 // outside the table land on a NaN slot.
 __device__ __forceinline__ uint32_t tab_slot(uint32_t x) {
     const uint32_t t = min(max(x & 0x7fffu, kTabLo), kTabHi);
-    return (t - kTabLo) + ((x >> 4) & 0x800u);
+    return 2 * (t - kTabLo) + ((x >> 15) & 1u);
 }
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Byte offsets into the table of the two bf16 values packed in x (o0: low half, o1: high
 // half): 8 tab_slot(...) of each, both halves at once with packed 16-bit integer
-// arithmetic (saturating subtract, minimum, shift).
+// arithmetic (saturating subtract, minimum, shift; 16 (kTabN + 1) + 8 < 2^16).
+static_assert(16 * (kTabN + 1) + 8 < 65536, "table byte offsets fit 16 bits");
 __device__ __forceinline__ void tab_offsets(uint32_t x, uint32_t& o0, uint32_t& o1) {
     const u16x2 m = __builtin_bit_cast(u16x2, x & 0x7fff7fffu);
     const u16x2 lo = {(unsigned short)kTabLo, (unsigned short)kTabLo};
     const u16x2 top = {(unsigned short)(kTabN + 1), (unsigned short)(kTabN + 1)};
     u16x2 c = __builtin_elementwise_sub_sat(m, lo);  // magnitude - kTabLo, or 0 below
     c = __builtin_elementwise_min(c, top);           // kTabN + 1 above
-    c = c << (unsigned short)3;
-    const uint32_t off = __builtin_bit_cast(uint32_t, c) | ((x >> 1) & 0x40004000u);  // + sign half
+    c = c << (unsigned short)4;
+    const uint32_t off = __builtin_bit_cast(uint32_t, c) | ((x >> 12) & 0x00080008u);  // + 8 sign
     o0 = off & 0xffffu;
     o1 = off >> 16;
 }
@@ -578,7 +579,7 @@ __device__ __forceinline__ double tab_at(const double* wt, uint32_t off) {
 // Whether the bf16 value in the low 16 bits of h has a table slot, and that slot.
 __device__ __forceinline__ bool tab_has(uint32_t h, uint32_t& slot) {
     const uint32_t t = h & 0x7fffu;
-    slot = (t - kTabLo) + ((h >> 4) & 0x800u);
+    slot = 2 * (t - kTabLo) + ((h >> 15) & 1u);
     return t - (kTabLo + 1) < (uint32_t)kTabN;
 }
 
@@ -673,12 +674,10 @@ template <typename E, int NT = kThreads>
 __device__ __forceinline__ void weight_table_write(const DrawRows<E>& r, double* dst) {
 #pragma unroll 4
     for (int k = threadIdx.x; k < kTabLen; k += NT) {
-        const uint32_t q = (uint32_t)k & (kTabHalf - 1);
-        double v = 0.0;
-        if (q == 0 || q == (uint32_t)kTabN + 1) {
-            v = __builtin_nan("");
-        } else if (q <= (uint32_t)kTabN) {
-            const uint32_t h = ((uint32_t)k / kTabHalf) << 15 | (kTabLo + q);
+        const uint32_t q = (uint32_t)k >> 1;
+        double v = __builtin_nan("");
+        if (q != 0 && q != (uint32_t)kTabN + 1) {
+            const uint32_t h = ((uint32_t)k & 1u) << 15 | (kTabLo + q);
             v = exp2_256(exp2_arg((double)__uint_as_float(h << 16), r.refA, r.c256), r.tab);
         }
         dst[k] = v;
@@ -841,7 +840,7 @@ __device__ __forceinline__ void exact_word_tab(const DrawRows<uint16_t>& r, uint
             bv[k] = r.b_of(zd[k]);
         }
         live[k] = av[k] != 0.0 || bv[k] != 0.0;
-        // a difference of two bf16 values with |z| in [2^-10, 32) is exact in fp32;
+        // a difference of two bf16 values with |z| in [2^-12, 32) is exact in fp32;
         // positions whose weights are both 0 need no sign
         dx_ok[k] = (it && id) || !live[k];
     }
