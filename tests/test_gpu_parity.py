@@ -337,6 +337,32 @@ def test_draw_deal_many_rounds(dev):
     t.assert_ok("draw deal")
 
 
+def test_weight_table_edges(dev):
+    """bf16 logits at the edges of the draw's weight table (|z| in [2^-12, 32)): values at
+    and one step outside both ends, zeros of either sign, subnormals and -inf, planted in
+    the target and draft rows of every position, so that the fast path, its NaN sentinels
+    and the fp64 exponential all meet them in the draw."""
+    say("weight table edges")
+    B, K, V = 24, 3, 9000
+    temps = [0.3 + 0.05 * b if b % 6 else 0.0 for b in range(B)]
+    inp = random_case(dev, B, K, V, torch.bfloat16, temps, seed=31, sigma=0.7, scale=1.0)
+    edges = [2.0 ** -12, 2.0 ** -12 - 2.0 ** -20, 32.0, 31.875, 2.0 ** -126, 2.0 ** -133, 0.0, 6.0, 1e-4]
+    vals = torch.tensor([s * e for e in edges for s in (1.0, -1.0)] + [-float("inf")] * 4,
+                        dtype=torch.bfloat16, device=dev)
+    g = torch.Generator(device=dev).manual_seed(32)
+    for z in (inp["target"], inp["draft"]):
+        idx = torch.randint(0, V, (B, z.shape[1], 300), generator=g, device=dev)
+        pick = torch.randint(0, vals.numel(), idx.shape, generator=g, device=dev)
+        z.scatter_(2, idx, vals[pick])
+    inp["tokens"] = W._draft_tokens(inp["draft"], inp["temperature"].cpu(), g)
+    t = Tally()
+    for step in range(3):
+        u = gpu_uniforms(31, step, B, K)
+        t.merge(compare(run_sampled(inp, u), oracle_sampled(inp, u), range(B), inp["temperature"].cpu()))
+    say("  ", t)
+    t.assert_ok("table edges")
+
+
 def test_small_temperature_equals_greedy(dev):
     say("T -> 0 against greedy")
     B, K, V = 32, 5, 20000
