@@ -363,6 +363,41 @@ def test_weight_table_edges(dev):
     t.assert_ok("table edges")
 
 
+def _random_shapes():
+    rng = np.random.default_rng(2024)
+    out = []
+    for V in [1, 7, 999, 4097, 40000, 152064, 300007] * 2:
+        K = int(rng.integers(0, 11))
+        B = int(rng.integers(1, 1 + max(1, min(40, 8_000_000 // ((2 * K + 1) * V)))))
+        dt = torch.bfloat16 if rng.random() < 0.7 else torch.float32
+        temps = [0.0 if rng.random() < 0.25 else float(rng.uniform(0.05, 1.5)) for _ in range(B)]
+        out.append((B, K, V, dt, temps, int(rng.integers(0, 1 << 30))))
+    # many short rows: the sweep takes several rounds of workgroups, so the draws are dealt
+    out.append((1500, 2, 1000, torch.bfloat16, [0.0 if b % 4 == 0 else 0.9 for b in range(1500)], 7))
+    # rows of more than 16 chunks (still staged): the resolve merges rows by (row, chunk) terms
+    out.append((2, 3, 1000003, torch.bfloat16, [0.8, 0.0], 11))
+    return out
+
+
+RANDOM_SHAPES = _random_shapes()
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM_SHAPES)))
+def test_random_shapes(dev, case):
+    """Seeded random (B, K, V, dtype, temperatures) against the oracle: the resolve's row
+    merge by lane groups (1 to 16 chunks a row) and its fallbacks, the sweep with and
+    without the draw deal, grids padded to whole rounds of XCDs."""
+    B, K, V, dt, temps, seed = RANDOM_SHAPES[case]
+    say(f"random shape B={B} K={K} V={V} {dt}")
+    inp = random_case(dev, B, K, V, dt, temps, seed=seed, sigma=float(0.2 + (seed % 7) * 0.3))
+    u = gpu_uniforms(seed, 0, B, K)
+    t = compare(run_sampled(inp, u), oracle_sampled(inp, u), range(B), inp["temperature"].cpu())
+    g = compare(run_greedy(inp), oracle_greedy(inp), range(B), None, greedy_only=True)
+    say("  ", t)
+    t.assert_ok("random shape")
+    g.assert_ok("random shape greedy")
+
+
 def test_small_temperature_equals_greedy(dev):
     say("T -> 0 against greedy")
     B, K, V = 32, 5, 20000
