@@ -58,6 +58,10 @@ constexpr double kLog2eD = 1.4426950408889634;
 constexpr double kDelta = 8e-6;
 constexpr double kLnDeltaHi = 7.999968000170666e-06;
 constexpr double kLnDeltaLo = -8.000032000170667e-06;
+// ln(1 + x) < x < -ln(1 - x) for 0 < x < 1, to the digits given
+static_assert(kLnDeltaHi < kDelta && kDelta < -kLnDeltaLo && kDelta - kLnDeltaHi < 3.3e-11 &&
+                  -kLnDeltaLo - kDelta < 3.3e-11,
+              "the bracket's logarithms");
 // Weights below 2^-kFlushLog2 of their row maximum count as 0.
 constexpr double kFlushLog2 = 70.0;
 // One shared weight reference for both rows while the row maxima differ by at most this
@@ -628,7 +632,7 @@ struct DrawRows {
 
 // The draw rows of sequence b and their weight parameters (no LDS access).
 template <typename E>
-__device__ __forceinline__ DrawRows<E> draw_rows(const VerifyArgs& a, int b, const SeqDesc& d,
+__device__ __forceinline__ DrawRows<E> draw_rows(const VerifyArgs& a, const SeqDesc& d,
                                                  const double* tab, const double* wt) {
     DrawRows<E> r;
     r.residual = d.mode == kModeResidual;
@@ -1598,7 +1602,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(VerifyArgs a, 
     }
     if constexpr (sizeof(E) == 2) {
         if (d.mode != kModeNone) {
-            const DrawRows<E> r = draw_rows<E>(a, b, d, tab, nullptr);  // the bracket is not used
+            const DrawRows<E> r = draw_rows<E>(a, d, tab, nullptr);  // the bracket is not used
             if (r.one_ref) weight_table_write<E, kResolveThreads>(r, a.wtab + (int64_t)b * kWtabLen);
         }
     }
@@ -1630,7 +1634,7 @@ void sweep_kernel(VerifyArgs a, int b0) {
     if (d.mode == kModeNone || d.b < b0 || d.b >= b0 + a.nseq2) return;  // whole workgroup
     const int b = d.b;
     const int c = (int)(j % (unsigned)a.nchunk2);
-    DrawRows<E> r = draw_rows<E>(a, b, d, tab, wt);
+    DrawRows<E> r = draw_rows<E>(a, d, tab, wt);
     const int w = threadIdx.x >> 6;
     SweepAcc acc;
     acc.lane = threadIdx.x & 63;
@@ -1692,7 +1696,7 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(VerifyArgs a, int 
     if (d.mode == kModeNone) return;  // whole workgroup
     if constexpr (sizeof(E) == 2) tc.store(wt);
     exp2_table_init(tab);  // its barrier also publishes wt
-    const DrawRows<E> r = draw_rows<E>(a, b, d, tab, sizeof(E) == 2 ? wt : nullptr);
+    const DrawRows<E> r = draw_rows<E>(a, d, tab, sizeof(E) == 2 ? wt : nullptr);
     if (small)
         final_seq_small<E, kFinalThreads, kSeg / kFinalThreads>(a, r, d, b, dp, bk0, bkt, a.nseg, kSeg);
     else
@@ -1922,7 +1926,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(VerifyArgs a) {
     d.u = u;
     d.mt = d.md = mx;
     d.trow = d.drow = b;
-    DrawRows<E> r = draw_rows<E>(a, b, d, tab, sizeof(E) == 2 ? wt : nullptr);
+    DrawRows<E> r = draw_rows<E>(a, d, tab, sizeof(E) == 2 ? wt : nullptr);
     r.t = row;
     r.d = row;
     r.vec_ok = vec_ok;
