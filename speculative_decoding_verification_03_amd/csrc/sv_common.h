@@ -219,6 +219,10 @@ struct TreeArgs {
 // resolve only) after their pass 1, on the same stream.
 int launch_pass1(const VerifyArgs& a, int bf16, int b0, int b1, void* stream);
 int launch_draw(const VerifyArgs& a, int bf16, int b0, int b1, void* stream);
+// The two draw kernels after the resolve (launch_draw's steps): the sweep over `blocks`
+// workgroups and the final kernel over sequences [b0, b1).
+int launch_sweep(const VerifyArgs& a, int bf16, int b0, unsigned blocks, void* stream);
+int launch_final(const VerifyArgs& a, int bf16, int b0, int b1, void* stream);
 int launch_uniforms(uint64_t seed, uint64_t domain, uint64_t step, int B, int K, float* u,
                     void* stream);
 int launch_tree(const TreeArgs& a, void* stream);
