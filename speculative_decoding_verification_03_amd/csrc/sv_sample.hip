@@ -144,13 +144,20 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(VerifyArgs a) {
             const int v = v0 + k * NT + tid;
             float z[VEC];
             Logit<E>::unpack(raw[k], z);
+            // the vector's NaN-propagating maximum: NaN if it holds a NaN, else +inf if it
+            // holds +inf; only a vector that beats the running maximum is searched for the
+            // lowest index reaching it
+            float tm = z[0];
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                bad |= (z[e] != z[e]) | (sampled && z[e] == INFINITY);
-                if (z[e] > mx) {
-                    mx = z[e];
-                    idx = v * VEC + e;
-                }
+            for (int e = 1; e < VEC; ++e) tm = nmax(tm, z[e]);
+            bad |= (tm != tm) | (sampled && tm == INFINITY);
+            if (tm > mx) {
+                int e0 = VEC - 1;
+#pragma unroll
+                for (int e = VEC - 1; e >= 0; --e)
+                    if (z[e] == tm) e0 = e;
+                mx = tm;
+                idx = v * VEC + e0;
             }
         }
     }
