@@ -1,6 +1,8 @@
 // Pass 2 of the verify step: the resolve kernel (accept tests, outputs, the draw's
 // descriptor and weight table), the early-exit prefix kernel, and the launch of the
 // resolve, sweep and final kernels.
+#include <atomic>
+
 #include "sv_draw.h"
 
 namespace sv {
@@ -513,19 +515,22 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(VerifyArgs a) {
 
 }  // namespace
 
-// Waves the sweep keeps resident on the current device (kDrawWaves per SIMD, 4 SIMDs per
-// compute unit), cached per device.
+// Waves the sweep keeps resident on the current device (SV_DRAW_WAVES per SIMD, 4 SIMDs
+// per compute unit), cached per device; calls from several host threads may fill an entry
+// together (with the same value).
 static int sweep_resident_waves() {
-    static int cache[64];
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1 << 30;
-    if (cache[dev] == 0) {
+    int w = cache[dev].load(std::memory_order_relaxed);
+    if (w == 0) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             return 1 << 30;
-        cache[dev] = cus * 4 * SV_DRAW_WAVES;
+        w = cus * 4 * SV_DRAW_WAVES;
+        cache[dev].store(w, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return w;
 }
 
 int launch_draw(const VerifyArgs& a, int bf16, int b0, int b1, void* stream) {

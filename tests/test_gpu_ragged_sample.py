@@ -217,6 +217,36 @@ def test_sample_parity(dev, B, V, dt):
     t.assert_ok("sampler")
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_sample_ties_and_bad_values(dev, dt):
+    """Greedy rows whose maximum is tied many times over (lowest index wins), rows with a
+    NaN, +inf or -inf planted at the first, a middle or the last position (the scalar tail,
+    V not a multiple of 8), and rows of -inf only: tokens and status equal the oracle's."""
+    B, V = 48, 10007
+    say(f"sampler ties and bad values {dt}")
+    g = torch.Generator(device=dev).manual_seed(4242)
+    z = torch.randint(-3, 2, (B, V), generator=g, device=dev).float()
+    T = torch.rand((B,), generator=g, device=dev) + 0.25
+    T[::2] = 0.0
+    spots = [0, V // 2 + 3, V - 1]
+    for j, pos in enumerate(spots):
+        z[8 + j, pos] = float("nan")          # greedy
+        z[9 + 2 * j, pos] = float("nan")      # sampled (odd rows)
+        z[20 + 2 * j, pos] = float("inf")     # greedy: a valid maximum
+        z[21 + 2 * j, pos] = float("inf")     # sampled: an error
+        z[30 + 2 * j, pos] = 5.0              # greedy: a single maximum there
+    z[40] = -float("inf")
+    z[41] = -float("inf")
+    z = z.to(dt).contiguous()
+    u = sv.sv_fill_uniforms(77, 1, 0, B, 0).reshape(B).contiguous()
+    r = to_host(sv.sv_sample(z, u, T))
+    o = O.sample(logits_to_host(z), u.cpu().numpy(), T.cpu().numpy())
+    np.testing.assert_array_equal(r["status"], o["status"])
+    np.testing.assert_array_equal(r["tokens"], o["tokens"])
+    assert (np.asarray(r["status"])[[8, 9, 21, 40, 41]] != 0).all()
+    assert r["tokens"][30] == 0 and r["tokens"][20] == 0 and r["tokens"][34] == V - 1
+
+
 # ------------------------------------------------------------------------------------
 # token trees (greedy) and the tree attention mask
 # ------------------------------------------------------------------------------------
