@@ -9,9 +9,10 @@ sequences, K=8 drafted tokens, V=152064 bf16 logits, Zipf(1.1)-offset target log
 T ~ U[0, 1.2] with a quarter of the sequences greedy (T = 0).  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 40] [--workload 4] [--no-cpu-baseline]
-                    [--path verify|ragged|sample|tree]
+                    [--path verify|greedy|ragged|sample|tree]
 
---path ragged: spec_verify_ragged on the same rows with K_b uniform on 1..K per sequence
+--path greedy: spec_verify_greedy on the same target rows, every sequence greedy (argmax
+rule, no draft rows read); --path ragged: spec_verify_ragged on the same rows with K_b uniform on 1..K per sequence
 (packed layout); --path sample: sv_sample on the B draft rows of position 0 (one draw per
 row from softmax(z / T)); --path tree: spec_verify_tree_greedy on 64 draft trees of 64
 nodes (V=152064 bf16).  Each prints the same JSON contract for its own workload.
@@ -159,6 +160,32 @@ def cpu_baseline(sets, us, budget_s=15.0):
     return one, cpu_baseline_threads(hosts, B, K, O, budget_s)
 
 
+def cpu_baseline_greedy(sets, budget_s=15.0):
+    """The oracle's greedy verify on whole sequences of the timed batches (one thread)."""
+    import numpy as np
+    import torch
+
+    from oracle import spec_verify_oracle as O
+
+    def host(x):
+        x = x.detach().cpu()
+        return x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.numpy()
+
+    B, K = sets[0]["B"], sets[0]["K"]
+    hosts = [dict(t=host(inp["target"]), x=inp["tokens"].cpu().numpy()) for inp in sets]
+    done, t_total = 0, 0.0
+    while t_total < budget_s:
+        h = hosts[(done // B) % len(hosts)]
+        b = done % B
+        t0 = time.perf_counter()
+        O.verify_greedy(h["t"][b:b + 1], h["x"][b:b + 1])
+        t_total += time.perf_counter() - t0
+        done += 1
+    return dict(value=done * (K + 1) / t_total, unit="positions/s", cores=1, kind="oracle",
+                sample=f"{done} greedy sequences ({done / B:.1f} passes over the {B}-sequence "
+                       f"batches), fp64 numpy oracle, one thread, {t_total:.1f} s of CPU time")
+
+
 def cpu_baseline_threads(hosts, B, K, O, budget_s):
     """The same oracle calls on the host's CPU share: one sequence per task on a pool of
     threads (numpy releases the interpreter lock inside its array operations), for about
@@ -196,7 +223,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", default="verify", choices=["verify", "ragged", "sample", "tree"])
+    ap.add_argument("--path", default="verify", choices=["verify", "greedy", "ragged", "sample", "tree"])
     ap.add_argument("--early-exit", action="store_true",
                     help="verify path: sv_fill_uniforms, then spec_verify_early_exit (rows read "
                          "only up to each sequence's first rejection; p, q past it not reported)")
@@ -295,6 +322,20 @@ def main():
             sv.sv_fill_uniforms_ragged(seed, 0, i, P["cu"], P["total"], K, out=u[k])
             sv.spec_verify_ragged(P["target"], P["draft"], P["cu"], P["tokens"], u[k],
                                   P["temperature"], K, out=outs[k], workspace=ws)
+    elif args.path == "greedy":
+        for x in sets:
+            x["draft"] = None
+        torch.cuda.empty_cache()
+        outs = [dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                     accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
+                     status=torch.empty((B,), dtype=torch.int32, device=dev))
+                for _ in range(nsets)]
+        p1_bytes = B * (K + 1) * V * (2 if c["dtype"] == torch.bfloat16 else 4)
+
+        def step(i):  # noqa: F811
+            k = i % nsets
+            x = sets[k]
+            sv.spec_verify_greedy(x["target"], x["tokens"], out=outs[k], workspace=ws)
     elif args.path == "sample":
         rows = [x["draft"][:, 0].contiguous() for x in sets]
         Ts = [x["temperature"] for x in sets]
@@ -415,6 +456,12 @@ def main():
         result["config"]["mean_positions"] = positions
         traffic = None
         result["roofline"]["traffic"] = None
+    elif args.path == "greedy":
+        result["metric"] = "verified positions/sec, every sequence greedy (spec_verify_greedy)"
+        result["config"]["workload"] = (f"greedy: the target rows of {W.describe(cfg)}, "
+                                       "workload-4 row recipe, T = 0 for every sequence")
+        result["config"]["arithmetic"] = "fp32 compares, int32 indices (argmax, lowest index on ties)"
+        result["roofline"]["traffic"] = None
     elif args.path == "tree":
         result["metric"] = "verified tree nodes/sec (greedy tree verification)"
         result["unit"] = "nodes/s"
@@ -444,6 +491,8 @@ def main():
             result["cpu_baseline"] = cpu_baseline_ragged(packs, u)
         elif args.path == "sample":
             result["cpu_baseline"] = cpu_baseline_sample(rows, u, Ts)
+        elif args.path == "greedy":
+            result["cpu_baseline"] = cpu_baseline_greedy(sets)
         else:
             result["cpu_baseline"], result["cpu_baseline_threads"] = cpu_baseline(sets, u)
     print(json.dumps(result), flush=True)
