@@ -10,7 +10,8 @@ the exercise's bound where V is small enough for 10^5 draws to meet it; the mult
 noise is then about 0.004).  The mean accept length is
 checked against the closed form E[n] = sum_{j=1..K} prod_{i<j} alpha_i, alpha_i =
 sum_v min(p_i(v), q_i(v)) (for rows that do not depend on context, P(n >= j) is the
-product of the first j acceptance rates), within 5 standard errors.  Fixed seeds, so the outcome is deterministic.
+product of the first j acceptance rates), within 5 standard errors.  The draft-side sampler's draws are tested against softmax(z / T) the
+same way.  Fixed seeds, so the outcome is deterministic.
 """
 import os
 
@@ -98,3 +99,23 @@ def test_emitted_tokens_follow_target(dev, V, K, T, noise, seed):
     # positions past the emitted tokens are padding
     k = np.arange(K + 1)[None, :]
     assert (tokens[k > n[:, None]] == -1).all()
+
+
+@pytest.mark.parametrize("V,T,dt,seed", [(40, 0.9, torch.float32, 5), (300, 1.3, torch.bfloat16, 6)])
+def test_sampler_draws_follow_softmax(dev, V, T, dt, seed):
+    """sv_sample over 10^5 copies of one row: the draws fit softmax(z / T) of the row's
+    logits as stored (bf16 values for bf16 rows)."""
+    print(f"sampler stats V={V} T={T} {dt}", flush=True)
+    rng = np.random.default_rng(seed)
+    z = torch.from_numpy(rng.normal(0, 2, V).astype(np.float32)).to(dt)
+    p = softmax(z.float().numpy().astype(np.float64), T)
+    B = 100_000
+    zz = z.to(dev).unsqueeze(0).expand(B, V).contiguous()
+    temp = torch.full((B,), T, dtype=torch.float32, device=dev)
+    u = sv.sv_fill_uniforms(seed, 1, 0, B, 0).reshape(B).contiguous()
+    r = sv.sv_sample(zz, u, temp)
+    torch.cuda.synchronize()
+    assert (r["status"].cpu().numpy() == 0).all()
+    c, lim = chi2_ok(np.bincount(r["tokens"].cpu().numpy(), minlength=V), p)
+    print(f"   chi2 {c:.1f} (limit {lim:.1f})", flush=True)
+    assert c < lim
