@@ -176,9 +176,11 @@ class Workspace:
 _default_ws = {}
 
 
-def _workspace(ws, device, B, K, V):
+def _workspace(ws, device, stream, B, K, V):
+    """The caller's Workspace, else a default one per (device, stream): calls that share a
+    workspace must not overlap, and calls on one stream never do."""
     if ws is None:
-        key = str(device)
+        key = (str(device), _stream(stream).value)
         ws = _default_ws.setdefault(key, Workspace(device))
     return ws.get(B, K, V)
 
@@ -210,7 +212,7 @@ def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature
             q=torch.empty((B, K), dtype=torch.float32, device=dev) if with_probs else None,
             status=torch.empty((B,), dtype=torch.int32, device=dev),
         )
-    ws = _workspace(workspace, dev, B, K, V)
+    ws = _workspace(workspace, dev, stream, B, K, V)
     st = getattr(lib(), _entry)(
         _ptr(target_logits), _ptr(draft_logits), code, _ptr(draft_tokens), _ptr(uniforms),
         _ptr(temperature), B, K, V, _ptr(out["tokens"]), _ptr(out["accept_len"]),
@@ -254,7 +256,7 @@ def spec_verify_philox(target_logits, draft_logits, draft_tokens, temperature, s
             uniforms=torch.empty((B, K + 1), dtype=torch.float32, device=dev),
         )
     _check(out["uniforms"], "uniforms", torch.float32, (B, K + 1))
-    ws = _workspace(workspace, dev, B, K, V)
+    ws = _workspace(workspace, dev, stream, B, K, V)
     st = lib().spec_verify_philox(
         _ptr(target_logits), _ptr(draft_logits), code, _ptr(draft_tokens), _ptr(temperature),
         B, K, V, int(seed), int(domain), int(step), _ptr(out["uniforms"]), _ptr(out["tokens"]),
@@ -280,7 +282,7 @@ def spec_verify_greedy(target_logits, draft_tokens, out=None, workspace=None, st
             accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
             status=torch.empty((B,), dtype=torch.int32, device=dev),
         )
-    ws = _workspace(workspace, dev, B, K, V)
+    ws = _workspace(workspace, dev, stream, B, K, V)
     st = lib().spec_verify_greedy(
         _ptr(target_logits), code, _ptr(draft_tokens), B, K, V, _ptr(out["tokens"]),
         _ptr(out["accept_len"]), _ptr(out["status"]), _ptr(ws), ws.numel(), _stream(stream))
@@ -319,7 +321,7 @@ def spec_verify_ragged(target_logits, draft_logits, cu_drafts, draft_tokens, uni
             q=torch.empty((total,), dtype=torch.float32, device=dev) if with_probs else None,
             status=torch.empty((B,), dtype=torch.int32, device=dev),
         )
-    ws = _workspace(workspace, dev, B, K_max, V)
+    ws = _workspace(workspace, dev, stream, B, K_max, V)
     st = lib().spec_verify_ragged(
         _ptr(target_logits), _ptr(draft_logits), code, _ptr(cu_drafts), total, int(K_max),
         _ptr(draft_tokens), _ptr(uniforms), _ptr(temperature), B, V, _ptr(out["tokens"]),
@@ -348,7 +350,7 @@ def spec_verify_greedy_ragged(target_logits, cu_drafts, draft_tokens, K_max, out
             accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
             status=torch.empty((B,), dtype=torch.int32, device=dev),
         )
-    ws = _workspace(workspace, dev, B, K_max, V)
+    ws = _workspace(workspace, dev, stream, B, K_max, V)
     st = lib().spec_verify_greedy_ragged(
         _ptr(target_logits), code, _ptr(cu_drafts), total, int(K_max), _ptr(draft_tokens), B, V,
         _ptr(out["tokens"]), _ptr(out["accept_len"]), _ptr(out["status"]), _ptr(ws),
@@ -370,7 +372,7 @@ def sv_sample(logits, uniforms, temperature, out=None, workspace=None, stream=No
     if out is None:
         out = dict(tokens=torch.empty((B,), dtype=torch.int32, device=dev),
                    status=torch.empty((B,), dtype=torch.int32, device=dev))
-    ws = _workspace(workspace, dev, B, 0, V)
+    ws = _workspace(workspace, dev, stream, B, 0, V)
     st = lib().sv_sample(_ptr(logits), code, _ptr(uniforms), _ptr(temperature), B, V,
                          _ptr(out["tokens"]), _ptr(out["status"]), _ptr(ws), ws.numel(),
                          _stream(stream))
@@ -397,7 +399,7 @@ def spec_verify_tree_greedy(target_logits, parents, node_tokens, out=None, with_
                    nodes=torch.empty((B, N), dtype=torch.int32, device=dev) if with_nodes else None,
                    accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
                    status=torch.empty((B,), dtype=torch.int32, device=dev))
-    ws = _workspace(workspace, dev, B, max(N - 1, 0), V)
+    ws = _workspace(workspace, dev, stream, B, max(N - 1, 0), V)
     st = lib().spec_verify_tree_greedy(
         _ptr(target_logits), code, _ptr(parents), _ptr(node_tokens), B, N, V, _ptr(out["tokens"]),
         _ptr(out["nodes"]), _ptr(out["accept_len"]), _ptr(out["status"]), _ptr(ws), ws.numel(),
