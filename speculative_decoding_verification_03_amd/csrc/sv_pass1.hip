@@ -6,7 +6,7 @@
 // rows keep the maximum m and S = sum_i exp((z_i - m) / T): the normaliser of the
 // temperature softmax of that page's "Desenvolva" listing.
 //
-// One workgroup per (row, chunk) tile of about 76 KB.  Each lane keeps kU 16-byte
+// One workgroup per (row, chunk) tile of about 76 KB.  Each lane keeps kU or kUDeep 16-byte
 // non-temporal loads in flight; the tail of a tile is handled by masking lanes to -inf,
 // which adds nothing to a sum and never wins a maximum.  Sampled tiles evaluate
 // 2^(z * c2 - R) with one FMA (the product is exact inside the FMA, so the only rounding
@@ -28,10 +28,23 @@ namespace {
 constexpr double kLog2eD = 1.4426950408889634;
 constexpr float kRescaleLog2 = 32.0f;
 constexpr float kSkipLog2 = 50.0f;
+// 16-byte loads in flight per lane: kU for small grids (8 waves per SIMD), kUDeep for
+// large ones (4 waves per SIMD; a whole tile of at most kUDeep * kThreads vectors in one
+// round of loads).  The deep variant's lower occupancy costs more in a short grid's last
+// round than its longer queue saves, so it is taken from kDeepBlocks workgroups on, about
+// 8 rounds of its resident workgroups (4 per CU on 256 CUs), and only for dense calls
+// with sampled rows that read every row: all-greedy calls measured no faster with it, and
+// in ragged and early-exit calls many workgroups of the grid find no row to read, so the
+// grid's real work is short and it measured slower.
 #ifndef SV_P1_LOADS
 #define SV_P1_LOADS 4
 #endif
-constexpr int kU = SV_P1_LOADS;  // 16-byte loads in flight per lane
+#ifndef SV_P1_LOADS_DEEP
+#define SV_P1_LOADS_DEEP 20
+#endif
+constexpr int kU = SV_P1_LOADS;
+constexpr int kUDeep = SV_P1_LOADS_DEEP;
+constexpr int64_t kDeepBlocks = 8192;
 
 struct SumExpAcc {
     float mx;   // NaN-propagating maximum of everything seen
@@ -99,10 +112,10 @@ __device__ __forceinline__ void argmax_vec(const float (&z)[N], int base, Argmax
 }
 
 // Streams [lo, hi) of `row`: a scalar head up to 16-byte alignment, then 16-byte vectors
-// in tiles of kU per lane (lanes past the end see -inf), then a scalar tail.  fvec is
+// in tiles of U per lane (lanes past the end see -inf), then a scalar tail.  fvec is
 // called with VEC elements and the index of the first; fscal with one element.  Each
 // lane sees its elements in increasing index order.
-template <typename E, class FV, class FS>
+template <typename E, int U, class FV, class FS>
 __device__ __forceinline__ void stream_tile(const E* row, int lo, int hi, FV&& fvec, FS&& fscal) {
     constexpr int VEC = Logit<E>::kVec;
     const int tid = threadIdx.x;
@@ -113,15 +126,15 @@ __device__ __forceinline__ void stream_tile(const E* row, int lo, int hi, FV&& f
     const int body0 = lo + head;
     const int nvec = (hi - body0) / VEC;
     const E* p = row + body0;
-    for (int v0 = 0; v0 < nvec; v0 += kU * kThreads) {
-        u32x4 raw[kU];
+    for (int v0 = 0; v0 < nvec; v0 += U * kThreads) {
+        u32x4 raw[U];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int v = v0 + u * kThreads + tid;
             raw[u] = v < nvec ? load16(p + (int64_t)v * VEC) : Logit<E>::neg_inf16();
         }
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
+        for (int u = 0; u < U; ++u) {
             float z[VEC];
             Logit<E>::unpack(raw[u], z);
             fvec(z, body0 + (v0 + u * kThreads + tid) * VEC);
@@ -133,12 +146,12 @@ __device__ __forceinline__ void stream_tile(const E* row, int lo, int hi, FV&& f
 
 // xi: the position of the row's draft token if it lies in this tile, else -1; its logit
 // goes into the partial for the resolve.
-template <typename E>
+template <typename E, int U>
 __device__ void tile_sumexp(const E* row, int lo, int hi, float c2, int xi, RowPartial* out) {
     __shared__ float shf[kWaves];
     __shared__ double shd[kWaves];
     SumExpAcc a{-INFINITY, -FLT_MAX, 0.0};
-    stream_tile<E>(
+    stream_tile<E, U>(
         row, lo, hi, [&](const float(&z)[Logit<E>::kVec], int) { sumexp_vec(z, c2, a); },
         [&](float z, int) {
             const float zz[1] = {z};
@@ -158,12 +171,12 @@ __device__ void tile_sumexp(const E* row, int lo, int hi, float c2, int xi, RowP
     }
 }
 
-template <typename E>
+template <typename E, int U>
 __device__ void tile_argmax(const E* row, int lo, int hi, RowPartial* out) {
     __shared__ float shv[kWaves];
     __shared__ int shi[kWaves];
     ArgmaxAcc a{-INFINITY, 0x7fffffff, 0};
-    stream_tile<E>(
+    stream_tile<E, U>(
         row, lo, hi,
         [&](const float(&z)[Logit<E>::kVec], int base) { argmax_vec(z, base, a); },
         [&](float z, int i) {
@@ -183,7 +196,7 @@ __device__ void tile_argmax(const E* row, int lo, int hi, RowPartial* out) {
     }
 }
 
-template <typename E>
+template <typename E, int U>
 __global__ __launch_bounds__(kThreads) void pass1_kernel(VerifyArgs a, int b0) {
     const int64_t blk = blockIdx.x;
     if (a.deal) {
@@ -228,9 +241,9 @@ __global__ __launch_bounds__(kThreads) void pass1_kernel(VerifyArgs a, int b0) {
             const int x = a.tokens[s.d0 + t];
             if (x >= lo && x < hi) xi = x;
         }
-        tile_sumexp<E>(row, lo, hi, (float)(kLog2eD / (double)T), xi, out);
+        tile_sumexp<E, U>(row, lo, hi, (float)(kLog2eD / (double)T), xi, out);
     }
-    else tile_argmax<E>(row, lo, hi, out);
+    else tile_argmax<E, U>(row, lo, hi, out);
 }
 
 }  // namespace
@@ -239,10 +252,14 @@ int launch_pass1(const VerifyArgs& a, int bf16, int b0, int b1, void* stream) {
     const int64_t blocks = (int64_t)(b1 - b0) * a.R * a.nchunk1;
     if (blocks <= 0) return 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (bf16)
-        hipLaunchKernelGGL(pass1_kernel<uint16_t>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a, b0);
-    else
-        hipLaunchKernelGGL(pass1_kernel<float>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a, b0);
+    const dim3 g((unsigned)blocks), t(kThreads);
+    if (blocks >= kDeepBlocks && a.temperature && !a.cu && !a.limit) {
+        if (bf16) hipLaunchKernelGGL((pass1_kernel<uint16_t, kUDeep>), g, t, 0, s, a, b0);
+        else hipLaunchKernelGGL((pass1_kernel<float, kUDeep>), g, t, 0, s, a, b0);
+    } else {
+        if (bf16) hipLaunchKernelGGL((pass1_kernel<uint16_t, kU>), g, t, 0, s, a, b0);
+        else hipLaunchKernelGGL((pass1_kernel<float, kU>), g, t, 0, s, a, b0);
+    }
     return (int)hipGetLastError();
 }
 
