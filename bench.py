@@ -247,7 +247,7 @@ def main():
 
     dev = torch.device("cuda:0")
     cfg = args.workload
-    c = W.CONFIGS[cfg]
+    c = W.WORKLOADS[cfg]
     log(f"bench: workload {cfg} ({W.describe(cfg)}), path {args.path}, generating inputs")
     nsets = 2
     sets = ([W.make_inputs(cfg, step=s, device=dev) for s in range(nsets)] if args.path != "tree"

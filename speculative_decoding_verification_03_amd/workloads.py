@@ -38,7 +38,7 @@ import math
 
 import torch
 
-CONFIGS = {
+WORKLOADS = {
     1: dict(B=1, K=4, V=1000, dtype=torch.float32),
     2: dict(B=8, K=4, V=32000, dtype=torch.float32),
     3: dict(B=64, K=5, V=128256, dtype=torch.bfloat16),
@@ -52,7 +52,7 @@ SIGMA_CFG5 = (1.3396, 0.4980, 0.1232)  # alpha ~ 0.5, 0.8, 0.95
 
 
 def describe(cfg):
-    c = CONFIGS[cfg]
+    c = WORKLOADS[cfg]
     return f"B={c['B']} K={c['K']} V={c['V']} {'bf16' if c['dtype'] == torch.bfloat16 else 'fp32'}"
 
 
@@ -85,7 +85,7 @@ def make_inputs(cfg, step=0, device="cuda", B=None, seed=None):
     temperature [B] fp32, cfg, B, K, V).  B may be lowered for smaller test cases; the
     first B sequences then follow the same recipe.
     """
-    c = CONFIGS[cfg]
+    c = WORKLOADS[cfg]
     Bf, K, V, dt = c["B"], c["K"], c["V"], c["dtype"]
     B = Bf if B is None else int(B)
     seed = (1000 + cfg) * 1_000_003 + step if seed is None else seed
@@ -226,5 +226,5 @@ def expected_draw_bytes(B, K, V, dtype):
 
 
 if __name__ == "__main__":
-    for k in CONFIGS:
-        print(k, describe(k), f"{math.prod((CONFIGS[k]['B'], CONFIGS[k]['K'] + 1, CONFIGS[k]['V']))} target logits")
+    for k in WORKLOADS:
+        print(k, describe(k), f"{math.prod((WORKLOADS[k]['B'], WORKLOADS[k]['K'] + 1, WORKLOADS[k]['V']))} target logits")
