@@ -71,3 +71,25 @@ def uniforms(seed, domain, step, B, K):
     categorical sample (replacement or bonus).
     """
     return [[uniform(seed, domain, step, b, t) for t in range(K + 1)] for b in range(B)]
+
+
+def uniforms_array(seed, domain, step, B, K):
+    """uniforms() as a float32 numpy array [B][K+1] (every value is exact in fp32)."""
+    import numpy as np
+    return np.array(uniforms(seed, domain, step, B, K), dtype=np.float32).reshape(B, K + 1)
+
+
+def uniforms_packed(seed, domain, step, cu, total):
+    """The packed layout of a ragged batch, float32 [total + B]: sequence b's K_b + 1
+    uniforms (the dense array's first K_b + 1 of row b) at cu[b] + b; the slots of a
+    sequence with invalid offsets stay 0."""
+    import numpy as np
+    cu = [int(v) for v in cu]
+    B = len(cu) - 1
+    out = np.zeros(total + B, dtype=np.float32)
+    for b in range(B):
+        k = cu[b + 1] - cu[b]
+        if cu[b] < 0 or k < 0 or cu[b + 1] > total:
+            continue
+        out[cu[b] + b:cu[b] + b + k + 1] = [uniform(seed, domain, step, b, t) for t in range(k + 1)]
+    return out

@@ -41,7 +41,10 @@ Readings where the pages are silent (each is part of the library contract too):
 * Data errors, per sequence (bit flags, OR-ed):
     ERR_TOKEN        a draft token outside [0, V)
     ERR_LOGIT        a NaN in any row the sequence reads, a row whose maximum is
-                     -inf, or (sampled sequences) a +inf logit
+                     -inf, or (sampled sequences) a +inf logit, or (sampled sequences
+                     with a valid T) a row whose maximum m has |m| * c2 >= 2^30,
+                     c2 = log2(e) / T rounded to fp32 (the range of scaled logits
+                     the verify path supports; see scaled_range_error)
     ERR_TEMPERATURE  T is NaN, negative, infinite, or positive but below the
                      smallest normal fp32 (1/T would not be finite in fp32)
     ERR_UNIFORM      (sampled sequences) a uniform that is NaN or outside [0, 1)
@@ -115,12 +118,25 @@ def argmax_first(z):
     return int(np.argmax(z))
 
 
-def accept_test(u, p_x, q_x):
-    """The exact rule's test r < p(x)/q(x), written as u*q < p so that q = 0 is defined.
+def log_prob_at(z, T, x):
+    """ln p(x) for p = softmax(z / T), fp64: (z_x - m)/T - ln sum_i exp((z_i - m)/T).
+    -inf exactly when z_x is -inf; it does not underflow where p(x) itself would."""
+    m = np.max(z)
+    return (z[x] - m) / T - math.log(float(np.sum(np.exp((z - m) / T))))
 
-    For q > 0 the two are the same predicate; q = 0 with p > 0 accepts; p = 0 rejects.
+
+def accept_test(u, lp_x, lq_x):
+    """The exact rule's test r < p(x)/q(x) on log-probabilities: ln u < ln p - ln q.
+
+    p = 0 (ln p = -inf) rejects, q = 0 with p > 0 accepts, u = 0 accepts any p > 0.
+    In log space the test holds the real-number predicate even where p(x) and q(x)
+    underflow fp64 on their own.
     """
-    return u * q_x < p_x
+    if lp_x == -math.inf:
+        return False
+    if lq_x == -math.inf:
+        return True
+    return (math.log(u) if u > 0.0 else -math.inf) < lp_x - lq_x
 
 
 def replacement_weights(p, q, x):
@@ -193,14 +209,34 @@ def temperature_error(T):
     return 0.0 < T < FP32_MIN_NORMAL
 
 
-def row_error(z, sampled):
-    """NaN anywhere, a maximum of -inf, or (sampled rows) a +inf logit."""
+LOG2E = 1.4426950408889634  # log2(e), rounded to fp64
+
+
+SCALED_RANGE = 2.0 ** 30
+
+
+def scaled_range_error(m, T):
+    """|m| * c2 >= 2^30 with c2 = log2(e)/T rounded to fp32 (the product of two fp32
+    values is exact in fp64).  The pages put no bound on logits or temperatures; this is
+    the library's contract (its first pass holds the scaled row maximum as an fp32
+    number whose rounding must stay far below the range of an fp32 exponential), and the
+    oracle applies the same rule so that both sides flag the same rows."""
+    c2 = float(np.float32(LOG2E / T))
+    return abs(float(m)) * c2 >= SCALED_RANGE
+
+
+def row_error(z, sampled, T=None):
+    """NaN anywhere, a maximum of -inf, or (sampled rows) a +inf logit; with a valid
+    temperature T > 0 also a maximum outside the scaled range (scaled_range_error)."""
     if np.isnan(z).any():
         return True
     m = np.max(z)
     if m == -np.inf:
         return True
-    return sampled and m == np.inf
+    if sampled and m == np.inf:
+        return True
+    return bool(sampled and T is not None and T > 0.0 and not temperature_error(T)
+                and scaled_range_error(m, T))
 
 
 # ----------------------------------------------------------------------------
@@ -231,7 +267,7 @@ def verify_sequence(zt, zd, x, u, T):
         status |= SEQ_ERR_TOKEN
     rows_t = [decode_logits(zt[t]) for t in range(K + 1)]
     rows_d = [] if greedy else [decode_logits(zd[t]) for t in range(K)]
-    if any(row_error(r, not greedy) for r in rows_t + rows_d):
+    if any(row_error(r, not greedy, T) for r in rows_t + rows_d):
         status |= SEQ_ERR_LOGIT
     if not greedy:
         uu = [float(v) for v in u]
@@ -254,14 +290,21 @@ def verify_sequence(zt, zd, x, u, T):
         tokens[K] = argmax_first(rows_t[K])
         return dict(tokens=tokens, n=K, p=nan_k, q=list(nan_k), status=status, draws=[])
 
-    # Sampled: p_t(x_t) and q_t(x_t) for every drafted position.
-    p_x = [prob_at(rows_t[t], T, x[t]) for t in range(K)]
-    q_x = [prob_at(rows_d[t], T, x[t]) for t in range(K)]
+    # Sampled: ln p_t(x_t) and ln q_t(x_t) for every drafted position.
+    lp_x = [log_prob_at(rows_t[t], T, x[t]) for t in range(K)]
+    lq_x = [log_prob_at(rows_d[t], T, x[t]) for t in range(K)]
+    p_x = [math.exp(v) for v in lp_x]
+    q_x = [math.exp(v) for v in lq_x]
     draws = []
     for t in range(K):
-        ratio = p_x[t] / q_x[t] if q_x[t] > 0.0 else math.inf
-        draws.append(("test", t, abs(uu[t] - ratio)))
-        if accept_test(uu[t], p_x[t], q_x[t]):
+        # margin: |u - p/q|; p = 0 or q = 0 decide the test whatever u is
+        if lp_x[t] == -math.inf or lq_x[t] == -math.inf:
+            margin = math.inf
+        else:
+            d = lp_x[t] - lq_x[t]
+            margin = abs(uu[t] - (math.exp(d) if d < 700.0 else math.inf))
+        draws.append(("test", t, margin))
+        if accept_test(uu[t], lp_x[t], lq_x[t]):
             continue
         # First rejection: replacement from the pointwise residual.
         p = softmax_t(rows_t[t], T)

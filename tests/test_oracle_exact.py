@@ -271,6 +271,11 @@ def test_softmax_closed_form(T, shift):
     np.testing.assert_allclose(got, p, rtol=tol, atol=0)
     for x in (0, 5, 17, 36):
         assert abs(O.prob_at(z, T, x) - p[x]) <= tol * p[x]
+        lp = O.log_prob_at(z, T, x)
+        if p[x] == 0:
+            assert lp == -math.inf
+        else:
+            assert abs(lp - math.log(p[x])) <= tol
 
 
 def test_bf16_decoding_matches_torch():
@@ -464,7 +469,10 @@ def test_errors(T):
         assert st(T=float("nan")) & O.SEQ_ERR_TEMPERATURE
         assert st(T=float("inf")) & O.SEQ_ERR_TEMPERATURE
         assert st(T=1e-39) & O.SEQ_ERR_TEMPERATURE
-        assert st(T=2.0 ** -126) == 0
+        # the smallest legal temperature: logits of order 1 scale past 2^30 ...
+        assert st(T=2.0 ** -126) == O.SEQ_ERR_LOGIT
+        # ... logits below 2^-97 in magnitude do not
+        assert st(zt=zt * 2.0 ** -99, zd=zd * 2.0 ** -99, T=2.0 ** -126) == 0
     assert st(x=[1, 10, 3], zt=np.where(np.arange(10) == 3, np.nan, zt).astype(np.float32)) == \
         O.SEQ_ERR_TOKEN | O.SEQ_ERR_LOGIT
 
@@ -484,3 +492,58 @@ def test_zero_residual_mass_falls_back_to_target():
     assert f["status"] == O.SEQ_NOTE_FALLBACK and f["n"] == t
     p = O.softmax_t(zt[t].astype(np.float64), 1.0)
     assert f["tokens"][t] == O.categorical_draw(p, 0.25)[0]
+
+
+def test_scaled_range_rule():
+    """A sampled row whose maximum m has |m| * fp32(log2(e)/T) >= 2^30 is a data error
+    (outside the scaled range the library supports); greedy rows and rows just inside
+    are not."""
+    V = 6
+    c2 = float(np.float32(1.4426950408889634))           # T = 1
+    assert c2 * 2.0 ** 29 < 2.0 ** 30 <= c2 * 2.0 ** 30
+
+    def rows(top):
+        """Rows whose maximum is top (the draft's too); the other logits lie below it."""
+        base = np.array([1.0, 0.5, -0.25, -1.0, 1.0, 0.75])
+        zt = np.array([top * base] * 3, dtype=np.float32)
+        zd = np.array([top * base[::-1]] * 2, dtype=np.float32)
+        return zt, zd
+
+    for top, T, err in ((2.0 ** 29, 1.0, 0), (2.0 ** 30, 1.0, O.SEQ_ERR_LOGIT),
+                        (3.0e38, 1.0, O.SEQ_ERR_LOGIT),
+                        (10.0, 1e-8, O.SEQ_ERR_LOGIT), (0.5, 1e-8, 0),
+                        (10.0, 2e-38, O.SEQ_ERR_LOGIT), (1e-30, 2e-38, 0)):
+        zt, zd = rows(top)
+        r = O.verify_sequence(zt, zd, [1, 3], [0.5, 0.5, 0.5], T)
+        assert r["status"] == err, (top, T, r["status"])
+        g = O.verify_sequence(zt, None, [1, 3], None, 0.0)
+        assert g["status"] == 0                                   # greedy rows: exempt
+    # a logit of -2^127 that is not the maximum is no error (its weight is 0) ...
+    zt = np.array([[0.0, -(2.0 ** 127), 1.0, -2.0, 0.5, 0.0]] * 3, dtype=np.float32)
+    zd = np.array([[1.0, -(2.0 ** 127), 0.0, 2.0, -3.0, 0.5]] * 2, dtype=np.float32)
+    assert O.verify_sequence(zt, zd, [1, 3], [0.5] * 3, 1.0)["status"] == 0
+    # ... but a row entirely at -2^30 has its maximum out of range
+    zt = np.full((3, V), -(2.0 ** 30), dtype=np.float32)
+    zd = np.zeros((2, V), dtype=np.float32)
+    assert O.verify_sequence(zt, zd, [1, 3], [0.5] * 3, 1.0)["status"] == O.SEQ_ERR_LOGIT
+
+
+def test_accept_test_where_p_and_q_underflow():
+    """r < p(x)/q(x) holds its real-number value where p(x) and q(x) each underflow
+    fp64: p(x)/q(x) = e^0.5 > 1 accepts for every u; e^-0.5 accepts exactly for
+    u < e^-0.5.  Where only p(x) underflows the ratio is ~e^-1000: only u = 0 accepts."""
+    zt = np.array([[0.0, -1000.0, -1e4], [0.0, 0.0, 0.0]])
+    zd = np.array([[0.0, -1000.5, -1e4]])
+    for u in (0.0, 0.3, 0.999999):
+        r = O.verify_sequence(zt, zd, [1], [u, 0.5], 1.0)
+        assert r["n"] == 1 and r["tokens"][0] == 1
+        assert r["p"][0] == 0.0 and r["q"][0] == 0.0
+    zd2 = np.array([[0.0, -999.5, -1e4]])
+    e = math.exp(-0.5)
+    for u, acc in ((0.0, True), (e * (1 - 1e-9), True), (e * (1 + 1e-9), False), (0.9, False)):
+        r = O.verify_sequence(zt, zd2, [1], [u, 0.5], 1.0)
+        assert (r["n"] == 1) == acc, (u, r)
+    zd3 = np.array([[0.0, 0.0, -1e4]])
+    for u, acc in ((0.0, True), (2.0 ** -24, False), (0.5, False)):
+        r = O.verify_sequence(zt, zd3, [1], [u, 0.5], 1.0)
+        assert (r["n"] == 1) == acc, (u, r)
