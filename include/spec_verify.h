@@ -132,9 +132,10 @@ sv_status spec_verify(const void* target_logits, const void* draft_logits, int d
  * read in two rounds (the first third, then the rest for the sequences that accepted all
  * of the first); a sequence whose test fails in the first round reads nothing more.  The
  * emitted tokens, accept lengths and draws are bit-identical to spec_verify's.
- * Differences: out_p / out_q are NaN for positions whose rows were not read (past the
- * round in which the sequence stopped), and a NaN or +inf logit in a row that was not
- * read is not reported.  Arguments as for spec_verify.
+ * Differences: out_p / out_q hold p_t(x_t), q_t(x_t) only for the positions up to and
+ * including the first rejection n (all K when every draft is accepted) and are NaN after
+ * it, and a NaN or +inf logit in a row of a position after n is not reported (whether or
+ * not its round read it).  Arguments as for spec_verify.
  */
 sv_status spec_verify_early_exit(const void* target_logits, const void* draft_logits, int dtype,
                                  const int32_t* draft_tokens, const float* uniforms,

@@ -73,21 +73,12 @@ constexpr int32_t kStopBit = 0x40000000;
 
 // Pass-1 chunks of about kChunkBytes1 (long streams per workgroup), more when the batch
 // is too small to fill the chip, never shorter than kMinChunk1 elements.
-#ifndef SV_P1_CHUNK_KB
-#define SV_P1_CHUNK_KB 76
-#endif
-constexpr int64_t kChunkBytes1 = SV_P1_CHUNK_KB * 1024;
+constexpr int64_t kChunkBytes1 = 76 * 1024;
 constexpr int kTargetBlocks1 = 4096;
 constexpr int kMinChunk1 = 4096;
-#ifndef SV_TARGET_BLOCKS2
-#define SV_TARGET_BLOCKS2 2560
-#endif
-constexpr int kTargetBlocks2 = SV_TARGET_BLOCKS2;
+constexpr int kTargetBlocks2 = 2560;
 // Threads of a sweep workgroup: each wave sweeps its own run of draw segments.
-#ifndef SV_SWEEP_THREADS
-#define SV_SWEEP_THREADS 256
-#endif
-constexpr int kSweepThreads = SV_SWEEP_THREADS;
+constexpr int kSweepThreads = 256;
 // The one-workgroup-per-row sampler: threads, and the longest row it takes (segments).
 constexpr int kSampleThreads = 1024;
 constexpr int kSampleMaxSeg = kSampleThreads;

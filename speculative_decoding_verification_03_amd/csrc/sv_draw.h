@@ -62,10 +62,7 @@ constexpr double kFlushLog2 = 70.0;
 // many binary orders of magnitude (then every weight that is not flushed stays normal).
 constexpr double kMaxRefGapLog2 = 900.0;
 // Threads of a final workgroup (one workgroup per sequence; a multiple of kSeg / 8).
-#ifndef SV_FINAL_THREADS
-#define SV_FINAL_THREADS 512
-#endif
-constexpr int kFinalThreads = SV_FINAL_THREADS;
+constexpr int kFinalThreads = 512;
 
 // bf16 weight table in LDS, the signs interleaved: slot 2q + s holds the weight of the bf16
 // value with sign s whose 15-bit magnitude field is kTabLo + q, for q in [1, kTabN]: biased
@@ -79,23 +76,15 @@ constexpr uint32_t kTabHi = kTabLo + kTabN + 1;
 constexpr int kTabLen = 2 * (kTabN + 2);
 
 // Waves per SIMD the sweep kernel's register allocation must allow (4 workgroups per CU).
-#ifndef SV_DRAW_WAVES
-#define SV_DRAW_WAVES 4
-#endif
+constexpr int kDrawWaves = 4;
 
 // 16-byte vectors per row whose loads are in flight together per lane; a span is what one
 // wave covers with them.
-#ifndef SV_SWEEP_G
-#define SV_SWEEP_G 1
-#endif
-constexpr int kG = SV_SWEEP_G;
+constexpr int kG = 1;
 // Words of the fast path between scheduling fences (their table reads may overlap).
 constexpr unsigned kXcds = 8;  // XCDs of an MI355X
 
-#ifndef SV_SWEEP_WPF
-#define SV_SWEEP_WPF 4
-#endif
-constexpr int kWordsPerFence = SV_SWEEP_WPF;
+constexpr int kWordsPerFence = 4;
 constexpr int kSpan16 = 64 * kG * 8;
 static_assert(kSeg % kSpan16 == 0 && kSeg / kSpan16 <= 32, "draw segments are whole spans of bf16 vectors");
 
@@ -122,6 +111,16 @@ struct SeqDesc {
 
 __device__ __forceinline__ bool temperature_bad(float T) {
     return (T != T) || T < 0.0f || T == INFINITY || (T > 0.0f && T < FLT_MIN);
+}
+
+// A sampled row whose maximum m has |m| c2 >= 2^30, c2 = fp32(log2(e) / T), is a data
+// error: pass 1 holds each lane's exponent reference R ~ m c2 as an fp32 number, whose
+// rounding (up to half an ulp of R, 32 at 2^30) shifts the row maximum's own term
+// 2^(m c2 - R); beyond 2^30 that shift could leave the range of an fp32 exponential and
+// lose the term.  Checked only for a valid temperature (c2 finite and positive); the
+// product of the two fp32 values is exact in fp64.
+__device__ __forceinline__ bool scaled_range_bad(float m, float c2) {
+    return c2 > 0.0f && c2 < INFINITY && fabs((double)m) * (double)c2 >= 0x1p30;
 }
 
 // ------------------------------------------------------------------------------------

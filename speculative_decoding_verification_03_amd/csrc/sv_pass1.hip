@@ -36,14 +36,8 @@ constexpr float kSkipLog2 = 50.0f;
 // with sampled rows that read every row: all-greedy calls measured no faster with it, and
 // in ragged and early-exit calls many workgroups of the grid find no row to read, so the
 // grid's real work is short and it measured slower.
-#ifndef SV_P1_LOADS
-#define SV_P1_LOADS 4
-#endif
-#ifndef SV_P1_LOADS_DEEP
-#define SV_P1_LOADS_DEEP 20
-#endif
-constexpr int kU = SV_P1_LOADS;
-constexpr int kUDeep = SV_P1_LOADS_DEEP;
+constexpr int kU = 4;
+constexpr int kUDeep = 20;
 constexpr int64_t kDeepBlocks = 8192;
 
 struct SumExpAcc {
@@ -77,12 +71,10 @@ __device__ __forceinline__ void sumexp_vec(const float (&z)[N], float c2, SumExp
         if (a.s != 0.0) a.s *= exp2((double)a.R - (double)Rn);
         a.R = Rn;
     }
-#ifndef SV_P1_NOSKIP
     // the whole wave's terms are below 2^-kSkipLog2 of its references (each reference is at
     // most the row maximum times c2): over any row they add less than V 2^-kSkipLog2
     // relative to the sum, far below the fp32 rounding of the terms themselves
     if (__all(top < -kSkipLog2)) return;
-#endif
     float e[N];
 #pragma unroll
     for (int k = 0; k < N; ++k) e[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[k], c2, -a.R));

@@ -25,13 +25,12 @@ static_assert(kRowsLds <= 64, "with every row in LDS (2K + 1 <= kRowsLds) one wa
 // Pass-1 partials of one sequence the resolve stages in LDS (16 KB); more stay in memory.
 constexpr int kPartsLds = 1024;
 // Threads of a resolve workgroup (one workgroup per sequence).
-#ifndef SV_RESOLVE_THREADS
-#define SV_RESOLVE_THREADS 1024
-#endif
-constexpr int kResolveThreads = SV_RESOLVE_THREADS;
+constexpr int kResolveThreads = 1024;
 
-__device__ __forceinline__ bool row_bad(float m, bool sampled) {
-    return (m != m) || m == -INFINITY || (sampled && m == INFINITY);
+// A row the sequence reads is bad when its maximum is NaN (a NaN anywhere) or -inf, or,
+// sampled, +inf or out of the scaled range (c2 = fp32(log2(e) / T)).
+__device__ __forceinline__ bool row_bad(float m, bool sampled, float c2) {
+    return (m != m) || m == -INFINITY || (sampled && (m == INFINITY || scaled_range_bad(m, c2)));
 }
 
 struct RowStat {
@@ -181,7 +180,7 @@ __device__ __forceinline__ int merge_rows_grouped(const VerifyArgs& a, const Seq
     }
     if (c != 0) return 0;
     if (i < kRowsLds) rows[i] = r;
-    return row_bad(r.m, sampled) ? kSeqErrLogit : 0;
+    return row_bad(r.m, sampled, c2) ? kSeqErrLogit : 0;
 }
 
 // The test of position t: r < p/q, i.e. r St < Sd 2^((ex - dxm) c2) with ex = zx - mt and
@@ -304,7 +303,7 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
         }
         const RowStat r = staged ? merge_row(a, s, in, parts, i, sampled, c2, tab, by_pair ? terms : nullptr)
                                  : merge_row(a, s, in, src, i, sampled, c2, tab, nullptr);
-        if (row_bad(r.m, sampled)) err |= kSeqErrLogit;
+        if (row_bad(r.m, sampled, c2)) err |= kSeqErrLogit;
         if (i < kRowsLds) rows[i] = r;
     }
     err = block_or<NW>(err, shi);  // also orders the rows[] writes before the reads below
@@ -515,7 +514,7 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(VerifyArgs a) {
 
 }  // namespace
 
-// Waves the sweep keeps resident on the current device (SV_DRAW_WAVES per SIMD, 4 SIMDs
+// Waves the sweep keeps resident on the current device (kDrawWaves per SIMD, 4 SIMDs
 // per compute unit), cached per device; calls from several host threads may fill an entry
 // together (with the same value).
 static int sweep_resident_waves() {
@@ -527,7 +526,7 @@ static int sweep_resident_waves() {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             return 1 << 30;
-        w = cus * 4 * SV_DRAW_WAVES;
+        w = cus * 4 * kDrawWaves;
         cache[dev].store(w, std::memory_order_relaxed);
     }
     return w;

@@ -93,10 +93,6 @@ __device__ __forceinline__ bool row_segment_sums(const DrawRows<E>& r, int V, do
     return block_or<NT / 64>(bad, shi) != 0;  // its barrier also publishes segsum
 }
 
-#ifndef SV_SAMPLE_LOADS
-#define SV_SAMPLE_LOADS 4
-#endif
-
 // grid = rows, one workgroup per row.  Phase 1 streams the row for its maximum (greedy
 // rows: the lowest index reaching it), with normal loads so that the row stays in cache.
 // Sampled rows then tabulate their weights against that maximum (bf16), sum the weights
@@ -131,7 +127,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(VerifyArgs a) {
     float mx = -INFINITY;
     int idx = 0x7fffffff;
     int bad = 0;
-    constexpr int kU = SV_SAMPLE_LOADS;
+    constexpr int kU = 4;
     for (int v0 = 0; v0 < nvec; v0 += kU * NT) {
         u32x4 raw[kU];
 #pragma unroll
@@ -172,6 +168,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(VerifyArgs a) {
     err |= block_or<NW>(bad ? kSeqErrLogit : 0, shi);
     block_argmax<NW>(mx, idx, shv, shi);
     if (mx == -INFINITY) err |= kSeqErrLogit;
+    if (sampled && scaled_range_bad(mx, (float)(kLog2eD / (double)T))) err |= kSeqErrLogit;
     if (err || !sampled) {
         if (tid == 0) {
             a.out_tokens[b] = err ? -1 : idx;

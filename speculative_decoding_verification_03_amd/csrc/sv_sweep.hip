@@ -469,7 +469,7 @@ __device__ __forceinline__ void sweep_wave_exp(const DrawRows<E>& r, int lo, int
 // [c spc, (c + 1) spc) of the draw row(s), each wave a contiguous run of them, into
 // per-segment partials.
 template <typename E>
-__global__ __launch_bounds__(kSweepThreads) __attribute__((amdgpu_waves_per_eu(SV_DRAW_WAVES)))
+__global__ __launch_bounds__(kSweepThreads) __attribute__((amdgpu_waves_per_eu(kDrawWaves)))
 void sweep_kernel(VerifyArgs a, int b0) {
     constexpr int NW = kSweepThreads / 64;
     __shared__ double tab[kExpTable];
