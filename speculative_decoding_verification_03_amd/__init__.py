@@ -134,6 +134,17 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _record(stream, *tensors):
+    """Kernels on a stream other than the current one use these tensors (allocated on the
+    current stream): tell the caching allocator, so that their memory is not handed to
+    other work before that stream has finished with it."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def _dtype_code(t):
     torch = _torch()
     if t.dtype == torch.bfloat16:
@@ -159,7 +170,10 @@ def _check(t, name, dtype=None, shape=None):
 
 
 class Workspace:
-    """Device workspace for spec_verify / spec_verify_greedy, grown on demand."""
+    """Device workspace for spec_verify / spec_verify_greedy, grown on demand.  Every call
+    that uses it on a stream other than the current one records the buffer on that stream,
+    so a buffer dropped when the workspace grows is not reused while work on that stream
+    may still touch it."""
 
     def __init__(self, device="cuda"):
         self.device = device
@@ -182,7 +196,9 @@ def _workspace(ws, device, stream, B, K, V):
     if ws is None:
         key = (str(device), _stream(stream).value)
         ws = _default_ws.setdefault(key, Workspace(device))
-    return ws.get(B, K, V)
+    buf = ws.get(B, K, V)
+    _record(stream, buf)
+    return buf
 
 
 def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature,
@@ -220,6 +236,7 @@ def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature
         _ptr(ws), ws.numel(), _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, _entry)
+    _record(stream, *out.values())
     return out
 
 
@@ -264,6 +281,7 @@ def spec_verify_philox(target_logits, draft_logits, draft_tokens, temperature, s
         _ptr(ws), ws.numel(), _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_philox")
+    _record(stream, *out.values())
     return out
 
 
@@ -288,6 +306,7 @@ def spec_verify_greedy(target_logits, draft_tokens, out=None, workspace=None, st
         _ptr(out["accept_len"]), _ptr(out["status"]), _ptr(ws), ws.numel(), _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy")
+    _record(stream, *out.values())
     return out
 
 
@@ -329,6 +348,7 @@ def spec_verify_ragged(target_logits, draft_logits, cu_drafts, draft_tokens, uni
         _ptr(ws), ws.numel(), _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_ragged")
+    _record(stream, *out.values())
     return out
 
 
@@ -357,6 +377,7 @@ def spec_verify_greedy_ragged(target_logits, cu_drafts, draft_tokens, K_max, out
         ws.numel(), _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_ragged")
+    _record(stream, *out.values())
     return out
 
 
@@ -378,6 +399,7 @@ def sv_sample(logits, uniforms, temperature, out=None, workspace=None, stream=No
                          _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "sv_sample")
+    _record(stream, *out.values())
     return out
 
 
@@ -406,6 +428,7 @@ def spec_verify_tree_greedy(target_logits, parents, node_tokens, out=None, with_
         _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_tree_greedy")
+    _record(stream, *out.values())
     return out
 
 
@@ -424,6 +447,7 @@ def sv_tree_attention_mask(parents, out=None, with_depth=True, stream=None):
                                       _ptr(out["status"]), _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "sv_tree_attention_mask")
+    _record(stream, *out.values())
     return out
 
 
@@ -440,6 +464,7 @@ def sv_fill_uniforms_ragged(seed, domain, step, cu_drafts, total, K_max, out=Non
                                        int(total), int(K_max), _ptr(out), _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "sv_fill_uniforms_ragged")
+    _record(stream, out)
     return out
 
 
@@ -453,6 +478,7 @@ def sv_fill_uniforms(seed, domain, step, B, K, out=None, device="cuda", stream=N
                                 _ptr(out), _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "sv_fill_uniforms")
+    _record(stream, out)
     return out
 
 
