@@ -17,3 +17,17 @@ def pytest_configure(config):
 def have_gpu():
     import torch
     return torch.cuda.is_available()
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """The parity tallies of the run (draws, near-ties, draws within 1e-5 of an edge,
+    hard mismatches), one line per check that reported one."""
+    try:
+        from parity_util import REPORT
+    except ImportError:
+        return
+    if not REPORT:
+        return
+    terminalreporter.write_sep("-", "parity tallies (GPU vs fp64 oracle)")
+    for name, t in REPORT:
+        terminalreporter.write_line(f"{name}: {t}")

@@ -17,7 +17,8 @@ import speculative_decoding_verification_03_amd as sv
 from speculative_decoding_verification_03_amd import workloads as W
 from oracle import philox
 from oracle import spec_verify_oracle as O
-from parity_util import Tally, compare, logits_to_host, to_host
+from parity_util import (Tally, compare, early_exit_expected, host_uniforms, logits_to_host,
+                         to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +36,10 @@ def dev():
 
 
 def gpu_uniforms(seed, step, B, K):
-    return sv.sv_fill_uniforms(seed, 0, step, B, K)
+    """The uniforms of (seed, domain 0, step) from the oracle's generator, on the device:
+    both sides of a parity test read the same array, and none of it comes from the HIP
+    library (test_uniforms_bit_exact checks the library's own generator)."""
+    return torch.from_numpy(host_uniforms(seed, 0, step, B, K)).to("cuda")
 
 
 def run_sampled(inp, u):
@@ -449,6 +453,7 @@ def test_philox_entry_point_equals_two_calls(dev, cfg, B):
                               31337, 2, 9)
     torch.cuda.synchronize()
     f = to_host(f)
+    np.testing.assert_array_equal(f["uniforms"], host_uniforms(31337, 2, 9, Bn, K))
     np.testing.assert_array_equal(f["uniforms"], u.cpu().numpy())
     for k in ("tokens", "accept_len", "status"):
         np.testing.assert_array_equal(f[k], a[k])
@@ -456,41 +461,154 @@ def test_philox_entry_point_equals_two_calls(dev, cfg, B):
         np.testing.assert_array_equal(f[k].view(np.uint32), a[k].view(np.uint32))
 
 
-def _assert_early_exit_matches(full, ee, K, what):
+def _early_exit_vs_oracle(inp, u, what):
+    """spec_verify_early_exit against the oracle directly: tokens, accept lengths and
+    statuses up to near-ties, p and q within 1e-5 up to the first rejection and NaN
+    exactly after it.  Also bit-equal to spec_verify where both report."""
+    K = inp["K"] if "K" in inp else inp["tokens"].shape[1]
+    B = inp["target"].shape[0]
+    ee = to_host(sv.spec_verify_early_exit(inp["target"], inp["draft"], inp["tokens"], u,
+                                           inp["temperature"]))
+    full = to_host(sv.spec_verify(inp["target"], inp["draft"], inp["tokens"], u,
+                                  inp["temperature"]))
+    T = inp["temperature"].cpu()
+    orc = oracle_sampled(inp, u)
+    t = compare(ee, early_exit_expected(orc, ee, T, K), range(B), T)
+    say(f"   {what}: {t}")
+    t.assert_ok(what)
     for k in ("tokens", "accept_len", "status"):
         np.testing.assert_array_equal(ee[k], full[k], err_msg=f"{what}: {k}")
     for k in ("p", "q"):
-        f, e = full[k], ee[k]
-        read = ~np.isnan(e)
-        np.testing.assert_array_equal(e[read].view(np.uint32), f[read].view(np.uint32),
+        read = ~np.isnan(ee[k])
+        np.testing.assert_array_equal(ee[k][read].view(np.uint32), full[k][read].view(np.uint32),
                                       err_msg=f"{what}: {k}")
-        # unread positions come after the sequence's first rejection
-        for b in range(f.shape[0]):
-            n = int(full["accept_len"][b])
-            miss = np.nonzero(~read[b])[0]
-            if len(miss) and not np.isnan(f[b]).all():
-                assert miss.min() > n, (what, b, n, miss.min())
+    return t
 
 
 @pytest.mark.parametrize("cfg,B", [(4, None), (3, None), (2, None), (1, 700)])
-def test_early_exit_equals_full_read(dev, cfg, B):
-    """spec_verify_early_exit: the same tokens, accept lengths and statuses as spec_verify
-    bit for bit; p and q equal wherever the rows were read."""
-    inp = W.make_inputs(cfg, step=4, device=dev, B=B)
-    say(f"early exit: workload {cfg} B={inp['B']}")
-    u = sv.sv_fill_uniforms(1000 + cfg, 0, 4, inp["B"], inp["K"])
-    full = to_host(sv.spec_verify(inp["target"], inp["draft"], inp["tokens"], u, inp["temperature"]))
-    ee = to_host(sv.spec_verify_early_exit(inp["target"], inp["draft"], inp["tokens"], u,
-                                           inp["temperature"]))
-    _assert_early_exit_matches(full, ee, inp["K"], f"workload {cfg}")
+def test_early_exit_against_oracle(dev, cfg, B):
+    t = Tally()
+    for step in (4, 5):
+        inp = W.make_inputs(cfg, step=step, device=dev, B=B)
+        say(f"early exit: workload {cfg} B={inp['B']} step {step}")
+        u = gpu_uniforms(1000 + cfg, step, inp["B"], inp["K"])
+        t.merge(_early_exit_vs_oracle(inp, u, f"workload {cfg}"))
+    t.assert_ok(f"early exit workload {cfg}")
+    assert t.draws > 0
 
 
 @pytest.mark.parametrize("case", range(len(EDGE)))
 def test_early_exit_edge_shapes(dev, case):
     B, K, V, dt, temps = EDGE[case]
-    inp = random_case(dev, B, K, V, dt, temps, seed=700 + case, sigma=0.3)
-    u = gpu_uniforms(5 + case, 1, B, K)
-    full = to_host(sv.spec_verify(inp["target"], inp["draft"], inp["tokens"], u, inp["temperature"]))
-    ee = to_host(sv.spec_verify_early_exit(inp["target"], inp["draft"], inp["tokens"], u,
-                                           inp["temperature"]))
-    _assert_early_exit_matches(full, ee, K, f"edge {case}")
+    say(f"early exit edge case {case}: B={B} K={K} V={V} {dt}")
+    for rep in range(2):
+        inp = random_case(dev, B, K, V, dt, temps, seed=700 + 10 * case + rep, sigma=0.3 + rep)
+        u = gpu_uniforms(5 + case, rep, B, K)
+        _early_exit_vs_oracle(inp, u, f"edge {case}")
+
+
+def test_early_exit_unread_rows(dev):
+    """Rows after a sequence's first rejection do not count: a NaN planted in the bonus
+    row (never read) or in a row of the first round after the rejection (read, unused)
+    goes unreported and the tokens are those of the clean rows; p and q are NaN after
+    the rejection.  The same NaN in the rejected position's row is a data error."""
+    B, K, V = 6, 8, 5000
+    inp = random_case(dev, B, K, V, torch.float32, [1.0] * B, seed=808, sigma=3.0)
+    # draft rows that put their mass where the target has none: the first draft is rejected
+    inp["draft"][:, :, :] = inp["target"][:, :K] - 40.0
+    low = torch.argmin(inp["target"][:, :K], dim=-1)
+    inp["draft"].scatter_(2, low[..., None], 60.0)
+    inp["tokens"] = low.to(torch.int32).contiguous()
+    u = gpu_uniforms(808, 0, B, K)
+    clean = to_host(sv.spec_verify_early_exit(inp["target"], inp["draft"], inp["tokens"], u,
+                                              inp["temperature"]))
+    assert (clean["accept_len"] == 0).all()
+    assert np.isnan(clean["p"][:, 1:]).all() and np.isnan(clean["q"][:, 1:]).all()
+    assert not np.isnan(clean["p"][:, 0]).any() and not np.isnan(clean["q"][:, 0]).any()
+    orc = oracle_sampled(inp, u)
+    np.testing.assert_array_equal(clean["tokens"], orc["tokens"])
+    planted = dict(inp)
+    planted["target"] = inp["target"].clone()
+    planted["target"][:2, K, 17] = float("nan")          # the bonus row: never read
+    planted["target"][2, 1, 17] = float("nan")           # first round, after the rejection
+    planted["target"][3:, 0, 17] = float("nan")          # the rejected position's row
+    got = to_host(sv.spec_verify_early_exit(planted["target"], planted["draft"], planted["tokens"],
+                                            u, planted["temperature"]))
+    np.testing.assert_array_equal(got["tokens"][:3], clean["tokens"][:3])
+    np.testing.assert_array_equal(got["status"][:3], clean["status"][:3])
+    assert (got["status"][3:] == 2).all() and (got["accept_len"][3:] == -1).all()
+
+
+def test_workspace_growth_on_side_stream(dev):
+    """Two calls on a stream other than the current one, the second growing the shared
+    workspace (its old buffer is dropped while the first call may still run on that
+    stream), while the current stream allocates and overwrites memory of the old
+    buffer's size: both calls' results equal the oracle's."""
+    side = torch.cuda.Stream()
+    ws = sv.Workspace(dev)
+    a = W.make_inputs(3, step=11, device=dev)
+    b = W.make_inputs(4, step=11, device=dev, B=96)
+    ua = gpu_uniforms(1003, 11, a["B"], a["K"])
+    ub = gpu_uniforms(1004, 11, b["B"], b["K"])
+    old = sv.sv_workspace_bytes(a["B"], a["K"], a["V"])
+    assert sv.sv_workspace_bytes(b["B"], b["K"], b["V"]) > old
+    side.wait_stream(torch.cuda.current_stream())
+    ra = sv.spec_verify(a["target"], a["draft"], a["tokens"], ua, a["temperature"], workspace=ws,
+                        stream=side)
+    rb = sv.spec_verify(b["target"], b["draft"], b["tokens"], ub, b["temperature"], workspace=ws,
+                        stream=side)
+    junk = [torch.full((old,), 255, dtype=torch.uint8, device=dev) for _ in range(4)]
+    torch.cuda.synchronize()
+    del junk
+    for inp, u, r, what in ((a, ua, ra, "first call"), (b, ub, rb, "grown workspace")):
+        t = compare(to_host(r), oracle_sampled(inp, u), range(inp["B"]), inp["temperature"].cpu())
+        say(f"   side stream, {what}: {t}")
+        t.assert_ok(what)
+
+
+def test_scaled_range_and_underflowing_ratios(dev):
+    """Rows whose maximum m has |m| * fp32(log2(e)/T) >= 2^30 are data errors, rows just
+    inside are not (T = 1 and the smallest legal temperatures, greedy rows exempt); tests
+    whose p(x) and q(x) each underflow fp64 keep the value of the ratio p/q.  Statuses,
+    tokens and accept lengths equal the oracle's; the sampler flags the same rows."""
+    B, K, V = 10, 2, 1000
+    g = torch.Generator(device=dev).manual_seed(1234)
+    zt = torch.randn((B, K + 1, V), generator=g, device=dev)
+    zd = zt[:, :K] + 0.5 * torch.randn((B, K, V), generator=g, device=dev)
+    T = torch.ones(B, device=dev)
+    zt[0, 1, 7] = 2.0 ** 30                        # T = 1, out of range
+    zt[1] *= 2.0 ** 26; zd[1] *= 2.0 ** 26         # |m| = 2^29: inside
+    zt[1, :, 3] = 2.0 ** 29; zd[1, :, 3] = 2.0 ** 29
+    T[2] = 2e-38                                   # logits of order 1: out of range
+    zt[3] *= 1e-31; zd[3] *= 1e-31; T[3] = 2e-38   # |m| ~ 4e-31: inside, one-hot laws
+    zd[4, 0, 11] = 3.0e38                          # a draft row out of range
+    zt[5, 0, 0] = 3.0e38; T[5] = 0.0               # greedy: no range rule
+    # p(x) and q(x) both ~e^-1000: ratio e^0.5 (rows otherwise equal: accept for every u),
+    # or a ratio near e^-0.5 (other draft logits differ, so a rejection has residual mass)
+    zt[6, 0] = 0.0; zt[6, 0, 5] = -1000.0
+    zd[6, 0] = 0.0; zd[6, 0, 5] = -1000.5
+    zt[7, 0] = 0.0; zt[7, 0, 5] = -1000.0
+    zd[7, 0] = 0.3 * torch.randn((V,), generator=g, device=dev); zd[7, 0, 5] = -999.5
+    zt[8, 0] = 0.0; zt[8, 0, 5] = -1000.0; zd[8, 0] = 0.0   # p underflows alone: reject
+    tokens = torch.argmax(zd, dim=-1).to(torch.int32)
+    tokens[6:9, 0] = 5
+    inp = dict(target=zt.contiguous(), draft=zd.contiguous(), tokens=tokens.contiguous(),
+               temperature=T)
+    for step in range(4):
+        u = gpu_uniforms(4321, step, B, K)
+        got = run_sampled(inp, u)
+        orc = oracle_sampled(inp, u)
+        np.testing.assert_array_equal(got["status"], orc["status"])
+        np.testing.assert_array_equal(got["accept_len"], orc["accept_len"])
+        np.testing.assert_array_equal(got["tokens"], orc["tokens"])
+        assert list(orc["status"][[0, 2, 4]]) == [2, 2, 2]
+        assert (orc["status"][[1, 3, 5, 6, 7, 8, 9]] & ~16 == 0).all()
+        assert orc["accept_len"][6] >= 1 and orc["accept_len"][8] == 0
+    # the sampler on the same rows (position 0): the same rows out of range
+    rows = zt[:, 0].contiguous()
+    us = torch.from_numpy(host_uniforms(99, 1, 0, B, 0).reshape(B)).to(dev)
+    r = to_host(sv.sv_sample(rows, us, T))
+    o = O.sample(logits_to_host(rows), us.cpu().numpy(), T.cpu().numpy())
+    np.testing.assert_array_equal(r["status"], o["status"])
+    np.testing.assert_array_equal(r["tokens"], o["tokens"])
+    assert o["status"][2] == 2 and o["status"][1] == 0 and o["status"][5] == 0
