@@ -8,18 +8,29 @@ spec_verify_philox (the uniforms come from the first workgroups of pass 1; with
 sequences, K=8 drafted tokens, V=152064 bf16 logits, Zipf(1.1)-offset target logits,
 T ~ U[0, 1.2] with a quarter of the sequences greedy (T = 0).  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 40] [--workload 4] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 40] [--min-warmup-ms 200]
+                    [--workload 1-5] [--no-cpu-baseline]
                     [--path verify|greedy|ragged|sample|tree]
 
+Warm-up: at least --warmup steps and at least --min-warmup-ms of back-to-back steps.
+From idle, the first ~25 ms of sustained load on an MI355X run at shifting clocks (the
+step time first dips, then rises by up to a quarter, then settles), so a short warm-up
+measures the transient; the JSON line reports the warm-up actually run.
+
 --path greedy: spec_verify_greedy on the same target rows, every sequence greedy (argmax
-rule, no draft rows read); --path ragged: spec_verify_ragged on the same rows with K_b uniform on 1..K per sequence
-(packed layout); --path sample: sv_sample on the B draft rows of position 0 (one draw per
-row from softmax(z / T)); --path tree: spec_verify_tree_greedy on 64 draft trees of 64
-nodes (V=152064 bf16).  Each prints the same JSON contract for its own workload.
+rule, no draft rows read); --path ragged: spec_verify_ragged on the same rows with K_b
+uniform on 1..K per sequence (packed layout); --path sample: sv_sample on the B draft
+rows of position 0 (one draw per row from softmax(z / T)); --path tree:
+spec_verify_tree_greedy on 64 draft trees of 64 nodes (V=152064 bf16).  Each prints the
+same JSON contract for its own workload.
+
+The CPU leg (cpu_baseline) times the fp64 oracle on the timed batches and compares its
+results with the GPU's (the parity object: draws, near-ties, hard mismatches).
 """
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -65,155 +76,266 @@ def host_logits(x):
     return x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.numpy()
 
 
-def cpu_baseline_ragged(packs, us, budget_s=15.0):
-    """The oracle on whole sequences of the ragged batches, about budget_s s of CPU time."""
+def to_host(out):
+    return {k: (None if v is None else v.detach().cpu().numpy()) for k, v in out.items()}
+
+
+def host_info():
+    """The host the CPU leg runs on: CPU model, counts, and the share of it this process
+    may use (OMP_NUM_THREADS when set, else the smaller of the affinity mask and the
+    cgroup's CPU quota)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0))
+    quota = None
+    try:
+        a, b = open("/sys/fs/cgroup/cpu.max").read().split()
+        if a != "max":
+            quota = int(a) / int(b)
+    except (OSError, ValueError):
+        pass
+    try:
+        omp = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        omp = 0
+    share = omp if omp > 0 else min(affinity, math.ceil(quota) if quota else affinity)
+    return dict(cpu_model=model, nproc=os.cpu_count(), affinity=affinity, cgroup_cpus=quota,
+                omp_num_threads=omp or None, share=max(1, min(share, affinity)))
+
+
+# --------------------------------------------------------------------------------------
+# CPU leg: the oracle on the timed batches, and the parity of the GPU results with it
+# --------------------------------------------------------------------------------------
+
+def _orc_arrays(results, B, K):
+    """verify_sequence results {b: dict} -> the arrays oracle.parity.compare reads."""
+    import numpy as np
+    o = dict(tokens=np.full((B, K + 1), -1, np.int32), accept_len=np.full(B, -1, np.int32),
+             status=np.full(B, -1, np.int32), p=np.full((B, K), np.nan, np.float32),
+             q=np.full((B, K), np.nan, np.float32), draws={})
+    for b, r in results.items():
+        o["tokens"][b] = r["tokens"]
+        o["accept_len"][b] = r["n"]
+        o["status"][b] = r["status"]
+        if K:
+            o["p"][b] = np.asarray(r["p"], np.float64).astype(np.float32)
+            o["q"][b] = np.asarray(r["q"], np.float64).astype(np.float32)
+        o["draws"][b] = r["draws"]
+    return o
+
+
+def cpu_legs_dense(hosts, records, seed, greedy, info, early_exit=False, budget_s=20.0):
+    """The oracle on (record, sequence) tasks of the timed batches, in record order.
+
+    hosts[k]: host inputs of input set k; records: (philox step, set k, host GPU outputs)
+    of the steps whose outputs were kept.  Three legs: the C oracle on the host's CPU
+    share (about half the budget; its results give the parity tally), the C oracle on one
+    thread and the numpy oracle on one thread (a quarter each).  early_exit: the GPU
+    reports p and q only up to each sequence's first rejection (NaN after it).
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import c_oracle as Cor
+    from oracle import parity, philox
+    from oracle import spec_verify_oracle as O
+
+    B, K = hosts[0]["B"], hosts[0]["K"]
+    tasks = [(j, b) for j in range(len(records)) for b in range(B)]
+    unis = [None if greedy else philox.uniforms_array(seed, 0, st, B, K) for st, _, _ in records]
+
+    def args_of(task):
+        j, b = task
+        h = hosts[records[j][1]]
+        T = float(h["T"][b])
+        sampled = T != 0.0 and not greedy
+        return (h["t"][b], h["d"][b] if sampled else None, h["x"][b],
+                unis[j][b] if sampled else None, T if sampled else 0.0)
+
+    def leg(fn, threads, budget):
+        done, res = 0, {}
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            t0 = time.perf_counter()
+            while done < len(tasks) and time.perf_counter() - t0 < budget:
+                chunk = tasks[done:done + 8 * threads]
+                for task, r in zip(chunk, ex.map(lambda t: fn(*args_of(t)), chunk)):
+                    res[task] = r
+                done += len(chunk)
+            wall = time.perf_counter() - t0
+        return done, wall, res
+
+    n_all, w_all, res_all = leg(Cor.verify_sequence, info["share"], budget_s / 2)
+    n_one, w_one, _ = leg(Cor.verify_sequence, 1, budget_s / 4)
+    n_np, w_np, _ = leg(O.verify_sequence, 1, budget_s / 4)
+
+    import numpy as np
+    tally = parity.Tally()
+    uni_ok = True
+    for j, (st, k, gpu) in enumerate(records):
+        mine = {b: res_all[(j, b)] for b in range(B) if (j, b) in res_all}
+        if not mine:
+            break
+        T = hosts[k]["T"] if not greedy else None
+        orc = _orc_arrays(mine, B, K)
+        if early_exit:
+            for b in mine:
+                n = int(gpu["accept_len"][b])
+                if T[b] != 0 and 0 <= n < K:
+                    orc["p"][b, n + 1:] = np.nan
+                    orc["q"][b, n + 1:] = np.nan
+        if not greedy and "uniforms" in gpu:
+            uni_ok = uni_ok and bool(np.array_equal(gpu["uniforms"], unis[j]))
+        tally.merge(parity.compare(gpu, orc, sorted(mine), T, greedy_only=greedy))
+    what = "greedy verify" if greedy else "verify"
+    cpu = f"{info['cpu_model']}; nproc {info['nproc']}, affinity {info['affinity']}, " \
+          f"cgroup CPUs {info['cgroup_cpus']}"
+    main = dict(value=n_all * (K + 1) / w_all, unit="positions/s", cores=info["share"],
+                kind="oracle",
+                sample=f"{n_all} sequences of the timed steps ({n_all / B:.1f} batches), C fp64 "
+                       f"oracle ({what}) on {info['share']} threads (the host's CPU share), "
+                       f"{w_all:.1f} s of wall time; host: {cpu}",
+                host=info)
+    one = dict(value=n_one * (K + 1) / w_one, unit="positions/s", cores=1, kind="oracle",
+               sample=f"{n_one} sequences, C fp64 oracle on one thread, {w_one:.1f} s")
+    nump = dict(value=n_np * (K + 1) / w_np, unit="positions/s", cores=1, kind="oracle",
+                sample=f"{n_np} sequences, numpy fp64 oracle on one thread, {w_np:.1f} s")
+    par = dict(tally.as_dict(), oracle="C fp64 oracle, uniforms from the oracle's own "
+               "counter generator", steps=len({j for j, _ in res_all}),
+               ok=tally_ok(tally) and uni_ok)
+    if not greedy:
+        par["gpu_uniforms_equal_oracle_generator"] = uni_ok
+    return main, one, nump, par
+
+
+def tally_ok(t):
+    from oracle import parity
+    return (not t.hard and not t.prob_bad
+            and t.near_ties <= parity.NEAR_TIE_BUDGET * max(t.draws, 1))
+
+
+def cpu_leg_ragged(packs, records, seed, budget_s=15.0):
+    """The numpy oracle on whole sequences of the ragged batches' last steps (one thread),
+    compared with the GPU's results."""
     import numpy as np
 
+    from oracle import parity, philox
     from oracle import spec_verify_oracle as O
     B = packs[0]["B"]
     hosts = []
-    for P, u in zip(packs, us):
+    for P in packs:
         hosts.append(dict(t=host_logits(P["target"]), d=host_logits(P["draft"]),
                           cu=P["cu"].cpu().numpy(), x=P["tokens"].cpu().numpy(),
-                          u=u.cpu().numpy(), T=P["temperature"].cpu().numpy(), K=P["K_max"]))
+                          T=P["temperature"].cpu().numpy(), K=P["K_max"], total=P["total"]))
+    tally = parity.Tally()
     done, pos, t_total = 0, 0, 0.0
-    while t_total < budget_s:
-        h = hosts[(done // B) % len(hosts)]
+    while t_total < budget_s and done < len(records) * B:
+        st, k, gpu = records[done // B]
+        h = hosts[k]
         b = done % B
+        if b == 0:
+            u = philox.uniforms_packed(seed, 0, st, h["cu"], h["total"])
         t0 = time.perf_counter()
-        r = O.verify_ragged(h["t"], h["d"], h["cu"], h["x"], h["u"], h["T"], h["K"], seqs=[b])
+        r = O.verify_ragged(h["t"], h["d"], h["cu"], h["x"], u, h["T"], h["K"], seqs=[b])
         t_total += time.perf_counter() - t0
+        c0, c1 = int(h["cu"][b]), int(h["cu"][b + 1])
+        g1 = dict(tokens=gpu["tokens"][None, c0 + b:c1 + b + 1], accept_len=gpu["accept_len"][b:b + 1],
+                  status=gpu["status"][b:b + 1], p=gpu["p"][None, c0:c1], q=gpu["q"][None, c0:c1])
+        o1 = dict(tokens=r["tokens"][None, c0 + b:c1 + b + 1], accept_len=r["accept_len"][b:b + 1],
+                  status=r["status"][b:b + 1], p=r["p"][None, c0:c1], q=r["q"][None, c0:c1],
+                  draws={0: r["draws"][b]})
+        tally.merge(parity.compare(g1, o1, [0], np.asarray(h["T"][b:b + 1])))
         pos += int(r["K"][b]) + 1
         done += 1
-    del np
-    return dict(value=pos / t_total, unit="positions/s", cores=1, kind="oracle",
-                sample=f"{done} sequences ({pos} positions) of the ragged batches, fp64 numpy "
-                       f"oracle, one thread, {t_total:.1f} s of CPU time")
+    base = dict(value=pos / t_total, unit="positions/s", cores=1, kind="oracle",
+                sample=f"{done} sequences ({pos} positions) of the ragged batches' last steps, "
+                       f"fp64 numpy oracle, one thread, {t_total:.1f} s of CPU time")
+    return base, dict(tally.as_dict(), oracle="numpy fp64 oracle", ok=tally_ok(tally))
 
 
-def cpu_baseline_sample(rows, us, Ts, budget_s=15.0):
-    """The oracle's sampler on rows of the timed batches, about budget_s s of CPU time."""
+def cpu_leg_sample(rows, Ts, records, seed, budget_s=15.0):
+    """The numpy oracle's sampler on rows of the last steps, compared with the GPU's draws."""
+    import numpy as np
+
+    from oracle import parity, philox
     from oracle import spec_verify_oracle as O
-    hosts = [(host_logits(z), u.cpu().numpy(), T.cpu().numpy()) for z, u, T in zip(rows, us, Ts)]
+    hosts = [(host_logits(z), T.cpu().numpy()) for z, T in zip(rows, Ts)]
     B = hosts[0][0].shape[0]
+    tally = parity.Tally()
     done, t_total = 0, 0.0
-    while t_total < budget_s:
-        z, u, T = hosts[(done // B) % len(hosts)]
+    while t_total < budget_s and done < len(records) * B:
+        st, k, gpu = records[done // B]
+        z, T = hosts[k]
         b = done % B
+        if b == 0:
+            u = philox.uniforms_array(seed, 1, st, B, 0).reshape(B)
         t0 = time.perf_counter()
-        O.sample(z[b:b + 1], u[b:b + 1], T[b:b + 1])
+        r = O.sample(z[b:b + 1], u[b:b + 1], T[b:b + 1])
         t_total += time.perf_counter() - t0
+        g1 = dict(tokens=gpu["tokens"][b:b + 1, None],
+                  accept_len=np.where(gpu["status"][b:b + 1] & ~16, -1, 0),
+                  status=gpu["status"][b:b + 1], p=np.zeros((1, 0)), q=np.zeros((1, 0)))
+        o1 = dict(tokens=r["tokens"][:, None], accept_len=np.where(r["status"] & ~16, -1, 0),
+                  status=r["status"], p=np.zeros((1, 0)), q=np.zeros((1, 0)),
+                  draws={0: r["draws"][0]})
+        tally.merge(parity.compare(g1, o1, [0], T[b:b + 1]))
         done += 1
-    return dict(value=done / t_total, unit="draws/s", cores=1, kind="oracle",
-                sample=f"{done} rows of the timed batches, fp64 numpy oracle, one thread, "
+    base = dict(value=done / t_total, unit="draws/s", cores=1, kind="oracle",
+                sample=f"{done} rows of the last steps, fp64 numpy oracle, one thread, "
                        f"{t_total:.1f} s of CPU time")
+    return base, dict(tally.as_dict(), oracle="numpy fp64 oracle", ok=tally_ok(tally))
 
 
-def cpu_baseline_tree(trees, budget_s=15.0):
-    """The oracle's tree verification on whole trees of the timed batches."""
+def cpu_leg_tree(trees, records, budget_s=15.0):
+    """The numpy oracle's tree verification on whole trees of the last steps (one thread),
+    compared with the GPU's results (bit for bit)."""
     from oracle import spec_verify_oracle as O
     hosts = [(host_logits(t["target"]), t["parents"].cpu().numpy(), t["tokens"].cpu().numpy())
              for t in trees]
     B, N = hosts[0][1].shape
-    done, t_total = 0, 0.0
-    while t_total < budget_s:
-        z, par, tok = hosts[(done // B) % len(hosts)]
+    done, t_total, mism = 0, 0.0, 0
+    while t_total < budget_s and done < len(records) * B:
+        st, k, gpu = records[done // B]
+        z, par, tok = hosts[k]
         b = done % B
         t0 = time.perf_counter()
-        O.verify_tree_sequence(z[b], par[b], tok[b])
+        r = O.verify_tree_sequence(z[b], par[b], tok[b])
         t_total += time.perf_counter() - t0
+        if (list(gpu["tokens"][b]) != r["tokens"] or int(gpu["accept_len"][b]) != r["n"]
+                or int(gpu["status"][b]) != r["status"]):
+            mism += 1
         done += 1
-    return dict(value=done * N / t_total, unit="nodes/s", cores=1, kind="oracle",
-                sample=f"{done} trees of {N} nodes of the timed batches, fp64 numpy oracle, "
+    base = dict(value=done * N / t_total, unit="nodes/s", cores=1, kind="oracle",
+                sample=f"{done} trees of {N} nodes of the last steps, fp64 numpy oracle, "
                        f"one thread, {t_total:.1f} s of CPU time")
+    return base, dict(sequences=done, hard=mism, oracle="numpy fp64 oracle (greedy: bit for bit)",
+                      ok=mism == 0)
 
 
-def cpu_baseline(sets, us, budget_s=15.0):
-    """The fp64 oracle as it stands, on the host: whole sequences of the timed batches,
-    cycling through them until about budget_s seconds of CPU work (one thread: numpy)."""
-    import numpy as np
+def copy_gbps(dev):
+    """Device-to-device copy of 1 GiB (read + write), as GB/s of traffic: the same
+    box's streaming rate, beside the published peak."""
     import torch
-
-    from oracle import spec_verify_oracle as O
-
-    def host(x):
-        x = x.detach().cpu()
-        return x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.numpy()
-
-    B, K = sets[0]["B"], sets[0]["K"]
-    hosts = []
-    for inp, u in zip(sets, us):
-        hosts.append(dict(t=host(inp["target"]), d=host(inp["draft"]), x=inp["tokens"].cpu().numpy(),
-                          u=u.cpu().numpy(), T=inp["temperature"].cpu().numpy()))
-    done, t_total = 0, 0.0
-    while t_total < budget_s:
-        h = hosts[(done // B) % len(hosts)]
-        b = done % B
-        t0 = time.perf_counter()
-        O.verify_sequence(h["t"][b], h["d"][b] if h["T"][b] != 0 else None, h["x"][b], h["u"][b],
-                          float(h["T"][b]))
-        t_total += time.perf_counter() - t0
-        done += 1
-    one = dict(value=done * (K + 1) / t_total, unit="positions/s", cores=1, kind="oracle",
-               sample=f"{done} sequences ({done / B:.1f} passes over the {B}-sequence batches), "
-                      f"fp64 numpy oracle, one thread, {t_total:.1f} s of CPU time")
-    return one, cpu_baseline_threads(hosts, B, K, O, budget_s)
-
-
-def cpu_baseline_greedy(sets, budget_s=15.0):
-    """The oracle's greedy verify on whole sequences of the timed batches (one thread)."""
-    import numpy as np
-    import torch
-
-    from oracle import spec_verify_oracle as O
-
-    def host(x):
-        x = x.detach().cpu()
-        return x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.numpy()
-
-    B, K = sets[0]["B"], sets[0]["K"]
-    hosts = [dict(t=host(inp["target"]), x=inp["tokens"].cpu().numpy()) for inp in sets]
-    done, t_total = 0, 0.0
-    while t_total < budget_s:
-        h = hosts[(done // B) % len(hosts)]
-        b = done % B
-        t0 = time.perf_counter()
-        O.verify_greedy(h["t"][b:b + 1], h["x"][b:b + 1])
-        t_total += time.perf_counter() - t0
-        done += 1
-    return dict(value=done * (K + 1) / t_total, unit="positions/s", cores=1, kind="oracle",
-                sample=f"{done} greedy sequences ({done / B:.1f} passes over the {B}-sequence "
-                       f"batches), fp64 numpy oracle, one thread, {t_total:.1f} s of CPU time")
-
-
-def cpu_baseline_threads(hosts, B, K, O, budget_s):
-    """The same oracle calls on the host's CPU share: one sequence per task on a pool of
-    threads (numpy releases the interpreter lock inside its array operations), for about
-    budget_s seconds of wall time."""
-    from concurrent.futures import ThreadPoolExecutor
-
-    try:
-        share = int(os.environ.get("OMP_NUM_THREADS", "0"))
-    except ValueError:
-        share = 0
-    nt = max(1, min(share if share > 0 else 16, os.cpu_count() or 1))
-
-    def one(i):
-        h = hosts[(i // B) % len(hosts)]
-        b = i % B
-        O.verify_sequence(h["t"][b], h["d"][b] if h["T"][b] != 0 else None, h["x"][b], h["u"][b],
-                          float(h["T"][b]))
-
-    done = 0
-    t0 = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=nt) as ex:
-        while time.perf_counter() - t0 < budget_s:
-            list(ex.map(one, range(done, done + 4 * nt)))
-            done += 4 * nt
-    wall = time.perf_counter() - t0
-    return dict(value=done * (K + 1) / wall, unit="positions/s", cores=nt, kind="oracle",
-                sample=f"{done} sequences of the timed batches, fp64 numpy oracle on {nt} threads, "
-                       f"{wall:.1f} s of wall time")
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * COPY_BYTES / (ms * 1e-3) / 1e9
 
 
 def main():
@@ -221,6 +343,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--min-warmup-ms", type=float, default=200.0,
+                    help="keep warming up until this many ms of back-to-back steps have run")
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="verify", choices=["verify", "greedy", "ragged", "sample", "tree"])
@@ -248,40 +372,44 @@ def main():
     dev = torch.device("cuda:0")
     cfg = args.workload
     c = W.WORKLOADS[cfg]
+    esize = 2 if c["dtype"] == torch.bfloat16 else 4
     log(f"bench: workload {cfg} ({W.describe(cfg)}), path {args.path}, generating inputs")
     nsets = 2
     sets = ([W.make_inputs(cfg, step=s, device=dev) for s in range(nsets)] if args.path != "tree"
             else [W.make_inputs(cfg, step=s, device=dev, B=1) for s in range(nsets)])
     B, K, V = sets[0]["B"], sets[0]["K"], sets[0]["V"]
-    u = [torch.empty((B, K + 1), dtype=torch.float32, device=dev) for _ in range(nsets)]
-    outs = [dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
-                 accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
-                 p=torch.empty((B, K), dtype=torch.float32, device=dev),
-                 q=torch.empty((B, K), dtype=torch.float32, device=dev),
-                 status=torch.empty((B,), dtype=torch.int32, device=dev)) for _ in range(nsets)]
     ws = sv.Workspace(dev)
     seed = 1000 + cfg
     temps = sets[0]["temperature"]
     positions = B * (K + 1)
     p1_bytes = W.logit_bytes(B, K, V, c["dtype"], temps)
 
-    for k in range(nsets):
-        outs[k]["uniforms"] = u[k]
+    def new_out():
+        return dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                    accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
+                    p=torch.empty((B, K), dtype=torch.float32, device=dev),
+                    q=torch.empty((B, K), dtype=torch.float32, device=dev),
+                    status=torch.empty((B,), dtype=torch.int32, device=dev),
+                    uniforms=torch.empty((B, K + 1), dtype=torch.float32, device=dev))
 
-    def step(i):
+    outs = [new_out() for _ in range(nsets)]
+    keep_timed = args.path == "verify"  # every timed step writes outputs of its own
+
+    def step(i, out=None):
         k = i % nsets
         x = sets[k]
+        o = outs[k] if out is None else out
         if args.early_exit:
-            sv.sv_fill_uniforms(seed, 0, i, B, K, out=u[k])
-            sv.spec_verify_early_exit(x["target"], x["draft"], x["tokens"], u[k], x["temperature"],
-                                      out=outs[k], workspace=ws)
+            sv.sv_fill_uniforms(seed, 0, i, B, K, out=o["uniforms"])
+            sv.spec_verify_early_exit(x["target"], x["draft"], x["tokens"], o["uniforms"],
+                                      x["temperature"], out=o, workspace=ws)
         elif args.separate_uniforms:
-            sv.sv_fill_uniforms(seed, 0, i, B, K, out=u[k])
-            sv.spec_verify(x["target"], x["draft"], x["tokens"], u[k], x["temperature"],
-                           out=outs[k], workspace=ws)
+            sv.sv_fill_uniforms(seed, 0, i, B, K, out=o["uniforms"])
+            sv.spec_verify(x["target"], x["draft"], x["tokens"], o["uniforms"], x["temperature"],
+                           out=o, workspace=ws)
         else:
             sv.spec_verify_philox(x["target"], x["draft"], x["tokens"], x["temperature"], seed, 0,
-                                  i, out=outs[k], workspace=ws)
+                                  i, out=o, workspace=ws)
 
     if args.path == "tree":
         trees = [W.make_tree_inputs(device=dev, V=V, dtype=c["dtype"], step=s_)
@@ -293,9 +421,9 @@ def main():
                      status=torch.empty((B,), dtype=torch.int32, device=dev))
                 for _ in range(nsets)]
         positions = B * N
-        p1_bytes = B * N * V * (2 if c["dtype"] == torch.bfloat16 else 4)
+        p1_bytes = B * N * V * esize
 
-        def step(i):  # noqa: F811
+        def step(i, out=None):  # noqa: F811
             k = i % nsets
             t = trees[k]
             sv.spec_verify_tree_greedy(t["target"], t["parents"], t["tokens"], out=outs[k],
@@ -316,7 +444,7 @@ def main():
         p1_bytes = sum(W.ragged_logit_bytes(P["kb"], V, c["dtype"], P["temperature"])
                        for P in packs) / nsets
 
-        def step(i):  # noqa: F811
+        def step(i, out=None):  # noqa: F811
             k = i % nsets
             P = packs[k]
             sv.sv_fill_uniforms_ragged(seed, 0, i, P["cu"], P["total"], K, out=u[k])
@@ -330,9 +458,9 @@ def main():
                      accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
                      status=torch.empty((B,), dtype=torch.int32, device=dev))
                 for _ in range(nsets)]
-        p1_bytes = B * (K + 1) * V * (2 if c["dtype"] == torch.bfloat16 else 4)
+        p1_bytes = B * (K + 1) * V * esize
 
-        def step(i):  # noqa: F811
+        def step(i, out=None):  # noqa: F811
             k = i % nsets
             x = sets[k]
             sv.spec_verify_greedy(x["target"], x["tokens"], out=outs[k], workspace=ws)
@@ -346,13 +474,14 @@ def main():
                      status=torch.empty((B,), dtype=torch.int32, device=dev))
                 for _ in range(nsets)]
         positions = B
-        p1_bytes = B * V * (2 if c["dtype"] == torch.bfloat16 else 4)
+        p1_bytes = B * V * esize
 
-        def step(i):  # noqa: F811
+        def step(i, out=None):  # noqa: F811
             k = i % nsets
             sv.sv_fill_uniforms(seed, 1, i, B, 0, out=u[k].view(B, 1))
             sv.sv_sample(rows[k], u[k], Ts[k], out=outs[k], workspace=ws)
 
+    box_copy = copy_gbps(dev)
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -362,18 +491,29 @@ def main():
         log(f"bench: copy calibration, 3 copies of {COPY_BYTES} bytes")
         del src, dst
 
-    log(f"bench: warmup {args.warmup}")
-    for i in range(args.warmup):
-        step(i)
+    # warm-up: at least args.warmup steps and at least args.min_warmup_ms of back-to-back
+    # steps (the clocks settle after ~25 ms of load)
+    log(f"bench: warmup (at least {args.warmup} steps and {args.min_warmup_ms:.0f} ms)")
+    n_warm = 0
     torch.cuda.synchronize()
+    tw0 = time.perf_counter()
+    while n_warm < args.warmup or (time.perf_counter() - tw0) * 1e3 < args.min_warmup_ms:
+        for _ in range(10):
+            step(n_warm)
+            n_warm += 1
+        torch.cuda.synchronize()
+        if n_warm >= 1_000_000:
+            break
+    warm_ms = (time.perf_counter() - tw0) * 1e3
 
     # clean timed region
     log(f"bench: timing {args.steps} steps")
+    touts = [new_out() for _ in range(args.steps)] if keep_timed else None
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for i in range(args.steps):
-        step(args.warmup + i)
+        step(n_warm + i, touts[i] if keep_timed else None)
     e1.record()
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
@@ -386,7 +526,7 @@ def main():
     f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     f0.record()
     for i in range(args.steps):
-        step(args.warmup + args.steps + i)
+        step(n_warm + args.steps + i)
     f1.record()
     torch.cuda.synchronize()
     calls, ms_p1, ms_p2 = sv.sv_profile_end()
@@ -394,11 +534,31 @@ def main():
     ms_pass1 = ms_p1 / calls
     ms_pass2 = ms_p2 / calls
 
-    acc = torch.cat([o["accept_len"].float() for o in outs]) if "accept_len" in outs[0] else None
-    bad = int(sum(int((o["status"] & ~16).ne(0).sum()) for o in outs))
+    # outputs whose inputs the CPU leg can rebuild: every timed step (verify path), else
+    # each input set's last step
+    if keep_timed:
+        records = [(n_warm + i, (n_warm + i) % nsets, to_host(touts[i])) for i in range(args.steps)]
+    else:
+        last = n_warm + 2 * args.steps - 1
+        records = sorted(((s_, s_ % nsets, to_host(outs[s_ % nsets]))
+                          for s_ in (last - 1, last)), key=lambda r: r[1])
+    acc_all = [r[2]["accept_len"] for r in records] if "accept_len" in records[0][2] else None
+    bad = int(sum(int(((r[2]["status"] & ~16) != 0).sum()) for r in records))
     value = positions / (ms_step * 1e-3)
     achieved = p1_bytes / (ms_pass1 * 1e-3) / 1e9
     traffic = measured_traffic(cfg)
+
+    # bytes of the draws (pass 2): the drawn row pair of each residual draw, the one row of
+    # each bonus draw, from the kept steps' accept lengths
+    draw_bytes = 0.0
+    if args.path == "verify":
+        for st, k, o in records:
+            T_k = sets[k]["temperature"].cpu().numpy()
+            ok = (T_k != 0) & ((o["status"] & ~16) == 0)
+            n = o["accept_len"]
+            draw_bytes += float(((ok & (n < K)) * 2 + (ok & (n == K)) * 1).sum()) * V * esize
+        draw_bytes /= len(records)
+    call_bytes = p1_bytes + draw_bytes
 
     result = {
         "metric": "verified positions/sec and logit-read GB/s (% HBM peak) at B×(K+1)×V",
@@ -407,6 +567,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_min_ms": args.min_warmup_ms,
+        "warmup_steps_run": n_warm,
+        "warmup_ms": warm_ms,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -422,13 +585,15 @@ def main():
             "arithmetic": "pass 1 fp32 exp with fp64 sums; resolve and pass 2 fp64",
             "parallelism": "single GPU",
         },
-        "logit_read_gbps_call": p1_bytes / (ms_step * 1e-3) / 1e9,
-        "hbm_peak_frac_call": p1_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "logit_bytes_call": call_bytes,
+        "logit_read_gbps_call": call_bytes / (ms_step * 1e-3) / 1e9,
+        "hbm_peak_frac_call": call_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "ms_pass1": ms_pass1,
         "ms_pass2": ms_pass2,
         "ms_per_step_profiled": ms_step_profiled,
-        "mean_accept_len": None if acc is None else float(acc.mean()),
+        "mean_accept_len": None if acc_all is None else float(sum(a.mean() for a in acc_all) / len(acc_all)),
         "sequences_with_data_errors": bad,
+        "box": {"device": torch.cuda.get_device_name(0), "copy_gbps": box_copy},
         "roofline": {
             "kernel": "pass1_kernel (logit row streaming)",
             "bound": "hbm",
@@ -454,7 +619,6 @@ def main():
             f"(mean {sum(kbs) / len(kbs):.2f}), workload-4 row recipe")
         result["config"]["K_max"] = K
         result["config"]["mean_positions"] = positions
-        traffic = None
         result["roofline"]["traffic"] = None
     elif args.path == "greedy":
         result["metric"] = "verified positions/sec, every sequence greedy (spec_verify_greedy)"
@@ -465,7 +629,6 @@ def main():
     elif args.path == "tree":
         result["metric"] = "verified tree nodes/sec (greedy tree verification)"
         result["unit"] = "nodes/s"
-        result["dtype"] = "f32"
         result["config"] = {
             "workload": f"tree: B={B} trees of N={N} nodes (levels {list(W.TREE_LEVELS)}), "
                         f"V={V} {'bf16' if c['dtype'] == torch.bfloat16 else 'fp32'}, "
@@ -484,17 +647,25 @@ def main():
         result["roofline"]["kernel"] = ("sample_kernel (one workgroup per row; algorithmic bytes: "
                                         "each row read once)")
     if not args.no_cpu_baseline:
-        log("bench: cpu baseline (oracle)")
+        log("bench: cpu baseline (oracle) and parity")
+        info = host_info()
         if args.path == "tree":
-            result["cpu_baseline"] = cpu_baseline_tree(trees)
+            result["cpu_baseline"], result["parity"] = cpu_leg_tree(trees, records)
         elif args.path == "ragged":
-            result["cpu_baseline"] = cpu_baseline_ragged(packs, u)
+            result["cpu_baseline"], result["parity"] = cpu_leg_ragged(packs, records, seed)
         elif args.path == "sample":
-            result["cpu_baseline"] = cpu_baseline_sample(rows, u, Ts)
-        elif args.path == "greedy":
-            result["cpu_baseline"] = cpu_baseline_greedy(sets)
+            result["cpu_baseline"], result["parity"] = cpu_leg_sample(rows, Ts, records, seed)
         else:
-            result["cpu_baseline"], result["cpu_baseline_threads"] = cpu_baseline(sets, u)
+            hosts = [dict(t=host_logits(x["target"]),
+                          d=None if x["draft"] is None else host_logits(x["draft"]),
+                          x=x["tokens"].cpu().numpy(), T=x["temperature"].cpu().numpy(), B=B, K=K)
+                     for x in sets]
+            main_, one, nump, par = cpu_legs_dense(hosts, records, seed, args.path == "greedy", info,
+                                                   early_exit=args.early_exit)
+            result["cpu_baseline"] = main_
+            result["cpu_baseline_single_thread"] = one
+            result["cpu_baseline_numpy"] = nump
+            result["parity"] = par
     print(json.dumps(result), flush=True)
 
 
