@@ -27,7 +27,8 @@
  *     (impossible in exact arithmetic) it draws from p_t and flags NOTE_FALLBACK.
  *
  * Memory.  Every pointer named "device" is device memory owned by the caller.  The
- * library never allocates, frees or retains memory.  All calls are asynchronous on
+ * library never allocates, frees or retains memory (spec_verify_noalloc uses a static
+ * scratch array of the library instead of a caller workspace).  All calls are asynchronous on
  * `stream` (a hipStream_t passed as void*; NULL = the null stream) and never
  * synchronise the host.  Outputs stay on the device.
  *
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SV_ABI_VERSION 4
+#define SV_ABI_VERSION 5
 
 /* Host-side return codes. */
 typedef enum sv_status {
@@ -55,7 +56,9 @@ typedef enum sv_status {
     SV_ERR_ARG = 1,        /* bad size, NULL required pointer, misaligned pointer        */
     SV_ERR_DTYPE = 2,      /* dtype is not one of sv_dtype                                */
     SV_ERR_WORKSPACE = 3,  /* workspace NULL, misaligned or smaller than required        */
-    SV_ERR_HIP = 4         /* a kernel launch failed                                      */
+    SV_ERR_HIP = 4,        /* a kernel launch failed                                      */
+    SV_ERR_SCRATCH = 5     /* spec_verify_noalloc: the call needs more workspace than its
+                              static scratch buffer holds (SV_NOALLOC_SCRATCH_BYTES)        */
 } sv_status;
 
 /* Logit storage.  bf16 = the upper 16 bits of an IEEE fp32 (round-trip exact widening). */
@@ -68,7 +71,9 @@ typedef enum sv_dtype {
 #define SV_SEQ_OK               0
 #define SV_SEQ_ERR_TOKEN        1   /* a draft token outside [0, V)                                 */
 #define SV_SEQ_ERR_LOGIT        2   /* NaN in a row the sequence reads, a row whose max is -inf, or
-                                       (sampled sequences) a +inf logit                             */
+                                       (sampled sequences) a +inf logit or a row whose maximum m
+                                       has |m| * fp32(log2(e) / T) >= 2^30 (outside the supported
+                                       range of scaled logits)                                      */
 #define SV_SEQ_ERR_TEMPERATURE  4   /* T NaN, negative, infinite, or in (0, FLT_MIN)                */
 #define SV_SEQ_ERR_UNIFORM      8   /* (sampled sequences) u NaN or outside [0, 1)                  */
 #define SV_SEQ_NOTE_FALLBACK   16   /* not an error: a categorical draw fell back (see above)       */
@@ -124,6 +129,30 @@ sv_status spec_verify(const void* target_logits, const void* draft_logits, int d
                       int32_t* out_tokens, int32_t* out_accept_len,
                       float* out_p, float* out_q, int32_t* out_status,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify for callers that cannot allocate device memory, not even a workspace:
+ * code being captured into a HIP graph, serving loops and harnesses that forbid
+ * allocation.  The same computation, kernels and outputs as spec_verify (bit for bit);
+ * the workspace is a static device array of the library, SV_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) per GPU, which each GPU the library runs on holds until the process ends.
+ * The call itself allocates nothing (no hipMalloc, no events).
+ *
+ * Arguments as for spec_verify, without workspace and workspace_bytes.  The stream
+ * must belong to the current device (whose copy of the array is used).  Returns
+ * SV_ERR_SCRATCH, before any HIP call, when sv_workspace_bytes(B, K, V) exceeds
+ * SV_NOALLOC_SCRATCH_BYTES (B=1024, K=10, V=262144 needs 55.5 MiB and fits), and
+ * SV_ERR_ARG when the stream belongs to another device.  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (different streams, or host threads
+ * without ordering) race.  Nothing in the array needs to start at zero: each call
+ * initialises what it reads.
+ */
+#define SV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+sv_status spec_verify_noalloc(const void* target_logits, const void* draft_logits, int dtype,
+                              const int32_t* draft_tokens, const float* uniforms,
+                              const float* temperature, int B, int K, int V,
+                              int32_t* out_tokens, int32_t* out_accept_len,
+                              float* out_p, float* out_q, int32_t* out_status, void* stream);
 
 /*
  * spec_verify reading each sequence's rows only up to its first rejection: the tests run

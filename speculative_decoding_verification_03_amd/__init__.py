@@ -12,17 +12,18 @@ __all__ = [
     "LibraryMissing", "SpecVerifyError", "lib", "lib_path",
     "sv_abi_version", "sv_status_string", "sv_workspace_bytes",
     "spec_verify", "spec_verify_greedy", "sv_fill_uniforms", "Workspace", "spec_verify_philox",
-    "spec_verify_early_exit",
+    "spec_verify_early_exit", "spec_verify_noalloc", "SV_NOALLOC_SCRATCH_BYTES",
     "spec_verify_ragged", "spec_verify_greedy_ragged", "sv_fill_uniforms_ragged", "sv_sample",
     "spec_verify_tree_greedy", "sv_tree_attention_mask", "SV_TREE_MAX_NODES",
     "sv_profile_begin", "sv_profile_end",
-    "SV_OK", "SV_ERR_ARG", "SV_ERR_DTYPE", "SV_ERR_WORKSPACE", "SV_ERR_HIP",
+    "SV_OK", "SV_ERR_ARG", "SV_ERR_DTYPE", "SV_ERR_WORKSPACE", "SV_ERR_HIP", "SV_ERR_SCRATCH",
     "SV_DTYPE_F32", "SV_DTYPE_BF16",
     "SV_SEQ_ERR_TOKEN", "SV_SEQ_ERR_LOGIT", "SV_SEQ_ERR_TEMPERATURE", "SV_SEQ_ERR_UNIFORM",
     "SV_SEQ_NOTE_FALLBACK", "SV_SEQ_ERR_OFFSETS", "SV_SEQ_ERR_TREE",
 ]
 
-SV_OK, SV_ERR_ARG, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_HIP = 0, 1, 2, 3, 4
+SV_OK, SV_ERR_ARG, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_HIP, SV_ERR_SCRATCH = 0, 1, 2, 3, 4, 5
+SV_NOALLOC_SCRATCH_BYTES = 64 << 20
 SV_DTYPE_F32, SV_DTYPE_BF16 = 0, 1
 SV_SEQ_ERR_TOKEN, SV_SEQ_ERR_LOGIT, SV_SEQ_ERR_TEMPERATURE, SV_SEQ_ERR_UNIFORM = 1, 2, 4, 8
 SV_SEQ_NOTE_FALLBACK = 16
@@ -69,6 +70,9 @@ def lib():
     L.spec_verify_early_exit.restype = i32
     L.spec_verify_early_exit.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32,
                                          vp, vp, vp, vp, vp, vp, sz, vp]
+    L.spec_verify_noalloc.restype = i32
+    L.spec_verify_noalloc.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32,
+                                      vp, vp, vp, vp, vp, vp]
     L.spec_verify_philox.restype = i32
     L.spec_verify_philox.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, u64, u64, u64, vp,
                                      vp, vp, vp, vp, vp, vp, sz, vp]
@@ -247,6 +251,30 @@ def spec_verify_early_exit(target_logits, draft_logits, draft_tokens, uniforms, 
     return spec_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, out=out,
                        with_probs=with_probs, workspace=workspace, stream=stream,
                        _entry="spec_verify_early_exit")
+
+
+def spec_verify_noalloc(target_logits, draft_logits, draft_tokens, uniforms, temperature, out,
+                        stream=None):
+    """spec_verify with the library's static scratch array as its workspace (for callers
+    that cannot allocate, e.g. under graph capture): `out` (tokens, accept_len, p, q,
+    status; p and q may be None) must be given.  Same outputs as spec_verify."""
+    torch = _torch()
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    code = _dtype_code(target_logits)
+    _check(target_logits, "target_logits")
+    _check(draft_logits, "draft_logits", target_logits.dtype, (B, K, V))
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K))
+    _check(uniforms, "uniforms", torch.float32, (B, K + 1))
+    _check(temperature, "temperature", torch.float32, (B,))
+    st = lib().spec_verify_noalloc(
+        _ptr(target_logits), _ptr(draft_logits), code, _ptr(draft_tokens), _ptr(uniforms),
+        _ptr(temperature), B, K, V, _ptr(out["tokens"]), _ptr(out["accept_len"]),
+        _ptr(out.get("p")), _ptr(out.get("q")), _ptr(out["status"]), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_noalloc")
+    _record(stream, *[t for t in out.values() if t is not None])
+    return out
 
 
 def spec_verify_philox(target_logits, draft_logits, draft_tokens, temperature, seed, domain, step,

@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
 SOURCES = ["sv_api.cpp", "sv_pass1.hip", "sv_resolve.hip", "sv_sweep.hip", "sv_final.hip", "sv_sample.hip",
-           "sv_rng.hip", "sv_tree.hip"]
+           "sv_rng.hip", "sv_tree.hip", "sv_noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

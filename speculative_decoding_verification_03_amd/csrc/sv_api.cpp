@@ -11,7 +11,33 @@
 
 #include "sv_common.h"
 
+namespace sv {
+
+// B*(K+1)*V and the block counts must fit comfortably.
+bool shape_ok(int B, int K, int V) {
+    if (B < 0 || K < 0 || V < 1) return false;
+    const __int128 cells = (__int128)B * (K + 1) * V;
+    if (cells > (__int128)INT64_MAX / 8) return false;
+    return true;
+}
+
+// Workspace for both entry points: the larger of the two layouts.
+size_t workspace_need(int B, int K, int V) {
+    size_t need = 0;
+    for (int esize : {2, 4})
+        for (int R : {2 * K + 1, K + 1}) {
+            const size_t t = make_layout(B, K, V, esize, R).total;
+            if (t > need) need = t;
+        }
+    return need;
+}
+
+}  // namespace sv
+
 namespace {
+
+using sv::shape_ok;
+using sv::workspace_need;
 
 // Benchmark timing: per recorded call three events (before pass 1, between the passes,
 // after pass 2).  Events are created on demand and kept for reuse.
@@ -42,25 +68,6 @@ Profile g_prof;
 using sv::Layout;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-
-// B*(K+1)*V and the block counts must fit comfortably.
-bool shape_ok(int B, int K, int V) {
-    if (B < 0 || K < 0 || V < 1) return false;
-    const __int128 cells = (__int128)B * (K + 1) * V;
-    if (cells > (__int128)INT64_MAX / 8) return false;
-    return true;
-}
-
-// Workspace for both entry points: the larger of the two layouts.
-size_t workspace_need(int B, int K, int V) {
-    size_t need = 0;
-    for (int esize : {2, 4})
-        for (int R : {2 * K + 1, K + 1}) {
-            const size_t t = sv::make_layout(B, K, V, esize, R).total;
-            if (t > need) need = t;
-        }
-    return need;
-}
 
 bool grid_ok(int B, int R, const Layout& L) {
     const __int128 blocks1 = (__int128)B * R * L.nchunk1;
@@ -110,22 +117,24 @@ sv::VerifyArgs make_args(const void* target, const void* draft, const int32_t* t
 // pass 1, then `second` (the resolve and draws, or the tree resolve), with the
 // benchmark events around each
 template <class F>
-sv_status launch_two(const sv::VerifyArgs& a, int bf16, void* stream, F&& second) {
+sv_status launch_two(const sv::VerifyArgs& a, int bf16, void* stream, F&& second, bool profile = true) {
     hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
-    if (g_prof.on) {
+    const bool prof = profile && g_prof.on;
+    if (prof) {
         for (auto& e : ev) e = g_prof.next();
         g_prof.calls++;
         g_prof.record(ev[0], stream);
     }
     if (sv::launch_pass1(a, bf16, 0, a.B, stream) != 0) return SV_ERR_HIP;
-    if (g_prof.on) g_prof.record(ev[1], stream);
+    if (prof) g_prof.record(ev[1], stream);
     if (second() != 0) return SV_ERR_HIP;
-    if (g_prof.on) g_prof.record(ev[2], stream);
+    if (prof) g_prof.record(ev[2], stream);
     return SV_OK;
 }
 
-sv_status launch(const sv::VerifyArgs& a, int bf16, void* stream) {
-    return launch_two(a, bf16, stream, [&] { return sv::launch_draw(a, bf16, 0, a.B, stream); });
+sv_status launch(const sv::VerifyArgs& a, int bf16, void* stream, bool profile = true) {
+    return launch_two(a, bf16, stream, [&] { return sv::launch_draw(a, bf16, 0, a.B, stream); },
+                      profile);
 }
 
 // Packed-layout sizes: (total + B) target rows of V elements must fit comfortably.
@@ -150,6 +159,7 @@ const char* sv_status_string(int status) {
         case SV_ERR_DTYPE: return "unsupported dtype";
         case SV_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case SV_ERR_HIP: return "HIP launch failed";
+        case SV_ERR_SCRATCH: return "the call needs more than the static scratch buffer";
         default: return "unknown status";
     }
 }
@@ -168,6 +178,23 @@ sv_status spec_verify(const void* target_logits, const void* draft_logits, int d
                       int32_t* out_tokens, int32_t* out_accept_len,
                       float* out_p, float* out_q, int32_t* out_status,
                       void* workspace, size_t workspace_bytes, void* stream) {
+    return (sv_status)sv::verify_dense_call(target_logits, draft_logits, dtype, draft_tokens,
+                                            uniforms, temperature, B, K, V, out_tokens,
+                                            out_accept_len, out_p, out_q, out_status, workspace,
+                                            workspace_bytes, stream, true, true);
+}
+
+}  // extern "C"
+
+namespace sv {
+
+int verify_dense_call(const void* target_logits, const void* draft_logits, int dtype,
+                      const int32_t* draft_tokens, const float* uniforms,
+                      const float* temperature, int B, int K, int V,
+                      int32_t* out_tokens, int32_t* out_accept_len,
+                      float* out_p, float* out_q, int32_t* out_status,
+                      void* workspace, size_t workspace_bytes, void* stream, bool profile,
+                      bool launch_it) {
     if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_DTYPE;
     if (!shape_ok(B, K, V)) return SV_ERR_ARG;
     if (B == 0) return SV_OK;
@@ -188,12 +215,17 @@ sv_status spec_verify(const void* target_logits, const void* draft_logits, int d
     const int R = 2 * K + 1;
     const Layout L = sv::make_layout(B, K, V, (int)esz, R);
     if (!grid_ok(B, R, L)) return SV_ERR_ARG;
+    if (!launch_it) return SV_OK;
 
     const sv::VerifyArgs a = make_args(target_logits, draft_logits, draft_tokens, uniforms,
                                        temperature, B, K, V, R, L, workspace, out_tokens,
                                        out_accept_len, out_p, out_q, out_status);
-    return launch(a, dtype == SV_DTYPE_BF16, stream);
+    return launch(a, dtype == SV_DTYPE_BF16, stream, profile);
 }
+
+}  // namespace sv
+
+extern "C" {
 
 sv_status spec_verify_early_exit(const void* target_logits, const void* draft_logits, int dtype,
                                  const int32_t* draft_tokens, const float* uniforms,

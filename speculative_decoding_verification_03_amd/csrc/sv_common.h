@@ -205,6 +205,20 @@ struct TreeArgs {
     int32_t* out_depth;       // [B][N] or null (mask kernel)
 };
 
+// Host helpers of the C entry points (sv_api.cpp): the shape check, the workspace size
+// of (B, K, V), and spec_verify's validation and launches on a given workspace (returns
+// an sv_status; profile: record the benchmark events while they are on; launch_it false:
+// validate the arguments only, touching neither the workspace nor the GPU).
+bool shape_ok(int B, int K, int V);
+size_t workspace_need(int B, int K, int V);
+int verify_dense_call(const void* target_logits, const void* draft_logits, int dtype,
+                      const int32_t* draft_tokens, const float* uniforms,
+                      const float* temperature, int B, int K, int V,
+                      int32_t* out_tokens, int32_t* out_accept_len,
+                      float* out_p, float* out_q, int32_t* out_status,
+                      void* workspace, size_t workspace_bytes, void* stream, bool profile,
+                      bool launch_it);
+
 // Internal launchers (return hipError_t as int; 0 = success).  Sequences [b0, b1).
 // launch_draw runs the resolve and the draws of those sequences (greedy-only calls: the
 // resolve only) after their pass 1, on the same stream.

@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
         "spec_verify_greedy", "sv_fill_uniforms", "sv_profile_begin", "sv_profile_end",
         "spec_verify_ragged", "spec_verify_greedy_ragged", "sv_sample",
         "sv_fill_uniforms_ragged", "spec_verify_tree_greedy", "sv_tree_attention_mask",
-        "spec_verify_philox", "spec_verify_early_exit"])
+        "spec_verify_philox", "spec_verify_early_exit", "spec_verify_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -39,10 +39,11 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert sv.sv_abi_version() == 4
+    assert sv.sv_abi_version() == 5
     assert sv.sv_status_string(sv.SV_OK) == "ok"
     assert sv.sv_status_string(sv.SV_ERR_ARG) == "invalid argument"
     assert sv.sv_status_string(sv.SV_ERR_WORKSPACE).startswith("workspace")
+    assert sv.sv_status_string(sv.SV_ERR_SCRATCH).startswith("the call needs more")
     assert sv.sv_status_string(99) == "unknown status"
 
 
@@ -286,3 +287,39 @@ def test_binding_refuses_host_tensors():
     t = torch.zeros((2, 3, 8))
     with pytest.raises(ValueError):
         sv.spec_verify_greedy(t, torch.zeros((2, 2), dtype=torch.int32))
+
+
+def call_noalloc(**kw):
+    args = dict(t=GOOD, d=GOOD, dtype=sv.SV_DTYPE_BF16, x=GOOD, u=GOOD, T=GOOD, B=4, K=3, V=64,
+                tok=GOOD, n=GOOD, p=GOOD, q=GOOD, st=GOOD)
+    args.update(kw)
+    a = args
+    return sv.lib().spec_verify_noalloc(_p(a["t"]), _p(a["d"]), a["dtype"], _p(a["x"]), _p(a["u"]),
+                                        _p(a["T"]), a["B"], a["K"], a["V"], _p(a["tok"]), _p(a["n"]),
+                                        _p(a["p"]), _p(a["q"]), _p(a["st"]), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), sv.SV_ERR_DTYPE),
+    (dict(B=-1), sv.SV_ERR_ARG),
+    (dict(V=0), sv.SV_ERR_ARG),
+    (dict(t=0), sv.SV_ERR_ARG),
+    (dict(u=0), sv.SV_ERR_ARG),
+    (dict(st=0), sv.SV_ERR_ARG),
+    (dict(t=GOOD + 1), sv.SV_ERR_ARG),
+    (dict(B=2 ** 30, K=2 ** 20, V=2 ** 30), sv.SV_ERR_ARG),
+    # more workspace than the static scratch array holds, refused before any HIP call
+    (dict(B=4096, K=10, V=262144), sv.SV_ERR_SCRATCH),
+    (dict(B=2048, K=16, V=152064), sv.SV_ERR_SCRATCH),
+    (dict(B=0, t=0, d=0, x=0, u=0, T=0, tok=0, n=0, st=0), sv.SV_OK),
+])
+def test_noalloc_rejects_bad_arguments_and_sizes(kw, status):
+    assert call_noalloc(**kw) == status
+
+
+def test_noalloc_limit_covers_the_workloads():
+    limit = 64 << 20
+    for B, K, V in ((1, 4, 1000), (8, 4, 32000), (64, 5, 128256), (256, 8, 152064),
+                    (1024, 10, 262144)):
+        assert sv.sv_workspace_bytes(B, K, V) <= limit
+    assert sv.sv_workspace_bytes(4096, 10, 262144) > limit
