@@ -95,8 +95,9 @@ sv::VerifyArgs make_args(const void* target, const void* draft, const int32_t* t
     a.R = R;
     a.nchunk1 = L.nchunk1;
     a.ch1 = L.ch1;
+    a.seg = L.seg;
     a.nseg = L.nseg;
-    sv::chunking2(B, V, a.nchunk2, a.spc);
+    sv::chunking2(B, V, L.seg, a.nchunk2, a.spc);
     a.desc = ws + L.off_desc;
     a.part1 = reinterpret_cast<sv::RowPartial*>(ws + L.off_part1);
     a.part2 = reinterpret_cast<sv::DrawPartial*>(ws + L.off_part2);

@@ -56,13 +56,16 @@ struct alignas(16) Bucket {
     double a, b;
 };
 
-constexpr int kSeg = 4096;         // positions per draw segment (one partial each)
+constexpr int kSeg = 4096;         // longest draw segment (positions; one partial each)
+constexpr int kSegMin = 512;       // shortest draw segment
+constexpr int64_t kSegCount = 4096;  // segments a call aims for: one per resident sweep wave
 constexpr int kWtabLen = 4356;     // doubles per sequence of the bf16 weight table
 constexpr int kSeqDescBytes = 64;  // workspace slot of the resolve's per-sequence result
 
 struct Layout {
     int nchunk1, ch1;  // pass-1 chunks per row and elements per chunk (multiple of 64)
-    int nseg;          // draw segments per sequence: ceil(V / kSeg)
+    int seg;           // positions per draw segment of this call (seg_len)
+    int nseg;          // draw segments per sequence: ceil(V / seg)
     size_t off_desc, off_part1, off_part2, off_bkt, off_wtab, off_limit, off_deal, off_deal_desc, total;
 };
 
@@ -98,14 +101,24 @@ inline void chunking1(int64_t rows, int V, int esize, int& nchunk1, int& ch1) {
     ch1 = (int)ch;
 }
 
-inline int segments(int V) { return (int)ceil_div(V, (int64_t)kSeg); }
+// Draw segment length of a call over B sequences of V positions: the shortest power of two
+// in [kSegMin, kSeg] that keeps the call's segments (one sweep wave each) near kSegCount,
+// so that a small batch still spreads its draws over the chip's waves; large batches take
+// kSeg (the sweep then needs several rounds of resident waves anyway).
+inline int seg_len(int64_t B, int V) {
+    int L = kSegMin;
+    while (L < kSeg && B * ceil_div(V, (int64_t)L) > kSegCount) L *= 2;
+    return L;
+}
+
+inline int segments(int V, int seg) { return (int)ceil_div(V, (int64_t)seg); }
 
 // Draw chunks (workgroups) per sequence for a launch over `seqs` sequences: about
 // kTargetBlocks2 workgroups in all; each chunk holds spc whole segments, at least one per
 // wave of a workgroup when the row has that many (each workgroup copies the weight table
 // once, so a chunk should keep all its waves busy).
-inline void chunking2(int64_t seqs, int V, int& nchunk2, int& spc) {
-    const int64_t nseg = segments(V);
+inline void chunking2(int64_t seqs, int V, int seg, int& nchunk2, int& spc) {
+    const int64_t nseg = segments(V, seg);
     const int64_t want = seqs > 0 ? ceil_div(kTargetBlocks2, seqs) : 1;
     const int64_t n = want < 1 ? 1 : (want > nseg ? nseg : want);
     int64_t per = ceil_div(nseg, n);
@@ -122,7 +135,8 @@ inline Layout make_layout(int B, int K, int V, int esize, int rows_per_seq) {
     (void)K;
     Layout L;
     chunking1((int64_t)B * rows_per_seq, V, esize, L.nchunk1, L.ch1);
-    L.nseg = segments(V);
+    L.seg = seg_len(B, V);
+    L.nseg = segments(V, L.seg);
     size_t off = 0;
     L.off_desc = off;
     off = align256(off + kSeqDescBytes * (size_t)B);
@@ -161,6 +175,7 @@ struct VerifyArgs {
     int nchunk1, ch1;          // pass-1 chunking
     int nchunk2, spc;          // draw chunking of this launch: chunks per sequence, segments
                                // per chunk
+    int seg;                   // positions per draw segment (seg_len)
     int nseg;                  // draw segments per sequence
     int nseq2;                 // sequences of this draw launch (set by the launcher)
     // The draw deal of this call (null when no draw follows): deal_desc[nseq2] descriptors

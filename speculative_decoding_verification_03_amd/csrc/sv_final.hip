@@ -301,7 +301,7 @@ __device__ __forceinline__ void final_seq(const VerifyArgs& a, DrawRows<E> r, co
                 base = sh_base;
             }
             int lo, hi;
-            seg_range(a.V, kSeg, hit, lo, hi);
+            seg_range(a.V, a.seg, hit, lo, hi);
             y = block_search<E, NT>(r, lo, hi, base, tgt, false, u);
         }
     }
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(VerifyArgs a, int 
     exp2_table_init(tab);  // its barrier also publishes wt
     const DrawRows<E> r = draw_rows<E>(a, d, tab, sizeof(E) == 2 ? wt : nullptr);
     if (small)
-        final_seq_small<E, kFinalThreads, kSeg / kFinalThreads>(a, r, d, b, dp, bk0, bkt, a.nseg, kSeg);
+        final_seq_small<E, kFinalThreads, kSeg / kFinalThreads>(a, r, d, b, dp, bk0, bkt, a.nseg, a.seg);
     else
         final_seq<E, kFinalThreads>(a, r, d, b);
 }

@@ -503,7 +503,7 @@ void sweep_kernel(VerifyArgs a, int b0) {
     if constexpr (sizeof(E) == 2) {
         if (r.use_tab) {
             // the wave's first loads go out before the tables reach LDS
-            const int lo = min(a.V, s0 * kSeg), hi = min(a.V, s1 * kSeg);
+            const int lo = min(a.V, s0 * a.seg), hi = min(a.V, s1 * a.seg);
             const bool have_first = r.vec_ok && hi - lo >= kSpan16;
             FirstSpan f;
             if (have_first) {
@@ -515,15 +515,15 @@ void sweep_kernel(VerifyArgs a, int b0) {
             tc.store(wt);
             exp2_table_init(tab);  // its barrier also publishes wt
             if (s0 < s1) {
-                if (r.residual) sweep_wave_tab<true>(r, lo, hi, kSeg, part, bkt, acc, f, have_first);
-                else sweep_wave_tab<false>(r, lo, hi, kSeg, part, bkt, acc, f, have_first);
+                if (r.residual) sweep_wave_tab<true>(r, lo, hi, a.seg, part, bkt, acc, f, have_first);
+                else sweep_wave_tab<false>(r, lo, hi, a.seg, part, bkt, acc, f, have_first);
             }
             done = true;
         }
     }
     if (!done) {
         exp2_table_init(tab);
-        if (s0 < s1) sweep_wave_exp<E>(r, min(a.V, s0 * kSeg), min(a.V, s1 * kSeg), kSeg, part, bkt, acc);
+        if (s0 < s1) sweep_wave_exp<E>(r, min(a.V, s0 * a.seg), min(a.V, s1 * a.seg), a.seg, part, bkt, acc);
     }
 }
 
