@@ -375,7 +375,7 @@ sv_status sv_sample(const void* logits, int dtype, const float* uniforms,
                                        1, L, workspace, out_tokens, nullptr, nullptr, nullptr,
                                        out_status);
     const int bf16 = dtype == SV_DTYPE_BF16;
-    if ((int64_t)V > (int64_t)sv::kSampleMaxSeg * sv::kSeg) return launch(a, bf16, stream);
+    if ((int64_t)V > (int64_t)sv::kSampleMaxSeg * sv::kSampleSeg) return launch(a, bf16, stream);
     // rows of at most kSampleMaxSeg segments: one workgroup per row does everything
     // (timed as the first phase)
     hipEvent_t ev[3] = {nullptr, nullptr, nullptr};

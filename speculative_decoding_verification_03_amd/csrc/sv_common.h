@@ -82,9 +82,11 @@ constexpr int kMinChunk1 = 4096;
 constexpr int kTargetBlocks2 = 2560;
 // Threads of a sweep workgroup: each wave sweeps its own run of draw segments.
 constexpr int kSweepThreads = 256;
-// The one-workgroup-per-row sampler: threads, and the longest row it takes (segments).
+// The one-workgroup-per-row sampler: threads, positions per segment sum, and the longest
+// row it takes (segments; longer rows take the verify kernels at K = 0).
 constexpr int kSampleThreads = 1024;
-constexpr int kSampleMaxSeg = kSampleThreads;
+constexpr int kSampleSeg = 2048;
+constexpr int kSampleMaxSeg = 2 * kSampleThreads;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -1,104 +1,165 @@
-// The draft-side sampler: one draw per row from softmax(z / T), argmax at T = 0.
+// The draft-side sampler: one draw per row from softmax(z / T), argmax at T = 0 (the
+// draft's temperature softmax and categorical draw of the "Desenvolva" listing on the
+// lesson page "Decodificação Especulativa e EAGLE").
+//
+// One 1024-thread workgroup per row.  A sampled row is read once: its weights are taken
+// against a provisional reference, kSampleLift binary orders of weight above R0 (the maximum
+// of the row's first vectors).  Against the row maximum M that scales every weight by one
+// common factor and so leaves the inverse CDF where it is.  The fp64 weights are summed per
+// kSampleSeg-position segment (one wave per segment) while the row's NaN-propagating maximum
+// is taken along, then the segment sums are scanned for u * W and the segment that holds it
+// is searched: token = min{ i : C_i > u * W }, C the prefix sums in index order.  The lift
+// keeps M's weight at 2^-kSampleLift or more, so every weight within 2^-75 of it stays a
+// normal fp64 number, and doubles the span M may lie above R0 before a weight could
+// overflow.  Only beyond that span ((M - R0) c2 > kSampleLift + kSampleRefGap binary orders,
+// e.g. a far outlier at a very low temperature) are the sums taken again against M.  Greedy
+// rows, and rows with a bad temperature or uniform, take one argmax pass.
 #include "sv_draw.h"
 
 namespace sv {
 
 namespace {
 
-// ------------------------------------------------------------------------------------
-// the draft-side sampler: one draw per row from softmax(z / T), the whole row in one
-// workgroup
-// ------------------------------------------------------------------------------------
+// Binary orders of magnitude the weights may reach above the reference's weight 1: sums
+// of up to 2^22 of them stay finite in fp64.
+constexpr double kSampleRefGap = 900.0;
+// Binary orders of weight between R0 and the provisional reference above it (at most
+// 1022 - 75, so that weights within 2^-75 of the row maximum's are normal numbers).
+constexpr double kSampleLift = 900.0;
+// 16-byte vectors per lane of one whole bf16 segment
+constexpr int kSegVecs = kSampleSeg / (64 * 8);
+static_assert(kSampleSeg % (64 * 8) == 0, "sampler segments are whole waves of bf16 vectors");
+static_assert(kSampleMaxSeg <= 2 * kSampleThreads, "the scan takes two segments per thread");
 
-// One wave's fp64 sum of the bonus weights over positions [lo, hi) of r.t: the table fast
-// path over a whole segment of 16-byte vectors when it applies, the exact path otherwise.
-// On the fast path a value outside the table reads NaN: its lane's vector is read again
-// (from cache) and its values outside the table take the fp64 exponential (the callers
-// have ruled out NaN and +inf logits).  bad: the exact path met a NaN or +inf logit
-// (wave-uniform).
-template <typename E>
-__device__ __forceinline__ double wave_row_sum(const DrawRows<E>& r, int lo, int hi, bool& bad) {
-    constexpr int VEC = Logit<E>::kVec;
-    const int lane = threadIdx.x & 63;
+// NaN-propagating maximum of the 8 bf16 values of a vector.
+__device__ __forceinline__ float vec_nmax(u32x4 v) {
+    float z[8];
+    Logit<uint16_t>::unpack(v, z);
+    float m = nmax(z[0], z[1]);
+#pragma unroll
+    for (int k = 2; k < 8; ++k) m = nmax(m, z[k]);
+    return m;
+}
+
+// Loads of one whole bf16 segment of a lane (positions lo + (k*64 + lane)*8 .. +7).
+__device__ __forceinline__ void seg_load(const uint16_t* row, int lo, int lane, u32x4 (&v)[kSegVecs]) {
+#pragma unroll
+    for (int k = 0; k < kSegVecs; ++k) v[k] = load16(row + lo + (k * 64 + lane) * 8);
+}
+
+// A lane's fp64 weight sum over its vectors of a whole bf16 segment (already loaded), with
+// table weights; a vector holding a value outside the table (its sum turns NaN on a
+// sentinel) is read again and summed with the exact weights.  mx: the lane's
+// NaN-propagating maximum of the values, updated.
+__device__ __forceinline__ double seg_sum_tab(const DrawRows<uint16_t>& r, const u32x4 (&v)[kSegVecs], int lo,
+                                              int lane, float& mx) {
     double s = 0.0;
-    bool exact = true;
-    if constexpr (sizeof(E) == 2) {
-        constexpr int kU = kSeg / (64 * VEC);  // vectors per lane of a whole segment
-        if (r.use_tab && r.vec_ok && hi - lo == kSeg) {
-            u32x4 v[kU];  // every load of the segment in flight at once
+    uint32_t again = 0;
 #pragma unroll
-            for (int k = 0; k < kU; ++k) v[k] = load16(r.t + lo + (k * 64 + lane) * VEC);
-            uint32_t again = 0;  // this lane's vectors with a value outside the table
+    for (int k = 0; k < kSegVecs; ++k) {
+        mx = nmax(mx, vec_nmax(v[k]));
+        const uint32_t x4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+        double sk = 0.0;
 #pragma unroll
-            for (int k = 0; k < kU; ++k) {
-                const uint32_t x4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-                double sk = 0.0;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    uint32_t o0, o1;
-                    tab_offsets(x4[q], o0, o1);
-                    sk += tab_at(r.wt, o0);
-                    sk += tab_at(r.wt, o1);
-                }
-                if (sk != sk) again |= 1u << k;
-                else s += sk;
-            }
-            while (again) {  // rare
-                const int k = __ffs(again) - 1;
-                again &= again - 1;
-                const u32x4 w = load16(r.t + lo + (k * 64 + lane) * VEC);
-                const uint32_t x4[4] = {w.x, w.y, w.z, w.w};
-                double sk = 0.0;
+        for (int q = 0; q < 4; ++q) {
+            uint32_t o0, o1;
+            tab_offsets(x4[q], o0, o1);
+            sk += tab_at(r.wt, o0);
+            sk += tab_at(r.wt, o1);
+        }
+        if (sk != sk) again |= 1u << k;
+        else s += sk;
+    }
+    while (again) {  // rare
+        const int k = __ffs(again) - 1;
+        again &= again - 1;
+        const u32x4 w = load16(r.t + lo + (k * 64 + lane) * 8);
+        const uint32_t x4[4] = {w.x, w.y, w.z, w.w};
+        double sk = 0.0;
 #pragma unroll 1
-                for (int q = 0; q < 8; ++q) {
-                    const uint32_t h = (x4[q >> 1] >> (16 * (q & 1))) & 0xffffu;
-                    sk += r.a_of(__uint_as_float(h << 16));
-                }
-                s += sk;
-            }
-            exact = false;
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t h = (x4[q >> 1] >> (16 * (q & 1))) & 0xffffu;
+            sk += r.a_of(__uint_as_float(h << 16));
         }
+        s += sk;
     }
-    bool b = false;
-    if (exact) {
-        s = 0.0;
-        for (int i0 = lo; i0 < hi; i0 += 64 * VEC) {
-            float z[VEC];
-            load_vec(r.t, i0 + lane * VEC, hi, r.vec_ok, z);
+    return s;
+}
+
+// A lane's weight sum over positions [lo, hi) element by element (exact weights), and the
+// NaN-propagating maximum of what it reads; positions past hi read -inf (weight 0).
+template <typename E>
+__device__ __forceinline__ double seg_sum_exact(const DrawRows<E>& r, int lo, int hi, int lane, float& mx) {
+    constexpr int VEC = Logit<E>::kVec;
+    double s = 0.0;
+    for (int i0 = lo; i0 < hi; i0 += 64 * VEC) {
+        float z[VEC];
+        load_vec(r.t, i0 + lane * VEC, hi, r.vec_ok, z);
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) {
-                b |= (z[k] != z[k]) | (z[k] == INFINITY);
-                s += r.a_of(z[k]);
-            }
+        for (int k = 0; k < VEC; ++k) {
+            mx = nmax(mx, z[k]);
+            s += r.a_of(z[k]);
         }
     }
-    bad = __any(b);
-    return wave_sum(s);
+    return s;
 }
 
-// Sums of the bonus weights of every segment of the row into segsum (one wave per
-// segment); returns whether a NaN or +inf logit was met.  Contains __syncthreads().
+// Sums of the weights of every segment of the row into segsum, one wave per segment
+// (segments w, w + NW, ...), and each lane's NaN-propagating maximum of the values read.
+// With the table (bf16, aligned rows) every whole segment's loads go out before the
+// previous one is summed.  first: the wave's first whole segment, already loaded (when
+// have_first).  Contains no barrier.
 template <typename E, int NT>
-__device__ __forceinline__ bool row_segment_sums(const DrawRows<E>& r, int V, double* segsum, int* shi) {
-    const int w = threadIdx.x >> 6, nseg = (V + kSeg - 1) / kSeg;
-    int bad = 0;
-    for (int k = w; k < nseg; k += NT / 64) {
-        int lo, hi;
-        seg_range(V, kSeg, k, lo, hi);
-        bool bk;
-        const double sk = wave_row_sum(r, lo, hi, bk);
-        bad |= bk;
-        if ((threadIdx.x & 63) == 0) segsum[k] = sk;
+__device__ __forceinline__ float row_segment_sums(const DrawRows<E>& r, int V, double* segsum, bool have_first,
+                                                  const u32x4 (&first)[kSegVecs]) {
+    constexpr int NW = NT / 64;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nseg = (V + kSampleSeg - 1) / kSampleSeg;
+    float mx = -INFINITY;
+    if constexpr (sizeof(E) == 2) {
+        if (r.use_tab && r.vec_ok) {
+            const uint16_t* t = reinterpret_cast<const uint16_t*>(r.t);
+            const int nwhole = V / kSampleSeg;
+            u32x4 cur[kSegVecs];
+            if (w < nwhole) {
+                if (have_first) {
+#pragma unroll
+                    for (int k = 0; k < kSegVecs; ++k) cur[k] = first[k];
+                } else {
+                    seg_load(t, w * kSampleSeg, lane, cur);
+                }
+            }
+            for (int k = w; k < nseg; k += NW) {
+                const int lo = k * kSampleSeg;
+                double s;
+                if (k < nwhole) {
+                    u32x4 nxt[kSegVecs];
+                    const bool more = k + NW < nwhole;
+                    if (more) seg_load(t, (k + NW) * kSampleSeg, lane, nxt);
+                    s = seg_sum_tab(r, cur, lo, lane, mx);
+                    if (more) {
+#pragma unroll
+                        for (int q = 0; q < kSegVecs; ++q) cur[q] = nxt[q];
+                    }
+                } else {
+                    s = seg_sum_exact(r, lo, V, lane, mx);
+                }
+                s = wave_sum(s);
+                if (lane == 0) segsum[k] = s;
+            }
+            return mx;
+        }
     }
-    return block_or<NT / 64>(bad, shi) != 0;  // its barrier also publishes segsum
+    for (int k = w; k < nseg; k += NW) {
+        const int lo = k * kSampleSeg;
+        double s = seg_sum_exact(r, lo, min(V, lo + kSampleSeg), lane, mx);
+        s = wave_sum(s);
+        if (lane == 0) segsum[k] = s;
+    }
+    return mx;
 }
 
-// grid = rows, one workgroup per row.  Phase 1 streams the row for its maximum (greedy
-// rows: the lowest index reaching it), with normal loads so that the row stays in cache.
-// Sampled rows then tabulate their weights against that maximum (bf16), sum the weights
-// per kSeg segment (one wave per segment; the row is read again, mostly from cache), scan
-// the segment sums for u * W and search the segment that holds it:
-// token = min{ i : C_i > u * W }, C the prefix sums in index order.
+// grid = rows, one workgroup per row (see the top of this file).
 template <typename E>
 __global__ __launch_bounds__(kSampleThreads) void sample_kernel(VerifyArgs a) {
     constexpr int NT = kSampleThreads, NW = NT / 64;
@@ -110,66 +171,66 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(VerifyArgs a) {
     __shared__ int shi[NW];
     __shared__ double shd[2 * NW];
     __shared__ double sh_base;
-    const int b = blockIdx.x, tid = threadIdx.x;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int V = a.V;
     const float T = a.temperature[b];
     const bool sampled = !(T == 0.0f);
     const E* row = static_cast<const E*>(a.target) + (int64_t)b * V;
     const float u = sampled ? a.uniforms[b] : 0.0f;
     const bool vec_ok = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
-    const int nvec = vec_ok ? V / VEC : 0;
     int err = 0;
     if (temperature_bad(T)) err |= kSeqErrTemperature;
     if (sampled && !(u >= 0.0f && u < 1.0f)) err |= kSeqErrUniform;
 
-    // phase 1: maximum, NaN and +inf (sampled rows), the lowest index of the maximum;
-    // kU loads in flight per thread
-    float mx = -INFINITY;
-    int idx = 0x7fffffff;
-    int bad = 0;
-    constexpr int kU = 4;
-    for (int v0 = 0; v0 < nvec; v0 += kU * NT) {
-        u32x4 raw[kU];
+    if (!sampled || err) {
+        // one pass: maximum, NaN and +inf (sampled rows), the lowest index of the maximum;
+        // kU loads in flight per thread
+        const int nvec = vec_ok ? V / VEC : 0;
+        float mx = -INFINITY;
+        int idx = 0x7fffffff;
+        int bad = 0;
+        constexpr int kU = 4;
+        for (int v0 = 0; v0 < nvec; v0 += kU * NT) {
+            u32x4 raw[kU];
 #pragma unroll
-        for (int k = 0; k < kU; ++k) {
-            const int v = v0 + k * NT + tid;
-            raw[k] = v < nvec ? *reinterpret_cast<const u32x4*>(row + (int64_t)v * VEC) : Logit<E>::neg_inf16();
-        }
+            for (int k = 0; k < kU; ++k) {
+                const int v = v0 + k * NT + tid;
+                raw[k] = v < nvec ? load16(row + (int64_t)v * VEC) : Logit<E>::neg_inf16();
+            }
 #pragma unroll
-        for (int k = 0; k < kU; ++k) {
-            const int v = v0 + k * NT + tid;
-            float z[VEC];
-            Logit<E>::unpack(raw[k], z);
-            // the vector's NaN-propagating maximum: NaN if it holds a NaN, else +inf if it
-            // holds +inf; only a vector that beats the running maximum is searched for the
-            // lowest index reaching it
-            float tm = z[0];
+            for (int k = 0; k < kU; ++k) {
+                const int v = v0 + k * NT + tid;
+                float z[VEC];
+                Logit<E>::unpack(raw[k], z);
+                // the vector's NaN-propagating maximum: NaN if it holds a NaN, else +inf if
+                // it holds +inf; only a vector that beats the running maximum is searched
+                // for the lowest index reaching it
+                float tm = z[0];
 #pragma unroll
-            for (int e = 1; e < VEC; ++e) tm = nmax(tm, z[e]);
-            bad |= (tm != tm) | (sampled && tm == INFINITY);
-            if (tm > mx) {
-                int e0 = VEC - 1;
+                for (int e = 1; e < VEC; ++e) tm = nmax(tm, z[e]);
+                bad |= (tm != tm) | (sampled && tm == INFINITY);
+                if (tm > mx) {
+                    int e0 = VEC - 1;
 #pragma unroll
-                for (int e = VEC - 1; e >= 0; --e)
-                    if (z[e] == tm) e0 = e;
-                mx = tm;
-                idx = v * VEC + e0;
+                    for (int e = VEC - 1; e >= 0; --e)
+                        if (z[e] == tm) e0 = e;
+                    mx = tm;
+                    idx = v * VEC + e0;
+                }
             }
         }
-    }
-    for (int i = nvec * VEC + tid; i < V; i += NT) {
-        const float z = Logit<E>::at(row, i);
-        bad |= (z != z) | (sampled && z == INFINITY);
-        if (z > mx) {
-            mx = z;
-            idx = i;
+        for (int i = nvec * VEC + tid; i < V; i += NT) {
+            const float z = Logit<E>::at(row, i);
+            bad |= (z != z) | (sampled && z == INFINITY);
+            if (z > mx) {
+                mx = z;
+                idx = i;
+            }
         }
-    }
-    err |= block_or<NW>(bad ? kSeqErrLogit : 0, shi);
-    block_argmax<NW>(mx, idx, shv, shi);
-    if (mx == -INFINITY) err |= kSeqErrLogit;
-    if (sampled && scaled_range_bad(mx, (float)(kLog2eD / (double)T))) err |= kSeqErrLogit;
-    if (err || !sampled) {
+        err |= block_or<NW>(bad ? kSeqErrLogit : 0, shi);
+        block_argmax<NW>(mx, idx, shv, shi);
+        if (mx == -INFINITY) err |= kSeqErrLogit;
+        if (sampled && scaled_range_bad(mx, (float)(kLog2eD / (double)T))) err |= kSeqErrLogit;
         if (tid == 0) {
             a.out_tokens[b] = err ? -1 : idx;
             a.out_status[b] = err;
@@ -177,51 +238,100 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(VerifyArgs a) {
         return;
     }
 
-    // phase 2: the weight table for reference mx (bf16)
-    exp2_table_init(tab);
+    // a sampled row with a valid temperature and uniform: the provisional reference R0,
+    // the maximum of the first NT vectors of the row, while the wave's first segment and
+    // the 2^(j/256) table come in
+    const int nwhole = V / kSampleSeg;
+    u32x4 first[kSegVecs];
+    const bool have_first = sizeof(E) == 2 && vec_ok && w < nwhole;
+    if constexpr (sizeof(E) == 2) {
+        if (have_first) seg_load(reinterpret_cast<const uint16_t*>(row), w * kSampleSeg, lane, first);
+    }
+    float z0[VEC];
+    load_vec(row, tid * VEC, V, vec_ok, z0);
+    exp2_table_fill(tab);
+    float m0 = z0[0];
+#pragma unroll
+    for (int k = 1; k < VEC; ++k) m0 = nmax(m0, z0[k]);
+    const float R0 = block_nmax<NW>(m0, shv);  // its barriers also publish tab
+
     SeqDesc d{};
     d.mode = kModeBonus;
     d.T = T;
     d.u = u;
-    d.mt = d.md = mx;
+    d.mt = d.md = R0;
     d.trow = d.drow = b;
     DrawRows<E> r = draw_rows<E>(a, d, tab, sizeof(E) == 2 ? wt : nullptr);
     r.t = row;
     r.d = row;
     r.vec_ok = vec_ok;
+    // the lifted reference (a float step above R0; the flush threshold stays kFlushLog2
+    // binary orders below R0)
+    const double c2 = kLog2eD / (double)T;
+    const double ref = (double)R0 + (double)(float)(kSampleLift / c2);
+    r.refA = r.refB = ref;
     if constexpr (sizeof(E) == 2) {
         weight_table_write<E, NT>(r, wt);
         __syncthreads();
     }
+    const float mx = row_segment_sums<E, NT>(r, V, segsum, have_first, first);
+    const float M = block_nmax<NW>(mx, shv);  // its barriers also publish segsum
+    const float c2f = (float)(kLog2eD / (double)T);
+    if ((M != M) || M == INFINITY || M == -INFINITY || scaled_range_bad(M, c2f)) {
+        if (tid == 0) {
+            a.out_tokens[b] = -1;
+            a.out_status[b] = kSeqErrLogit;
+        }
+        return;
+    }
+    if (!(((double)M - ref) * c2 <= kSampleRefGap)) {
+        // weights against R0 could overflow: the sums again against the row maximum
+        d.mt = d.md = M;
+        r = draw_rows<E>(a, d, tab, sizeof(E) == 2 ? wt : nullptr);
+        r.t = row;
+        r.d = row;
+        r.vec_ok = vec_ok;
+        if constexpr (sizeof(E) == 2) {
+            weight_table_write<E, NT>(r, wt);
+            __syncthreads();
+        }
+        row_segment_sums<E, NT>(r, V, segsum, false, first);
+        __syncthreads();
+    }
 
-    // phase 3: weight sums per segment (no NaN or +inf is left to find)
-    row_segment_sums<E, NT>(r, V, segsum, shi);
-
-    // phase 4: the segment holding u * W, then the index inside it
-    const int nseg = (V + kSeg - 1) / kSeg;
+    // the segment holding u * W (two segments per thread), then the index inside it
+    const int nseg = (V + kSampleSeg - 1) / kSampleSeg;
     int status = 0;
-    const double v = tid < nseg ? segsum[tid] : 0.0;
+    const int k0 = 2 * tid, k1 = 2 * tid + 1;
+    const double v0 = k0 < nseg ? segsum[k0] : 0.0;
+    const double v1 = k1 < nseg ? segsum[k1] : 0.0;
     double total;
-    const double ex = block_exclusive_scan<NW>(v, total, shd);
+    const double ex = block_exclusive_scan<NW>(v0 + v1, total, shd);
     int y = -1;
     if (total > 0.0) {
         const double target = (double)u * total;
-        int hit = block_min<NW>((tid < nseg && v > 0.0 && ex + v > target) ? tid : 0x7fffffff, shi);
+        // a segment without mass never holds the first crossing (guards rounding)
+        const bool c0 = v0 > 0.0 && ex + v0 > target;
+        const bool c1 = v1 > 0.0 && (ex + v0) + v1 > target;
+        int hit = block_min<NW>(c0 ? k0 : (c1 ? k1 : 0x7fffffff), shi);
         double tgt = target;
         if (hit == 0x7fffffff) {
             // rounding put u*W past every prefix: the last segment with mass, last index
-            hit = block_max<NW>((tid < nseg && v > 0.0) ? tid : -1, shi);
+            hit = block_max<NW>(v1 > 0.0 ? k1 : (v0 > 0.0 ? k0 : -1), shi);
             tgt = INFINITY;
             status |= kSeqNoteFallback;
         }
-        if (tid == hit) sh_base = ex;
-        __syncthreads();
-        int lo, hi;
-        seg_range(V, kSeg, hit, lo, hi);
-        y = block_search<E, NT>(r, lo, hi, sh_base, tgt, false, (double)u);
+        // total > 0 leaves some segment with mass, so hit >= 0 (checked all the same)
+        if (hit >= 0) {
+            if (tid == (hit >> 1)) sh_base = (hit & 1) ? ex + v0 : ex;
+            __syncthreads();
+            int lo, hi;
+            seg_range(V, kSampleSeg, hit, lo, hi);
+            y = block_search<E, NT>(r, lo, hi, sh_base, tgt, false, (double)u);
+        }
     }
     if (tid == 0) {
-        // the finite row maximum has weight 1: total > 0 and some index qualifies
+        // the finite row maximum has a positive weight: total > 0 and some index qualifies
         a.out_tokens[b] = y;
         a.out_status[b] = y < 0 ? kSeqErrLogit : status;
     }

@@ -251,6 +251,46 @@ def test_sample_ties_and_bad_values(dev, dt):
     assert r["tokens"][30] == 0 and r["tokens"][20] == 0 and r["tokens"][34] == V - 1
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_sample_far_maximum(dev, dt):
+    """Rows whose maximum lies far above that of their first few thousand positions, at a low
+    temperature: a cluster of near-equal peaks beyond them, at two heights, one that the
+    sampler's lifted provisional reference covers and one that needs its second pass over
+    the row; plus the greedy row of the same values.  Tokens and status equal the oracle's
+    and every sampled token is one of the peaks."""
+    V, n_u = 20007, 8
+    say(f"sampler far maximum {dt}")
+    if dt == torch.bfloat16:
+        T0 = 0.1       # 900 / (log2(e) / T) = 62 logits: 84 and 204 lie past it
+        peaks = [(84.0, 84.0, 83.5), (204.0, 204.0, 203.0)]
+    else:
+        T0 = 0.05      # 31 logits: 44 and 104 lie past it
+        peaks = [(44.0, 43.95, 43.9), (104.0, 103.95, 103.98)]
+    spots = [9000, 15001, V - 1]
+    rng = np.random.default_rng(31337)
+    rows, temps = [], []
+    for hi in peaks:
+        for t in [T0] * n_u + [0.0]:
+            z = rng.standard_normal(V).astype(np.float32)
+            z[spots] = hi
+            rows.append(z)
+            temps.append(t)
+    B = len(rows)
+    z = torch.from_numpy(np.stack(rows)).to(dev).to(dt).contiguous()
+    T = torch.tensor(temps, dtype=torch.float32, device=dev)
+    u = torch.from_numpy(host_uniforms(91, 1, 0, B, 0).reshape(B)).to(dev)
+    r = to_host(sv.sv_sample(z, u, T))
+    o = O.sample(logits_to_host(z), u.cpu().numpy(), T.cpu().numpy())
+    t = compare(sample_as_verify(r), sample_as_verify(o), range(B), T.cpu())
+    say("  ", t)
+    t.assert_ok("sampler, far maximum")
+    np.testing.assert_array_equal(r["status"], o["status"])
+    assert (np.asarray(r["status"]) & ~16 == 0).all()
+    assert set(np.asarray(r["tokens"]).tolist()) <= set(spots)
+    greedy = np.asarray(temps) == 0.0
+    assert (np.asarray(r["tokens"])[greedy] == spots[0]).all()
+
+
 # ------------------------------------------------------------------------------------
 # token trees (greedy) and the tree attention mask
 # ------------------------------------------------------------------------------------
