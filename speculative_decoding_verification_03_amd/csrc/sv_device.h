@@ -19,9 +19,22 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// One 16-byte streaming load (non-temporal: logits are read once).
+// A pointer to device global memory, marked so: the compiler then emits global loads
+// rather than flat ones, whose completion every wait for an LDS read would include too.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* gbl(const T* p) {
+    return (const __attribute__((address_space(1))) T*)p;
+}
+
+// A pointer to LDS, marked so.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(3))) T* lds(const T* p) {
+    return (const __attribute__((address_space(3))) T*)p;
+}
+
+// One 16-byte streaming load from global memory (non-temporal: logits are read once).
 __device__ __forceinline__ u32x4 load16(const void* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return __builtin_nontemporal_load(gbl(reinterpret_cast<const u32x4*>(p)));
 }
 
 // Logit element access: fp32 rows or bf16 rows (stored as uint16_t bit patterns).
@@ -31,7 +44,7 @@ struct Logit;
 template <>
 struct Logit<float> {
     static constexpr int kVec = 4;  // elements per 16-byte load
-    __device__ static __forceinline__ float at(const float* p, int64_t i) { return p[i]; }
+    __device__ static __forceinline__ float at(const float* p, int64_t i) { return gbl(p)[i]; }
     __device__ static __forceinline__ u32x4 neg_inf16() {
         const uint32_t n = 0xff800000u;
         return u32x4{n, n, n, n};
@@ -46,7 +59,7 @@ template <>
 struct Logit<uint16_t> {
     static constexpr int kVec = 8;
     __device__ static __forceinline__ float at(const uint16_t* p, int64_t i) {
-        return __uint_as_float((uint32_t)p[i] << 16);
+        return __uint_as_float((uint32_t)gbl(p)[i] << 16);
     }
     __device__ static __forceinline__ u32x4 neg_inf16() {
         const uint32_t n = 0xff80ff80u;  // two bf16 -inf

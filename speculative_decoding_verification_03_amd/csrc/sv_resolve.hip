@@ -43,15 +43,16 @@ struct RowStat {
 // ln x for finite x > 0 in fp64 (the resolve's few logarithms).
 __device__ __forceinline__ double ln(double x) { return log(x); }
 
-// Where the resolve finds a sequence's draft tokens and uniforms: the first kRowsLds
-// tokens and kRowsLds + 1 uniforms in LDS, later ones in memory.
+// Where the resolve finds a sequence's draft tokens and uniforms: the first nx tokens and
+// nu uniforms in LDS, later ones in memory.
 struct ResolveIn {
     const int32_t* xs;        // LDS tokens
     const float* us;          // LDS uniforms
     const int32_t* x;         // tokens in memory
     const float* u;           // uniforms in memory (null for greedy-only calls)
-    __device__ __forceinline__ int token(int t) const { return t < kRowsLds ? xs[t] : x[t]; }
-    __device__ __forceinline__ float uniform(int t) const { return t <= kRowsLds ? us[t] : u[t]; }
+    int nx, nu;
+    __device__ __forceinline__ int token(int t) const { return t < nx ? lds(xs)[t] : gbl(x)[t]; }
+    __device__ __forceinline__ float uniform(int t) const { return t < nu ? lds(us)[t] : gbl(u)[t]; }
 };
 
 // Row i (0..K_b target rows, K_b+1..2K_b draft rows) of sequence b from its pass-1 chunk
@@ -232,6 +233,8 @@ __device__ __forceinline__ SeqDesc resolve_seq(const VerifyArgs& a, int b, bool 
     in.u = a.uniforms ? a.uniforms + s.t0 : nullptr;
     in.xs = xs;
     in.us = us;
+    in.nx = kRowsLds;
+    in.nu = kRowsLds + 1;
     const int nparts = a.R * a.nchunk1;
     const RowPartial* src = a.part1 + (int64_t)b * nparts;
     const bool staged = nparts <= kPartsLds;
@@ -491,8 +494,9 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(VerifyArgs a) {
     ResolveIn in;
     in.x = a.tokens + s.d0;
     in.u = a.uniforms ? a.uniforms + s.t0 : nullptr;
-    in.xs = in.x;  // tokens and uniforms straight from memory
-    in.us = in.u;
+    in.xs = nullptr;  // tokens and uniforms straight from memory
+    in.us = nullptr;
+    in.nx = in.nu = 0;
     const RowPartial* parts = a.part1 + (int64_t)b * a.R * a.nchunk1;
     const int te = min(a.t1, K);
     int first = 0x7fffffff;
