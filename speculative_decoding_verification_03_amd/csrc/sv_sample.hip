@@ -6,38 +6,54 @@
 // against a provisional reference, kSampleLift binary orders of weight above R0 (the maximum
 // of the row's first vectors).  Against the row maximum M that scales every weight by one
 // common factor and so leaves the inverse CDF where it is.  The fp64 weights are summed per
-// kSampleSeg-position segment (one wave per segment) while the row's NaN-propagating maximum
-// is taken along, then the segment sums are scanned for u * W and the segment that holds it
-// is searched: token = min{ i : C_i > u * W }, C the prefix sums in index order.  The lift
-// keeps M's weight at 2^-kSampleLift or more, so every weight within 2^-75 of it stays a
-// normal fp64 number, and doubles the span M may lie above R0 before a weight could
-// overflow.  Only beyond that span ((M - R0) c2 > kSampleLift + kSampleRefGap binary orders,
-// e.g. a far outlier at a very low temperature) are the sums taken again against M.  Greedy
-// rows, and rows with a bad temperature or uniform, take one argmax pass.
+// kSampleSeg-position segment (one wave per segment), then the segment sums are scanned for
+// u * W and the segment that holds it is searched: token = min{ i : C_i > u * W }, C the
+// prefix sums in index order.  The lift keeps M's weight at 2^-kSampleLift or more, so every
+// weight within 2^-75 of it stays a normal fp64 number.
+//
+// The common path takes no per-element maximum: only the values read one by one pass
+// through a maximum mr (every value outside the bf16 weight table's magnitude range, NaN and
+// the infinities among them, and all values of rows without the table).  NaN or +inf there
+// is a data error.  Otherwise R0 <= M <= max(mr, kTabTop), which bounds |M| for the
+// scaled-range rule, and a total W of at most kSampleSumMax = 2^900 bounds every weight, so
+// no sum overflowed.  A row that fails either bound (a far outlier at a very low
+// temperature, many values near a far maximum, a row that opens with kSampleThreads vectors
+// of -inf, a temperature near the range limit) takes the slow path: a maximum pass for M,
+// the checks on it, and the sums again against M.  Greedy rows, and rows with a bad
+// temperature or uniform, take one argmax pass.
 #include "sv_draw.h"
 
 namespace sv {
 
 namespace {
 
-// Binary orders of magnitude the weights may reach above the reference's weight 1: sums
-// of up to 2^22 of them stay finite in fp64.
-constexpr double kSampleRefGap = 900.0;
+// Largest row total the common path keeps: no weight and no partial sum above it can have
+// overflowed.
+constexpr double kSampleSumMax = 0x1p900;
 // Binary orders of weight between R0 and the provisional reference above it (at most
 // 1022 - 75, so that weights within 2^-75 of the row maximum's are normal numbers).
 constexpr double kSampleLift = 900.0;
+// 2^5: every magnitude the bf16 weight table holds lies below it.
+constexpr float kTabTop = 32.0f;
+static_assert(kTabHi == 132u * 128u, "the table ends at biased exponent 132, magnitude 2^5");
 // 16-byte vectors per lane of one whole bf16 segment
 constexpr int kSegVecs = kSampleSeg / (64 * 8);
 static_assert(kSampleSeg % (64 * 8) == 0, "sampler segments are whole waves of bf16 vectors");
 static_assert(kSampleMaxSeg <= 2 * kSampleThreads, "the scan takes two segments per thread");
 
-// NaN-propagating maximum of the 8 bf16 values of a vector.
-__device__ __forceinline__ float vec_nmax(u32x4 v) {
-    float z[8];
-    Logit<uint16_t>::unpack(v, z);
-    float m = nmax(z[0], z[1]);
+// A thread's NaN-propagating maximum of the row's values (the threads stride the row).
+template <typename E, int NT>
+__device__ __forceinline__ float row_nmax(const E* row, int V, bool vec_ok) {
+    constexpr int VEC = Logit<E>::kVec;
+    const int nvec = vec_ok ? V / VEC : 0;
+    float m = -INFINITY;
+    for (int v = threadIdx.x; v < nvec; v += NT) {
+        float z[VEC];
+        Logit<E>::unpack(load16(row + (int64_t)v * VEC), z);
 #pragma unroll
-    for (int k = 2; k < 8; ++k) m = nmax(m, z[k]);
+        for (int k = 0; k < VEC; ++k) m = nmax(m, z[k]);
+    }
+    for (int i = nvec * VEC + threadIdx.x; i < V; i += NT) m = nmax(m, Logit<E>::at(row, i));
     return m;
 }
 
@@ -50,14 +66,13 @@ __device__ __forceinline__ void seg_load(const uint16_t* row, int lo, int lane, 
 // A lane's fp64 weight sum over its vectors of a whole bf16 segment (already loaded), with
 // table weights; a vector holding a value outside the table (its sum turns NaN on a
 // sentinel) is read again and summed with the exact weights.  mx: the lane's
-// NaN-propagating maximum of the values, updated.
+// NaN-propagating maximum of the values of the vectors read again, updated.
 __device__ __forceinline__ double seg_sum_tab(const DrawRows<uint16_t>& r, const u32x4 (&v)[kSegVecs], int lo,
                                               int lane, float& mx) {
     double s = 0.0;
     uint32_t again = 0;
 #pragma unroll
     for (int k = 0; k < kSegVecs; ++k) {
-        mx = nmax(mx, vec_nmax(v[k]));
         const uint32_t x4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
         double sk = 0.0;
 #pragma unroll
@@ -79,7 +94,9 @@ __device__ __forceinline__ double seg_sum_tab(const DrawRows<uint16_t>& r, const
 #pragma unroll 1
         for (int q = 0; q < 8; ++q) {
             const uint32_t h = (x4[q >> 1] >> (16 * (q & 1))) & 0xffffu;
-            sk += r.a_of(__uint_as_float(h << 16));
+            const float z = __uint_as_float(h << 16);
+            mx = nmax(mx, z);
+            sk += r.a_of(z);
         }
         s += sk;
     }
@@ -105,10 +122,11 @@ __device__ __forceinline__ double seg_sum_exact(const DrawRows<E>& r, int lo, in
 }
 
 // Sums of the weights of every segment of the row into segsum, one wave per segment
-// (segments w, w + NW, ...), and each lane's NaN-propagating maximum of the values read.
-// With the table (bf16, aligned rows) every whole segment's loads go out before the
-// previous one is summed.  first: the wave's first whole segment, already loaded (when
-// have_first).  Contains no barrier.
+// (segments w, w + NW, ...), and each lane's NaN-propagating maximum of the values read one
+// by one: with the table (bf16, aligned rows) those of the vectors that hold a value outside
+// it and of the row's tail, else every value.  With the table every whole segment's loads
+// go out before the previous one is summed.  first: the wave's first whole segment, already
+// loaded (when have_first).  Contains no barrier.
 template <typename E, int NT>
 __device__ __forceinline__ float row_segment_sums(const DrawRows<E>& r, int V, double* segsum, bool have_first,
                                                   const u32x4 (&first)[kSegVecs]) {
@@ -159,6 +177,62 @@ __device__ __forceinline__ float row_segment_sums(const DrawRows<E>& r, int V, d
     return mx;
 }
 
+// The segment that holds u * W, found by one wave from the segment sums in LDS (every wave
+// that calls it gets the same bits): each lane sums a run of consecutive segments in index
+// order, a wave scan gives the runs' prefix sums, and the first segment with mass whose
+// prefix passes u * W is the hit.  If rounding puts u * W past every prefix, the hit is the
+// last segment with mass and the target becomes +inf (fallback).  hit = -1 when W = 0.
+struct SegHit {
+    double total;   // W
+    double base;    // sum of the segments before the hit
+    double target;  // u * W, or +inf on the fallback
+    int hit;
+    bool fallback;
+};
+
+__device__ __forceinline__ SegHit seg_hit(const double* segsum, int nseg, double u) {
+    const int lane = threadIdx.x & 63;
+    const int per = (nseg + 63) / 64;
+    const int k0 = min(nseg, lane * per), k1 = min(nseg, k0 + per);
+    double run = 0.0;
+    for (int k = k0; k < k1; ++k) run += segsum[k];
+    const double incl = wave_inclusive_scan(run);
+    double ex = __shfl_up(incl, 1, 64);
+    if (lane == 0) ex = 0.0;
+    SegHit h;
+    h.total = __shfl(incl, 63, 64);
+    h.base = 0.0;
+    h.target = (double)u * h.total;
+    h.hit = -1;
+    h.fallback = false;
+    if (!(h.total > 0.0)) return h;
+    int first = 0x7fffffff, last = -1;
+    double fbase = 0.0, lbase = 0.0, acc = ex;
+    for (int k = k0; k < k1; ++k) {
+        const double v = segsum[k];
+        if (v > 0.0) {
+            // a segment without mass never holds the first crossing (guards rounding)
+            if (first == 0x7fffffff && acc + v > h.target) {
+                first = k;
+                fbase = acc;
+            }
+            last = k;
+            lbase = acc;
+        }
+        acc += v;
+    }
+    h.hit = wave_min(first);
+    if (h.hit != 0x7fffffff) {
+        h.base = __shfl(fbase, h.hit / per, 64);
+    } else {
+        h.hit = wave_max(last);  // W > 0: some segment has mass
+        h.base = __shfl(lbase, h.hit / per, 64);
+        h.target = INFINITY;
+        h.fallback = true;
+    }
+    return h;
+}
+
 // grid = rows, one workgroup per row (see the top of this file).
 template <typename E>
 __global__ __launch_bounds__(kSampleThreads) void sample_kernel(VerifyArgs a) {
@@ -169,8 +243,6 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(VerifyArgs a) {
     __shared__ double segsum[kSampleMaxSeg];
     __shared__ float shv[NW];
     __shared__ int shi[NW];
-    __shared__ double shd[2 * NW];
-    __shared__ double sh_base;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int V = a.V;
     const float T = a.temperature[b];
@@ -275,17 +347,29 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(VerifyArgs a) {
         __syncthreads();
     }
     const float mx = row_segment_sums<E, NT>(r, V, segsum, have_first, first);
-    const float M = block_nmax<NW>(mx, shv);  // its barriers also publish segsum
-    const float c2f = (float)(kLog2eD / (double)T);
-    if ((M != M) || M == INFINITY || M == -INFINITY || scaled_range_bad(M, c2f)) {
+    const float mr = block_nmax<NW>(mx, shv);  // its barriers also publish segsum
+    if (mr != mr || mr == INFINITY) {
         if (tid == 0) {
             a.out_tokens[b] = -1;
             a.out_status[b] = kSeqErrLogit;
         }
         return;
     }
-    if (!(((double)M - ref) * c2 <= kSampleRefGap)) {
-        // weights against R0 could overflow: the sums again against the row maximum
+    const int nseg = (V + kSampleSeg - 1) / kSampleSeg;
+    SegHit h = seg_hit(segsum, nseg, (double)u);
+    const float c2f = (float)(kLog2eD / (double)T);
+    // R0 <= M <= max(mr, kTabTop): a bound on |M| for the scaled-range rule
+    const float ub = fmaxf(fabsf(R0), fmaxf(mr, kTabTop));
+    if (!(h.total <= kSampleSumMax) || scaled_range_bad(ub, c2f)) {
+        // the slow path: the row maximum, its checks, the sums again against it
+        const float M = block_nmax<NW>(row_nmax<E, NT>(row, V, vec_ok), shv);
+        if ((M != M) || M == INFINITY || M == -INFINITY || scaled_range_bad(M, c2f)) {
+            if (tid == 0) {
+                a.out_tokens[b] = -1;
+                a.out_status[b] = kSeqErrLogit;
+            }
+            return;
+        }
         d.mt = d.md = M;
         r = draw_rows<E>(a, d, tab, sizeof(E) == 2 ? wt : nullptr);
         r.t = row;
@@ -297,43 +381,19 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(VerifyArgs a) {
         }
         row_segment_sums<E, NT>(r, V, segsum, false, first);
         __syncthreads();
+        h = seg_hit(segsum, nseg, (double)u);
     }
-
-    // the segment holding u * W (two segments per thread), then the index inside it
-    const int nseg = (V + kSampleSeg - 1) / kSampleSeg;
-    int status = 0;
-    const int k0 = 2 * tid, k1 = 2 * tid + 1;
-    const double v0 = k0 < nseg ? segsum[k0] : 0.0;
-    const double v1 = k1 < nseg ? segsum[k1] : 0.0;
-    double total;
-    const double ex = block_exclusive_scan<NW>(v0 + v1, total, shd);
+    // the index inside the hit segment
     int y = -1;
-    if (total > 0.0) {
-        const double target = (double)u * total;
-        // a segment without mass never holds the first crossing (guards rounding)
-        const bool c0 = v0 > 0.0 && ex + v0 > target;
-        const bool c1 = v1 > 0.0 && (ex + v0) + v1 > target;
-        int hit = block_min<NW>(c0 ? k0 : (c1 ? k1 : 0x7fffffff), shi);
-        double tgt = target;
-        if (hit == 0x7fffffff) {
-            // rounding put u*W past every prefix: the last segment with mass, last index
-            hit = block_max<NW>(v1 > 0.0 ? k1 : (v0 > 0.0 ? k0 : -1), shi);
-            tgt = INFINITY;
-            status |= kSeqNoteFallback;
-        }
-        // total > 0 leaves some segment with mass, so hit >= 0 (checked all the same)
-        if (hit >= 0) {
-            if (tid == (hit >> 1)) sh_base = (hit & 1) ? ex + v0 : ex;
-            __syncthreads();
-            int lo, hi;
-            seg_range(V, kSampleSeg, hit, lo, hi);
-            y = block_search<E, NT>(r, lo, hi, sh_base, tgt, false, (double)u);
-        }
+    if (h.hit >= 0) {
+        int lo, hi;
+        seg_range(V, kSampleSeg, h.hit, lo, hi);
+        y = block_search<E, NT>(r, lo, hi, h.base, h.target, false, (double)u);
     }
     if (tid == 0) {
-        // the finite row maximum has a positive weight: total > 0 and some index qualifies
+        // the finite row maximum has a positive weight: W > 0 and some index qualifies
         a.out_tokens[b] = y;
-        a.out_status[b] = y < 0 ? kSeqErrLogit : status;
+        a.out_status[b] = y < 0 ? kSeqErrLogit : (h.fallback ? kSeqNoteFallback : 0);
     }
 }
 

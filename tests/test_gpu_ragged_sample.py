@@ -3,6 +3,7 @@ with the fp64 oracle, on MI355X.  Same bar as the dense verify: greedy and data 
 bit-exact, sampled draws identical except near-ties (under 1e-4 of draws), reported
 probabilities within 1e-5 relative.
 """
+import math
 import os
 
 import numpy as np
@@ -289,6 +290,81 @@ def test_sample_far_maximum(dev, dt):
     assert set(np.asarray(r["tokens"]).tolist()) <= set(spots)
     greedy = np.asarray(temps) == 0.0
     assert (np.asarray(r["tokens"])[greedy] == spots[0]).all()
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_sample_row_shapes_near_the_limits(dev, dt):
+    """Sampled rows at the edges of the sampler's one-read path, each equal to the oracle:
+    a row that opens with 8192 -inf; a finite mask value (-1e30) among ordinary logits;
+    values whose weights against the provisional reference each lie just under 2^900, enough
+    of them that the row total passes it; a row maximum just inside and one just outside
+    the scaled-range rule at T = 1e-6 (an error in the oracle and on the GPU)."""
+    V, n_u = 20007, 6
+    say(f"sampler rows near the limits {dt}")
+    rng = np.random.default_rng(777)
+    nfirst = 8192 if dt == torch.bfloat16 else 4096   # the values the provisional max reads
+    rows, temps = [], []
+
+    def add(z, t):
+        for _ in range(n_u):
+            rows.append(z.copy())
+            temps.append(t)
+
+    def rnd(v=V):
+        return rng.standard_normal(v).astype(np.float32)
+
+    def cast(z):   # the values the kernel will see
+        return torch.from_numpy(z).to(dt).float().numpy()
+
+    z = rnd()
+    z[:8192] = -np.inf
+    add(z, 0.8)
+    z = rnd()
+    z[rng.choice(V, 500, replace=False)] = -1e30
+    add(z, 1.1)
+    z = cast(rnd())
+    r0 = float(z[:nfirst].max())
+
+    def down(v):   # the next value below v > 0 in the row's type
+        if dt == torch.float32:
+            return float(np.nextafter(np.float32(v), np.float32(0)))
+        b = torch.tensor([v], dtype=torch.bfloat16).view(torch.int16) - 1
+        return float(b.view(torch.bfloat16).float())
+
+    # a temperature at which some value of the row's type weighs 2^e, 895 <= e < 899.9,
+    # against the provisional reference (the lifted maximum of the first values)
+    for T in np.linspace(0.08, 0.12, 401).astype(np.float32):
+        c2 = math.log2(math.e) / float(T)
+        ref = r0 + float(np.float32(900.0 / c2))
+        spike = float(cast(np.array([ref + 899.6 / c2], dtype=np.float32))[0])
+        while (spike - ref) * c2 >= 899.9:
+            spike = down(spike)
+        e = (spike - ref) * c2
+        if e >= 895.0:
+            break
+    assert e >= 895.0
+    n = max(2, math.ceil(2.0 ** (900.3 - e)))
+    z[np.linspace(9000, V - 1, n).astype(np.int64)] = spike
+    add(z, float(T))
+    z = rnd()
+    z[13000] = 700.0     # 700 * log2(e) / 1e-6 < 2^30
+    add(z, 1e-6)
+    z = rnd()
+    z[13000] = 800.0     # 800 * log2(e) / 1e-6 >= 2^30: an error
+    add(z, 1e-6)
+    B = len(rows)
+    zt = torch.from_numpy(np.stack(rows)).to(dev).to(dt).contiguous()
+    Tt = torch.tensor(temps, dtype=torch.float32, device=dev)
+    u = torch.from_numpy(host_uniforms(92, 1, 0, B, 0).reshape(B)).to(dev)
+    r = to_host(sv.sv_sample(zt, u, Tt))
+    o = O.sample(logits_to_host(zt), u.cpu().numpy(), Tt.cpu().numpy())
+    np.testing.assert_array_equal(r["status"], o["status"])
+    t = compare(sample_as_verify(r), sample_as_verify(o), range(B), Tt.cpu())
+    say("  ", t)
+    t.assert_ok("sampler, rows near the limits")
+    st = np.asarray(r["status"]) & ~16
+    assert (st[:4 * n_u] == 0).all() and (st[4 * n_u:] != 0).all()
+    assert (np.asarray(r["tokens"])[3 * n_u:4 * n_u] == 13000).all()
 
 
 # ------------------------------------------------------------------------------------
