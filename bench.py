@@ -69,6 +69,32 @@ def measured_traffic(workload):
     return float(m_bytes.group(1))
 
 
+def needed_rows(temperature, accept_len, status, K):
+    """Logit rows the verify rule needs for one batch: the positions up to each sequence's
+    first rejection n (target and draft rows 0..n of a sampled sequence, K+1 target and K
+    draft rows if all K drafts are accepted; target rows 0..n of a greedy one).  A sequence
+    with a data error counts with every row."""
+    import numpy as np
+    T = np.asarray(temperature)
+    n = np.asarray(accept_len).astype(np.int64)
+    err = (np.asarray(status) & ~16) != 0
+    sampled = T != 0
+    full = K + 1 + np.where(sampled, K, 0)
+    rows = np.where(sampled, np.where(n == K, 2 * K + 1, 2 * (n + 1)), n + 1)
+    return int(np.where(err, full, rows).sum())
+
+
+def drawn_rows(temperature, accept_len, status, K):
+    """Rows pass 2 reads for one batch: the target and draft rows at the rejection of each
+    sampled sequence that rejected a draft, the target row K of each that accepted all;
+    none for greedy sequences or sequences with a data error."""
+    import numpy as np
+    T = np.asarray(temperature)
+    n = np.asarray(accept_len)
+    ok = (T != 0) & ((np.asarray(status) & ~16) == 0)
+    return int(((ok & (n < K)) * 2 + (ok & (n == K)) * 1).sum())
+
+
 def host_logits(x):
     import numpy as np
     import torch
@@ -546,22 +572,8 @@ def main():
     bad = int(sum(int(((r[2]["status"] & ~16) != 0).sum()) for r in records))
     value = positions / (ms_step * 1e-3)
     if args.path == "verify" and args.early_exit:
-        # the rows the rule needs: positions up to each sequence's first rejection (target
-        # and draft rows of sampled sequences, target rows of greedy ones); a sequence with
-        # a data error counts with every row
-        need = 0.0
-        for st, k, o in records:
-            T_k = sets[k]["temperature"].cpu().numpy()
-            n = o["accept_len"]
-            err = (o["status"] & ~16) != 0
-            for b in range(B):
-                if err[b]:
-                    rows = K + 1 + (K if T_k[b] != 0 else 0)
-                elif T_k[b] != 0:
-                    rows = (K + 1 + K) if n[b] == K else 2 * (n[b] + 1)
-                else:
-                    rows = n[b] + 1
-                need += rows
+        need = sum(needed_rows(sets[k]["temperature"].cpu().numpy(), o["accept_len"], o["status"], K)
+                   for st, k, o in records)
         p1_bytes = need / len(records) * V * esize
     achieved = p1_bytes / (ms_pass1 * 1e-3) / 1e9
     traffic = measured_traffic(cfg)
@@ -571,10 +583,8 @@ def main():
     draw_bytes = 0.0
     if args.path == "verify":
         for st, k, o in records:
-            T_k = sets[k]["temperature"].cpu().numpy()
-            ok = (T_k != 0) & ((o["status"] & ~16) == 0)
-            n = o["accept_len"]
-            draw_bytes += float(((ok & (n < K)) * 2 + (ok & (n == K)) * 1).sum()) * V * esize
+            draw_bytes += drawn_rows(sets[k]["temperature"].cpu().numpy(), o["accept_len"],
+                                     o["status"], K) * V * esize
         draw_bytes /= len(records)
     call_bytes = p1_bytes + draw_bytes
 
