@@ -566,6 +566,39 @@ def test_workspace_growth_on_side_stream(dev):
         t.assert_ok(what)
 
 
+def test_concurrent_calls_on_separate_streams(dev):
+    """Calls in flight together on three streams, each with a workspace of its own (two
+    verify batches of different shapes and a greedy batch, issued back to back with no
+    synchronisation between them): every result equals the oracle's."""
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    a = W.make_inputs(3, step=21, device=dev)
+    b = W.make_inputs(4, step=21, device=dev, B=48)
+    c = W.make_inputs(2, step=21, device=dev)
+    ua = gpu_uniforms(1003, 21, a["B"], a["K"])
+    ub = gpu_uniforms(1004, 21, b["B"], b["K"])
+    for s_ in streams:
+        s_.wait_stream(torch.cuda.current_stream())
+    ws = [sv.Workspace(dev) for _ in range(3)]
+    outs = []
+    for rep in range(3):
+        ra = sv.spec_verify(a["target"], a["draft"], a["tokens"], ua, a["temperature"],
+                            workspace=ws[0], stream=streams[0])
+        rb = sv.spec_verify(b["target"], b["draft"], b["tokens"], ub, b["temperature"],
+                            workspace=ws[1], stream=streams[1])
+        rc = sv.spec_verify_greedy(c["target"], c["tokens"], workspace=ws[2], stream=streams[2])
+        outs.append((ra, rb, rc))
+    torch.cuda.synchronize()
+    og = O.verify_greedy(logits_to_host(c["target"]), c["tokens"].cpu().numpy())
+    oa, ob = oracle_sampled(a, ua), oracle_sampled(b, ub)
+    for ra, rb, rc in outs:
+        for inp, o, r, what in ((a, oa, ra, "B=64 K=5"), (b, ob, rb, "B=48 K=8")):
+            t = compare(to_host(r), o, range(inp["B"]), inp["temperature"].cpu())
+            t.assert_ok(f"concurrent {what}")
+        g = to_host(rc)
+        for k in ("tokens", "accept_len", "status"):
+            np.testing.assert_array_equal(g[k], og[k], err_msg=f"concurrent greedy: {k}")
+
+
 def test_scaled_range_and_underflowing_ratios(dev):
     """Rows whose maximum m has |m| * fp32(log2(e)/T) >= 2^30 are data errors, rows just
     inside are not (T = 1 and the smallest legal temperatures, greedy rows exempt); tests
