@@ -108,3 +108,61 @@ def test_graph_replays_equal_eager(dev, entry):
         assert_same(got, to_host(ref), f"{entry}, replay {step}")
         say(f"   replay {step}: {int((got['status'] != 0).sum())} flagged, mean accept "
             f"{float(got['accept_len'].mean()):.2f}")
+
+
+@pytest.mark.parametrize("entry", ["spec_verify_greedy", "sv_sample"])
+def test_graph_replays_equal_eager_greedy_and_sampler(dev, entry):
+    cfg = 4
+    x0 = W.make_inputs(cfg, step=0, device=dev, B=64)
+    B, K = x0["B"], x0["K"]
+    say(f"graph capture of {entry}: B={B} K={K} V={x0['V']}")
+    if entry == "sv_sample":
+        static = dict(rows=x0["draft"][:, 0].contiguous(), temperature=x0["temperature"].clone())
+        u = torch.empty((B,), dtype=torch.float32, device=dev)
+        out = dict(tokens=torch.empty((B,), dtype=torch.int32, device=dev),
+                   status=torch.empty((B,), dtype=torch.int32, device=dev))
+    else:
+        static = dict(target=x0["target"].clone(), tokens=x0["tokens"].clone())
+        out = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                   accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
+                   status=torch.empty((B,), dtype=torch.int32, device=dev))
+    ws = sv.Workspace(dev)
+
+    def call(o, inp):
+        if entry == "sv_sample":
+            sv.sv_sample(inp["rows"], u, inp["temperature"], out=o, workspace=ws)
+        else:
+            sv.spec_verify_greedy(inp["target"], inp["tokens"], out=o, workspace=ws)
+
+    if entry == "sv_sample":
+        sv.sv_fill_uniforms(SEED, 1, 0, B, 0, out=u.view(B, 1))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out, static)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out, static)
+    torch.cuda.synchronize()
+    for step in range(1, 4):
+        x = W.make_inputs(cfg, step=step, device=dev, B=64)
+        fresh = (dict(rows=x["draft"][:, 0].contiguous(), temperature=x["temperature"])
+                 if entry == "sv_sample" else dict(target=x["target"], tokens=x["tokens"]))
+        for k in static:
+            static[k].copy_(fresh[k])
+        if entry == "sv_sample":
+            sv.sv_fill_uniforms(SEED, 1, step, B, 0, out=u.view(B, 1))
+        junk = torch.randn((512, 512), device=dev) @ torch.randn((512, 512), device=dev)
+        g.replay()
+        torch.cuda.synchronize()
+        got = to_host(out)
+        if entry == "sv_sample":
+            ref = to_host(sv.sv_sample(fresh["rows"], u, fresh["temperature"], workspace=sv.Workspace(dev)))
+        else:
+            ref = to_host(sv.spec_verify_greedy(fresh["target"], fresh["tokens"], workspace=sv.Workspace(dev)))
+        torch.cuda.synchronize()
+        del junk
+        for k in got:
+            np.testing.assert_array_equal(got[k], ref[k], err_msg=f"{entry}, replay {step}: {k}")
