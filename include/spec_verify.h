@@ -30,7 +30,9 @@
  * library never allocates, frees or retains memory (spec_verify_noalloc uses a static
  * scratch array of the library instead of a caller workspace).  All calls are asynchronous on
  * `stream` (a hipStream_t passed as void*; NULL = the null stream) and never
- * synchronise the host.  Outputs stay on the device.
+ * synchronise the host.  Outputs stay on the device.  No call records a memset or any
+ * operation other than kernel launches on `stream`, so calls can be captured in a HIP
+ * graph (the profiling pair sv_profile_begin/end excepted: it records events).
  *
  * Errors.  Argument errors are detected on the host BEFORE any HIP call and
  * returned synchronously (SV_ERR_ARG, SV_ERR_DTYPE, SV_ERR_WORKSPACE); a failed
