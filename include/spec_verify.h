@@ -160,8 +160,9 @@ sv_status spec_verify_noalloc(const void* target_logits, const void* draft_logit
  * spec_verify reading each sequence's rows only up to its first rejection: the tests run
  * left to right and stop there ("A Regra de Exatidão": the first rejection ends the step),
  * so the rows of later positions are never needed for the emitted tokens.  Positions are
- * read in two rounds (the first third, then the rest for the sequences that accepted all
- * of the first); a sequence whose test fails in the first round reads nothing more.  The
+ * read in rounds: [0, 2), then the rest for the sequences that accepted both (a call over
+ * more than 4 GiB of logit rows also stops at position 5); a sequence whose test fails in
+ * a round reads nothing more.  The
  * emitted tokens, accept lengths and draws are bit-identical to spec_verify's.
  * Differences: out_p / out_q hold p_t(x_t), q_t(x_t) only for the positions up to and
  * including the first rejection n (all K when every draft is accepted) and are NaN after

@@ -228,6 +228,9 @@ int verify_dense_call(const void* target_logits, const void* draft_logits, int d
 
 extern "C" {
 
+// Logit bytes of a full read above which early exit reads in three rounds, not two.
+constexpr double kEarlyExitBytes = 4.0 * (1 << 30);
+
 sv_status spec_verify_early_exit(const void* target_logits, const void* draft_logits, int dtype,
                                  const int32_t* draft_tokens, const float* uniforms,
                                  const float* temperature, int B, int K, int V,
@@ -259,11 +262,15 @@ sv_status spec_verify_early_exit(const void* target_logits, const void* draft_lo
                                  out_accept_len, out_p, out_q, out_status);
     a.limit = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + L.off_limit);
     const int bf16 = dtype == SV_DTYPE_BF16;
-    // two rounds: the first third of the positions, then the rest for the sequences that
-    // accepted all of them
-    const int r1 = (K + 3) / 3;
-    const int bounds[3] = {0, r1, K + 1};
-    const int rounds = r1 >= K + 1 ? 1 : 2;
+    // rounds of positions: [0, 2), then the rest for the sequences that accepted both; a
+    // call over more than kEarlyExitBytes of logit rows (where a round's fixed cost is
+    // small against the rows it can spare) also stops at position 5
+    int bounds[4];
+    int rounds = 0;
+    bounds[rounds++] = 0;
+    if (K + 1 > 2) bounds[rounds++] = 2;
+    if (K + 1 > 5 && (double)B * R * V * esz > kEarlyExitBytes) bounds[rounds++] = 5;
+    bounds[rounds] = K + 1;
     hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
     if (g_prof.on) {
         for (auto& e : ev) e = g_prof.next();
